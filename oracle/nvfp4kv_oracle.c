@@ -1,0 +1,341 @@
+/*
+ * CPU oracle for NVFP4 paged-KV decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Plain, slow, scalar C with fp64 arithmetic. Only
+ * the test suite, the smoke check and the benchmark's CPU-baseline leg may load
+ * it. It shares no code, header, table or constant with the GPU library: the
+ * pool layout below is re-derived here from its written definition.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [LMSYS]  "SGLang stores KV cache in 4 bits: long-context decode throughput
+ *            rises 26-30%, and FP8 stalls first under agent concurrency"
+ *            (summary of the LMSYS post "Accelerating Long-Context and Agentic
+ *            Inference with NVFP4 KV Cache").
+ *   [EUROK]  "NVFP4-KV-Cache auf der NVIDIA RTX PRO 6000 Blackwell Server
+ *            Edition: Genauigkeit, Nutzer".
+ *
+ * What is computed, step by step:
+ *   1. E2M1 element decode: a 4-bit float with one sign, two exponent and one
+ *      mantissa bit ([EUROK] "Bytes pro Token"). Reading: exponent bias 1, no
+ *      infinities or NaN, so the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ *   2. E4M3 block-scale decode: FP8 with four exponent and three mantissa bits
+ *      ([EUROK] "Bytes pro Token"). Reading: the OCP "fn" variant, bias 7,
+ *      subnormals m/8 * 2^-6, 0x7F/0xFF are NaN, largest finite 448.
+ *   3. Block scale of 16 contiguous values ([LMSYS] "Interpretation": one byte
+ *      of scale per 16 values): the E4M3 value nearest to amax / (6 g), ties to
+ *      the even code, clamped to the largest finite value (satfinite). g is the
+ *      per-tensor FP32 scale, 1.0 in every experiment ([LMSYS] "Perspective";
+ *      [EUROK] "Bytes pro Token"). The quotient is the exact real number.
+ *   4. Element codes: the E2M1 value nearest to x / (dec(s) g), ties to the
+ *      even code, saturating at 6; the sign bit is the sign bit of x. When the
+ *      scale is zero every code has magnitude 0 (a reading; the pages are
+ *      silent).
+ *   5. Packing: byte i of a token's 64 code bytes holds element 2i in its low
+ *      nibble and element 2i+1 in its high nibble; 8 data bytes plus 1 scale
+ *      byte per 16 values ([LMSYS] "Interpretation").
+ *   6. Dequantization: x^ = E2M1(c) * E4M3(s) * g ([LMSYS] "Interpretation":
+ *      decode dequantizes inside the attention kernel).
+ *   7. Attention for decode: softmax(sm_scale * q . k^_t) weighted sum of v^_t
+ *      over t < seq_len, per query head, with query head q reading KV head
+ *      q / (Hq / Hkv) (grouped-query attention, [EUROK] "Unterstuetzung in den
+ *      Engines"). Evaluated in fp64 as the plain definition: all logits, their
+ *      maximum, exponentials, sums, one division.
+ *
+ * Pool layout (the written definition both sides implement independently):
+ *   A pool holds num_pages pages; each page holds, for each KV head h, a K slab
+ *   then a V slab of 1152 bytes each:  slab(p, h, kind) starts at byte
+ *   ((p * Hkv + h) * 2 + kind) * 1152, kind 0 = K, 1 = V. A slab covers the 16
+ *   token rows r of the page and the 128 channels d of the head: 1024 code
+ *   bytes, then 128 scale bytes.
+ *     K code byte (row r, pair i = d/2):  r*64 + i
+ *     K scale byte (row r, block j = d/16): 1024 + r*8 + j
+ *     V code byte (row r, pair i):  ((i%16)*4 + r/4)*16 + (i/16)*4 + r%4
+ *     V scale byte (row r, block j): 1024 + ((r/4)*2 + j%2)*16 + (j/2)*4 + r%4
+ *   Token t of a sequence lives at page page_table[t/16], row t%16.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_D 128
+#define ORC_PAGE 16
+#define ORC_SLAB 1152
+
+/* ---- 1. E2M1 decode ---------------------------------------------------- */
+double orc_e2m1_value(int code) {
+  int sign = (code >> 3) & 1;
+  int e = (code >> 1) & 3;
+  int m = code & 1;
+  double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return sign ? -mag : mag;
+}
+
+/* ---- 2. E4M3 decode ---------------------------------------------------- */
+double orc_e4m3_value(int byte) {
+  int sign = (byte >> 7) & 1;
+  int e = (byte >> 3) & 15;
+  int m = byte & 7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp(m / 8.0, -6);
+  else
+    mag = ldexp(1.0 + m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+/* ---- 3. block scale: nearest E4M3 to amax / den, ties even, satfinite ---- */
+/* Walks the 127 non-negative finite E4M3 values upward; the result moves past
+ * value k exactly when amax/den lies above the midpoint of k and k+1, or on it
+ * with k odd (so that a tie lands on the even code). All products below carry
+ * few significant bits and are exact in double. */
+int orc_e4m3_nearest_of_quotient(double amax, double den) {
+  int k = 0;
+  while (k < 126) {
+    double mid = 0.5 * (orc_e4m3_value(k) + orc_e4m3_value(k + 1));
+    double thr = den * mid;
+    if (amax > thr || (amax == thr && (k & 1)))
+      ++k;
+    else
+      break;
+  }
+  return k;
+}
+
+int orc_scale_byte(float amax, float g) {
+  return orc_e4m3_nearest_of_quotient((double)amax, 6.0 * (double)g);
+}
+
+/* ---- 4. element code: nearest E2M1 to x / D, ties even, saturating -------- */
+int orc_e2m1_code(float x, double D) {
+  int sign = signbit(x) ? 8 : 0;
+  double ax = fabs((double)x);
+  int k = 0;
+  if (D == 0.0) return sign; /* zero scale: magnitude 0, sign kept */
+  while (k < 7) {
+    double mid = 0.5 * (orc_e2m1_value(k) + orc_e2m1_value(k + 1));
+    double thr = D * mid;
+    if (ax > thr || (ax == thr && (k & 1)))
+      ++k;
+    else
+      break;
+  }
+  return sign | k;
+}
+
+/* ---- 3+4+5: one block of 16 values ------------------------------------ */
+void orc_quantize_block16(const float* x, float g, uint8_t* codes8, uint8_t* scale) {
+  float amax = 0.0f;
+  int i;
+  for (i = 0; i < 16; ++i) {
+    float a = fabsf(x[i]);
+    if (a > amax) amax = a;
+  }
+  int s = orc_scale_byte(amax, g);
+  double D = orc_e4m3_value(s) * (double)g;
+  for (i = 0; i < 8; ++i) {
+    int lo = orc_e2m1_code(x[2 * i], D);
+    int hi = orc_e2m1_code(x[2 * i + 1], D);
+    codes8[i] = (uint8_t)(lo | (hi << 4));
+  }
+  *scale = (uint8_t)s;
+}
+
+/* ---- pool addressing (written definition, see header) ------------------- */
+int64_t orc_slab_offset(int64_t page, int head, int kind, int num_kv_heads) {
+  return ((page * num_kv_heads + head) * 2 + kind) * (int64_t)ORC_SLAB;
+}
+int orc_code_byte_offset(int kind, int row, int pair) {
+  if (kind == 0) return row * 64 + pair;
+  return ((pair % 16) * 4 + row / 4) * 16 + (pair / 16) * 4 + row % 4;
+}
+int orc_scale_byte_offset(int kind, int row, int block) {
+  if (kind == 0) return 1024 + row * 8 + block;
+  return 1024 + ((row / 4) * 2 + block % 2) * 16 + (block / 2) * 4 + row % 4;
+}
+int64_t orc_pool_bytes(int64_t num_pages, int num_kv_heads) {
+  return num_pages * num_kv_heads * 2 * (int64_t)ORC_SLAB;
+}
+
+static float orc_bf16_to_float(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* Quantize-on-write of T tokens of K and V ([T][Hkv][128], element strides
+ * given) into the pool at slot_mapping[t] = page*16 + row (negative = skip).
+ * src_dtype 0 = float32, 1 = bfloat16 bits. */
+void orc_quantize_to_pool(const void* k_src, const void* v_src, int src_dtype, int64_t token_stride,
+                          int64_t head_stride, const int32_t* slot_mapping, int num_tokens,
+                          int num_kv_heads, float g, uint8_t* pool) {
+  int t, h, kind, j, i;
+  for (t = 0; t < num_tokens; ++t) {
+    int32_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    int64_t page = slot / ORC_PAGE;
+    int row = slot % ORC_PAGE;
+    for (h = 0; h < num_kv_heads; ++h) {
+      for (kind = 0; kind < 2; ++kind) {
+        const void* src = kind == 0 ? k_src : v_src;
+        uint8_t* slab = pool + orc_slab_offset(page, h, kind, num_kv_heads);
+        for (j = 0; j < 8; ++j) {
+          float x[16];
+          uint8_t codes[8], s;
+          for (i = 0; i < 16; ++i) {
+            int64_t idx = t * token_stride + h * head_stride + 16 * j + i;
+            x[i] = src_dtype == 0 ? ((const float*)src)[idx]
+                                  : orc_bf16_to_float(((const uint16_t*)src)[idx]);
+          }
+          orc_quantize_block16(x, g, codes, &s);
+          for (i = 0; i < 8; ++i) slab[orc_code_byte_offset(kind, row, 8 * j + i)] = codes[i];
+          slab[orc_scale_byte_offset(kind, row, j)] = s;
+        }
+      }
+    }
+  }
+}
+
+/* ---- 6. dequantize one token row of one head ------------------------------ */
+void orc_dequant_row(const uint8_t* pool, int64_t page, int row, int head, int kind,
+                     int num_kv_heads, float g, double* out128) {
+  const uint8_t* slab = pool + orc_slab_offset(page, head, kind, num_kv_heads);
+  int d;
+  for (d = 0; d < ORC_D; ++d) {
+    int byte = slab[orc_code_byte_offset(kind, row, d / 2)];
+    int code = (d & 1) ? (byte >> 4) : (byte & 15);
+    int s = slab[orc_scale_byte_offset(kind, row, d / 16)];
+    out128[d] = orc_e2m1_value(code) * orc_e4m3_value(s) * (double)g;
+  }
+}
+
+/* Extend path: dequantize tokens [0, len) of each listed sequence into a dense
+ * workspace [row][Hkv][128] (fp64 here), row = cu_rows[s] + t. */
+void orc_dequant_workspace(const uint8_t* pool, int num_kv_heads, float g, const int32_t* page_table,
+                           int64_t page_table_stride, const int32_t* seq_lens, const int64_t* cu_rows,
+                           int n_seqs, double* k_out, double* v_out) {
+  int s, h;
+  int64_t t;
+  for (s = 0; s < n_seqs; ++s)
+    for (t = 0; t < seq_lens[s]; ++t) {
+      int64_t page = page_table[s * page_table_stride + t / ORC_PAGE];
+      int row = (int)(t % ORC_PAGE);
+      for (h = 0; h < num_kv_heads; ++h) {
+        int64_t o = ((cu_rows[s] + t) * num_kv_heads + h) * ORC_D;
+        orc_dequant_row(pool, page, row, h, 0, num_kv_heads, g, k_out + o);
+        orc_dequant_row(pool, page, row, h, 1, num_kv_heads, g, v_out + o);
+      }
+    }
+}
+
+/* ---- 7. decode attention over the dequantized cache ----------------------- */
+typedef struct {
+  const uint16_t* q; /* bf16 bits [B][Hq][128] */
+  const int32_t* page_table;
+  int64_t page_table_stride;
+  const int32_t* seq_lens;
+  int batch, num_q_heads, num_kv_heads;
+  const uint8_t* pool;
+  float g;
+  double sm_scale;
+  double* out; /* [B][Hq][128] */
+  double* lse; /* [B][Hq] */
+  const int32_t* units; /* optional list of (b*Hq + qh) to compute; NULL = all */
+  int n_units;
+  int next; /* work counter */
+  pthread_mutex_t lock;
+} orc_attn_job;
+
+static void orc_attn_one(orc_attn_job* J, int b, int qh) {
+  int group = J->num_q_heads / J->num_kv_heads;
+  int h = qh / group;
+  int64_t L = J->seq_lens[b];
+  double q[ORC_D], kd[ORC_D], vd[ORC_D], acc[ORC_D];
+  double* out = J->out + ((int64_t)b * J->num_q_heads + qh) * ORC_D;
+  double m = -INFINITY, sum = 0.0;
+  double* z;
+  int64_t t;
+  int d;
+  for (d = 0; d < ORC_D; ++d) q[d] = (double)orc_bf16_to_float(J->q[((int64_t)b * J->num_q_heads + qh) * ORC_D + d]);
+  for (d = 0; d < ORC_D; ++d) acc[d] = 0.0;
+  if (L <= 0) { /* empty sequence: output 0, lse -inf (a reading) */
+    for (d = 0; d < ORC_D; ++d) out[d] = 0.0;
+    if (J->lse) J->lse[(int64_t)b * J->num_q_heads + qh] = -INFINITY;
+    return;
+  }
+  z = (double*)malloc(sizeof(double) * (size_t)L);
+  for (t = 0; t < L; ++t) { /* logits */
+    int64_t page = J->page_table[b * J->page_table_stride + t / ORC_PAGE];
+    double dot = 0.0;
+    orc_dequant_row(J->pool, page, (int)(t % ORC_PAGE), h, 0, J->num_kv_heads, J->g, kd);
+    for (d = 0; d < ORC_D; ++d) dot += q[d] * kd[d];
+    z[t] = J->sm_scale * dot;
+    if (z[t] > m) m = z[t];
+  }
+  for (t = 0; t < L; ++t) { /* weights and weighted sum of values */
+    int64_t page = J->page_table[b * J->page_table_stride + t / ORC_PAGE];
+    double w = exp(z[t] - m);
+    orc_dequant_row(J->pool, page, (int)(t % ORC_PAGE), h, 1, J->num_kv_heads, J->g, vd);
+    sum += w;
+    for (d = 0; d < ORC_D; ++d) acc[d] += w * vd[d];
+  }
+  for (d = 0; d < ORC_D; ++d) out[d] = acc[d] / sum;
+  if (J->lse) J->lse[(int64_t)b * J->num_q_heads + qh] = m + log(sum);
+  free(z);
+}
+
+static void* orc_attn_worker(void* arg) {
+  orc_attn_job* J = (orc_attn_job*)arg;
+  for (;;) {
+    int u;
+    pthread_mutex_lock(&J->lock);
+    u = J->next++;
+    pthread_mutex_unlock(&J->lock);
+    if (u >= J->n_units) break;
+    {
+      int unit = J->units ? J->units[u] : u;
+      orc_attn_one(J, unit / J->num_q_heads, unit % J->num_q_heads);
+    }
+  }
+  return NULL;
+}
+
+/* Computes out/lse for the listed (b*Hq + qh) units (all when units == NULL),
+ * spreading whole units over n_threads threads; the arithmetic of a unit does
+ * not depend on the thread count. */
+void orc_decode_attn(const uint16_t* q_bf16, const int32_t* page_table, int64_t page_table_stride,
+                     const int32_t* seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                     const uint8_t* pool, float g, double sm_scale, double* out, double* lse,
+                     const int32_t* units, int n_units, int n_threads) {
+  orc_attn_job J;
+  pthread_t th[256];
+  int i;
+  J.q = q_bf16;
+  J.page_table = page_table;
+  J.page_table_stride = page_table_stride;
+  J.seq_lens = seq_lens;
+  J.batch = batch;
+  J.num_q_heads = num_q_heads;
+  J.num_kv_heads = num_kv_heads;
+  J.pool = pool;
+  J.g = g;
+  J.sm_scale = sm_scale;
+  J.out = out;
+  J.lse = lse;
+  J.units = units;
+  J.n_units = units ? n_units : batch * num_q_heads;
+  J.next = 0;
+  pthread_mutex_init(&J.lock, NULL);
+  if (n_threads < 1) n_threads = 1;
+  if (n_threads > 256) n_threads = 256;
+  if (n_threads == 1) {
+    orc_attn_worker(&J);
+  } else {
+    for (i = 0; i < n_threads; ++i) pthread_create(&th[i], NULL, orc_attn_worker, &J);
+    for (i = 0; i < n_threads; ++i) pthread_join(th[i], NULL);
+  }
+  pthread_mutex_destroy(&J.lock);
+}

@@ -1,0 +1,95 @@
+"""Each pin must bite: plant a plausible mistake in a copy of the oracle source,
+build it with gcc, and check that at least one pin fails. Also checks that the
+written pool layout is a bijection onto the slab."""
+import pytest
+
+import oracle
+from tests import test_oracle_attention as TA
+from tests import test_oracle_format as TF
+
+# (name, original text, replacement) — each is a single plausible slip that keeps every
+# memory access in bounds (the variants run in this process)
+MUTANTS = [
+    ("e2m1_exponent_bias", "ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e)"),
+    ("e2m1_mantissa_weight", "ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.25 * m, e - 1)"),
+    ("e4m3_exponent_bias", "mag = ldexp(1.0 + m / 8.0, e - 7);", "mag = ldexp(1.0 + m / 8.0, e - 8);"),
+    ("e4m3_subnormal_exponent", "mag = ldexp(m / 8.0, -6);", "mag = ldexp(m / 8.0, -7);"),
+    ("scale_ties_to_odd", "if (amax > thr || (amax == thr && (k & 1)))",
+     "if (amax > thr || (amax == thr && !(k & 1)))"),
+    ("scale_ties_up", "if (amax > thr || (amax == thr && (k & 1)))", "if (amax >= thr)"),
+    ("scale_divisor_4", "6.0 * (double)g", "4.0 * (double)g"),
+    ("scale_clamps_too_low", "while (k < 126) {", "while (k < 125) {"),
+    ("code_ties_to_odd", "if (ax > thr || (ax == thr && (k & 1)))", "if (ax > thr || (ax == thr && !(k & 1)))"),
+    ("code_sign_dropped", "int sign = signbit(x) ? 8 : 0;", "int sign = 0;"),
+    ("code_divisor_without_scale", "double D = orc_e4m3_value(s) * (double)g;", "double D = (double)g;"),
+    ("nibbles_swapped_on_write", "codes8[i] = (uint8_t)(lo | (hi << 4));", "codes8[i] = (uint8_t)(hi | (lo << 4));"),
+    ("amax_misses_last", "for (i = 0; i < 16; ++i) {\n    float a", "for (i = 0; i < 15; ++i) {\n    float a"),
+    ("dequant_drops_scale", "out128[d] = orc_e2m1_value(code) * orc_e4m3_value(s) * (double)g;",
+     "out128[d] = orc_e2m1_value(code) * (double)g;"),
+    ("dequant_wrong_nibble", "int code = (d & 1) ? (byte >> 4) : (byte & 15);",
+     "int code = (d & 1) ? (byte & 15) : (byte >> 4);"),
+    ("dequant_wrong_block", "int s = slab[orc_scale_byte_offset(kind, row, d / 16)];",
+     "int s = slab[orc_scale_byte_offset(kind, row, d / 32)];"),
+    ("gqa_head_modulo", "int h = qh / group;", "int h = qh % J->num_kv_heads;"),
+    ("no_sm_scale", "z[t] = J->sm_scale * dot;", "z[t] = dot;"),
+    ("value_row_shifted", "orc_dequant_row(J->pool, page, (int)(t % ORC_PAGE), h, 1,",
+     "orc_dequant_row(J->pool, page, (int)((t + 1) % ORC_PAGE), h, 1,"),
+    ("value_uses_key_slab", "orc_dequant_row(J->pool, page, (int)(t % ORC_PAGE), h, 1,",
+     "orc_dequant_row(J->pool, page, (int)(t % ORC_PAGE), h, 0,"),
+    ("last_token_dropped", "for (t = 0; t < L; ++t) { /* weights", "for (t = 0; t < L - 1; ++t) { /* weights"),
+    ("lse_without_max", "J->lse[(int64_t)b * J->num_q_heads + qh] = m + log(sum);",
+     "J->lse[(int64_t)b * J->num_q_heads + qh] = log(sum);"),
+    ("key_row_reversed", "orc_dequant_row(J->pool, page, (int)(t % ORC_PAGE), h, 0,",
+     "orc_dequant_row(J->pool, page, (int)(15 - t % ORC_PAGE), h, 0,"),
+    ("workspace_row_offset", "int64_t o = ((cu_rows[s] + t) * num_kv_heads + h) * ORC_D;",
+     "int64_t o = ((cu_rows[s] + t) * num_kv_heads) * ORC_D;"),
+    ("slab_kind_ignored", "return ((page * num_kv_heads + head) * 2 + kind) * (int64_t)ORC_SLAB;",
+     "return ((page * num_kv_heads + head) * 2) * (int64_t)ORC_SLAB;"),
+]
+
+
+def _pins(o):
+    yield lambda: TF.test_e2m1_closed_form(o)
+    yield lambda: TF.test_e4m3_decode_all_bytes_vs_library(o)
+    yield lambda: TF.test_worked_example_block_of_ones(o)
+    yield lambda: TF.test_scale_byte_saturates(o)
+    yield lambda: TF.test_scale_byte_vs_library_rne(o)
+    yield lambda: TF.test_e2m1_code_threshold_edges(o)
+    yield lambda: TF.test_round_trip_of_representable_blocks(o)
+    yield lambda: TF.test_zero_scale_reading(o)
+    yield lambda: TA.test_attention_vs_library_sdpa_on_representable_kv(o, 8, 2, [16, 50, 1])
+    yield lambda: TA.test_dequant_workspace_returns_representable_values_exactly(o)
+    yield lambda: TA.test_seq_len_one_returns_first_value_row(o)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    src = oracle.source_text()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    path = oracle.build_variant(src.replace(old, new, 1), str(tmp_path / f"mut_{name}.so"))
+    caught = None
+    with oracle.use_library(path):
+        for i, pin in enumerate(_pins(oracle)):
+            try:
+                pin()
+            except AssertionError:
+                caught = i
+                break
+    assert caught is not None, f"no pin catches mutant {name}"
+
+
+def test_unmutated_oracle_passes_all_mutation_pins():
+    oracle.lib()
+    for pin in _pins(oracle):
+        pin()
+
+
+def test_pool_layout_is_a_bijection(oracle_lib):
+    for kind in (0, 1):
+        codes = {oracle_lib.code_byte_offset(kind, r, i) for r in range(16) for i in range(64)}
+        scales = {oracle_lib.scale_byte_offset(kind, r, j) for r in range(16) for j in range(8)}
+        assert codes == set(range(1024)) and scales == set(range(1024, 1152))
+    # K rows are token-major (64 contiguous code bytes, 8 contiguous scale bytes per token)
+    assert [oracle_lib.code_byte_offset(0, 3, i) for i in range(64)] == list(range(192, 256))
+    assert [oracle_lib.scale_byte_offset(0, 3, j) for j in range(8)] == list(range(1048, 1056))
+    assert oracle_lib.slab_offset(2, 1, 1, 8) == ((2 * 8 + 1) * 2 + 1) * 1152
