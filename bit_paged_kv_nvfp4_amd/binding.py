@@ -1,0 +1,191 @@
+"""Thin ctypes binding of libnvfp4kv (include/nvfp4kv.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of the
+library. PyTorch supplies device memory and streams. Every function raises
+RuntimeError when the library returns a non-zero status, and importing the
+library fails loudly when it has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4kv.so")
+
+HEAD_DIM = 128
+PAGE_SIZE = 16
+SLAB_BYTES = 1152
+F32 = 0
+BF16 = 1
+
+EXPORTED = [
+    "nvfp4kv_pool_bytes",
+    "nvfp4kv_status_string",
+    "nvfp4kv_version",
+    "nvfp4_kv_quantize",
+    "nvfp4_paged_decode_attn_default_splits",
+    "nvfp4_paged_decode_attn_workspace_bytes",
+    "nvfp4_paged_decode_attn",
+    "nvfp4_kv_dequant_workspace",
+]
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("num_pages", ctypes.c_int64), ("num_kv_heads", ctypes.c_int32),
+                ("global_scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m bit_paged_kv_nvfp4_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        c = ctypes
+        P = c.c_void_p
+        L.nvfp4kv_pool_bytes.argtypes = [c.c_int64, c.c_int32]
+        L.nvfp4kv_pool_bytes.restype = c.c_int64
+        L.nvfp4kv_status_string.argtypes = [c.c_int32]
+        L.nvfp4kv_status_string.restype = c.c_char_p
+        L.nvfp4kv_version.argtypes = []
+        L.nvfp4kv_version.restype = c.c_int32
+        L.nvfp4_kv_quantize.argtypes = [P, P, c.c_int32, c.c_int64, c.c_int64, P, c.c_int64,
+                                        c.POINTER(PoolDesc), P]
+        L.nvfp4_kv_quantize.restype = c.c_int32
+        L.nvfp4_paged_decode_attn_default_splits.argtypes = [c.c_int32, c.c_int32, c.c_int32, c.c_int32]
+        L.nvfp4_paged_decode_attn_default_splits.restype = c.c_int32
+        L.nvfp4_paged_decode_attn_workspace_bytes.argtypes = [c.c_int32, c.c_int32, c.c_int32]
+        L.nvfp4_paged_decode_attn_workspace_bytes.restype = c.c_size_t
+        L.nvfp4_paged_decode_attn.argtypes = [P, P, c.c_int64, P, c.c_int32, c.c_int32, c.c_int32,
+                                              c.POINTER(PoolDesc), c.c_float, c.c_int32, P, c.c_size_t, P,
+                                              c.c_int32, P, P]
+        L.nvfp4_paged_decode_attn.restype = c.c_int32
+        L.nvfp4_kv_dequant_workspace.argtypes = [c.POINTER(PoolDesc), P, c.c_int64, P, P, c.c_int32, c.c_int32,
+                                                 P, P, c.c_int32, P]
+        L.nvfp4_kv_dequant_workspace.restype = c.c_int32
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().nvfp4kv_status_string(int(code)).decode()
+
+
+def _check(name: str, code: int) -> None:
+    if code != 0:
+        raise RuntimeError(f"{name} failed with status {code}: {status_string(code)}")
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+class Pool:
+    """NVFP4 KV pool of one layer: a device uint8 buffer of num_pages pages with
+    num_kv_heads K and V slabs each (layout in include/nvfp4kv.h)."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, device="cuda", global_scale: float = 1.0,
+                 data: torch.Tensor | None = None):
+        nbytes = nvfp4kv_pool_bytes(num_pages, num_kv_heads)
+        if data is None:
+            data = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        if data.numel() != nbytes or data.dtype != torch.uint8:
+            raise ValueError("pool buffer has the wrong size or dtype")
+        self.data = data
+        self.num_pages = int(num_pages)
+        self.num_kv_heads = int(num_kv_heads)
+        self.global_scale = float(global_scale)
+
+    def desc(self) -> PoolDesc:
+        return PoolDesc(self.data.data_ptr(), self.num_pages, self.num_kv_heads, self.global_scale)
+
+
+def nvfp4kv_pool_bytes(num_pages: int, num_kv_heads: int) -> int:
+    return int(lib().nvfp4kv_pool_bytes(int(num_pages), int(num_kv_heads)))
+
+
+def nvfp4_kv_quantize(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, pool: Pool, stream=None):
+    """k, v: [T, Hkv, 128] float32 or bfloat16 on the device (last dim contiguous);
+    slot_mapping: int32 [T] (negative = skip)."""
+    if k.dtype != v.dtype or k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must share dtype, shape and strides")
+    if k.dim() != 3 or k.shape[2] != HEAD_DIM or k.stride(2) != 1:
+        raise ValueError("k, v must be [T, Hkv, 128] with a contiguous last dimension")
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(k.dtype)
+    if dt is None:
+        raise ValueError("k, v must be float32 or bfloat16")
+    if slot_mapping.dtype != torch.int32 or slot_mapping.numel() != k.shape[0]:
+        raise ValueError("slot_mapping must be int32 [T]")
+    d = pool.desc()
+    _check("nvfp4_kv_quantize", lib().nvfp4_kv_quantize(_ptr(k), _ptr(v), dt, k.stride(0), k.stride(1),
+                                                         _ptr(slot_mapping), k.shape[0], ctypes.byref(d),
+                                                         _stream(stream)))
+
+
+def nvfp4_paged_decode_attn_default_splits(batch: int, num_kv_heads: int, max_seq_len: int, num_cus: int = 0) -> int:
+    return int(lib().nvfp4_paged_decode_attn_default_splits(batch, num_kv_heads, max_seq_len, num_cus))
+
+
+def nvfp4_paged_decode_attn_workspace_bytes(batch: int, num_q_heads: int, num_splits: int) -> int:
+    return int(lib().nvfp4_paged_decode_attn_workspace_bytes(batch, num_q_heads, num_splits))
+
+
+def nvfp4_paged_decode_attn(q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor, pool: Pool,
+                            sm_scale: float, max_seq_len: int, num_splits: int = 0,
+                            workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                            out_dtype: torch.dtype = torch.bfloat16, lse: torch.Tensor | None = None, stream=None):
+    """q: bf16 [B, Hq, 128]; page_table: int32 [B, stride]; seq_lens: int32 [B].
+    Returns out [B, Hq, 128] (and fills ``lse`` [B, Hq] float32 when given)."""
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [B, Hq, 128] tensor")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_contiguous():
+        raise ValueError("page_table must be contiguous int32 [B, stride]")
+    B, hq, _ = q.shape
+    if num_splits == 0:
+        num_splits = nvfp4_paged_decode_attn_default_splits(B, pool.num_kv_heads, max_seq_len)
+    if workspace is None:
+        nbytes = nvfp4_paged_decode_attn_workspace_bytes(B, hq, num_splits)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    odt = {torch.float32: F32, torch.bfloat16: BF16}.get(out.dtype)
+    if odt is None or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 or bfloat16")
+    d = pool.desc()
+    _check("nvfp4_paged_decode_attn",
+           lib().nvfp4_paged_decode_attn(_ptr(q), _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, hq,
+                                         int(max_seq_len), ctypes.byref(d), float(sm_scale), int(num_splits),
+                                         _ptr(workspace), workspace.numel(), _ptr(out), odt, _ptr(lse),
+                                         _stream(stream)))
+    return out
+
+
+def nvfp4_kv_dequant_workspace(pool: Pool, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                               row_offsets: torch.Tensor, max_seq_len: int, k_out: torch.Tensor,
+                               v_out: torch.Tensor, stream=None):
+    """Writes K^, V^ rows [row_offsets[s] + t] of k_out / v_out ([rows, Hkv, 128],
+    bf16 or float32) for t < seq_lens[s]."""
+    if row_offsets.dtype != torch.int64:
+        raise ValueError("row_offsets must be int64")
+    if k_out.dtype != v_out.dtype or not k_out.is_contiguous() or not v_out.is_contiguous():
+        raise ValueError("k_out and v_out must be contiguous and share a dtype")
+    odt = {torch.float32: F32, torch.bfloat16: BF16}.get(k_out.dtype)
+    if odt is None:
+        raise ValueError("workspace dtype must be float32 or bfloat16")
+    d = pool.desc()
+    _check("nvfp4_kv_dequant_workspace",
+           lib().nvfp4_kv_dequant_workspace(ctypes.byref(d), _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
+                                            _ptr(row_offsets), seq_lens.numel(), int(max_seq_len), _ptr(k_out),
+                                            _ptr(v_out), odt, _stream(stream)))

@@ -1,0 +1,192 @@
+// Host side of the C ABI declared in include/nvfp4kv.h: argument validation (no
+// HIP call before it passes) and kernel launches.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "nvfp4kv.h"
+#include "nvfp4kv_device.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// g must be a power of two in [2^-64, 2^64]: then every threshold of the encode
+// rule and every decoded value stays an exact fp32 product.
+bool valid_global_scale(float g) {
+  if (!(g > 0.0f) || !isfinite(g)) return false;
+  int e;
+  const float m = frexpf(g, &e);
+  return m == 0.5f && e - 1 >= -64 && e - 1 <= 64;
+}
+
+int32_t check_pool(const nvfp4kv_pool* pool) {
+  if (!pool || !pool->data) return NVFP4KV_ERR_NULL;
+  if (pool->num_pages < 1 || pool->num_kv_heads < 1) return NVFP4KV_ERR_SHAPE;
+  if (pool->num_pages > ((int64_t)1 << 40) / ((int64_t)pool->num_kv_heads * 2 * NVFP4KV_SLAB_BYTES))
+    return NVFP4KV_ERR_SHAPE;
+  if (!aligned16(pool->data)) return NVFP4KV_ERR_ALIGN;
+  if (!valid_global_scale(pool->global_scale)) return NVFP4KV_ERR_VALUE;
+  return NVFP4KV_OK;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? NVFP4KV_OK : NVFP4KV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t nvfp4kv_pool_bytes(int64_t num_pages, int32_t num_kv_heads) {
+  if (num_pages < 0 || num_kv_heads < 0) return 0;
+  return num_pages * num_kv_heads * 2 * (int64_t)NVFP4KV_SLAB_BYTES;
+}
+
+const char* nvfp4kv_status_string(int32_t status) {
+  switch (status) {
+    case NVFP4KV_OK: return "ok";
+    case NVFP4KV_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4KV_ERR_SHAPE: return "a size, count or stride is out of range";
+    case NVFP4KV_ERR_ALIGN: return "a pointer or stride is not 16-byte aligned";
+    case NVFP4KV_ERR_DTYPE: return "unsupported dtype";
+    case NVFP4KV_ERR_WORKSPACE: return "workspace too small";
+    case NVFP4KV_ERR_VALUE: return "a float argument is out of its allowed set";
+    case NVFP4KV_ERR_HIP: return "a HIP runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t nvfp4kv_version(void) { return 1; }
+
+int32_t nvfp4_kv_quantize(const void* k_src, const void* v_src, int32_t src_dtype, int64_t token_stride,
+                          int64_t head_stride, const int32_t* slot_mapping, int64_t num_tokens,
+                          const nvfp4kv_pool* pool, void* stream) {
+  if (int32_t e = check_pool(pool)) return e;
+  if (src_dtype != NVFP4KV_F32 && src_dtype != NVFP4KV_BF16) return NVFP4KV_ERR_DTYPE;
+  if (num_tokens < 0 || token_stride < 0 || head_stride < 0) return NVFP4KV_ERR_SHAPE;
+  if (num_tokens == 0) return NVFP4KV_OK;
+  if (!k_src || !v_src || !slot_mapping) return NVFP4KV_ERR_NULL;
+  if (num_tokens > ((int64_t)1 << 31) * 256 / ((int64_t)pool->num_kv_heads * 16)) return NVFP4KV_ERR_SHAPE;
+  const int64_t vec = src_dtype == NVFP4KV_F32 ? 4 : 8;  // elements per 16 bytes
+  if (!aligned16(k_src) || !aligned16(v_src) || token_stride % vec || head_stride % vec ||
+      (reinterpret_cast<uintptr_t>(slot_mapping) & 3u))
+    return NVFP4KV_ERR_ALIGN;
+  nvfp4kv::QuantizeArgs a;
+  a.k = k_src;
+  a.v = v_src;
+  a.bf16 = src_dtype == NVFP4KV_BF16;
+  a.token_stride = token_stride;
+  a.head_stride = head_stride;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.pool = static_cast<uint8_t*>(pool->data);
+  a.num_kv_heads = pool->num_kv_heads;
+  a.g = pool->global_scale;
+  return hip_status(nvfp4kv::launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t nvfp4_paged_decode_attn_default_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
+                                               int32_t num_cus) {
+  if (batch < 1 || num_kv_heads < 1 || max_seq_len < 1) return 1;
+  if (num_cus <= 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    num_cus = cus;
+  }
+  const int64_t pages = (max_seq_len + NVFP4KV_PAGE_SIZE - 1) / NVFP4KV_PAGE_SIZE;
+  const int64_t units = (int64_t)batch * num_kv_heads;
+  const int64_t target_waves = (int64_t)num_cus * 16;  // resident one-wave work items per CU
+  int64_t s = (target_waves + units - 1) / units;
+  const int64_t max_by_pages = pages / 4 > 1 ? pages / 4 : 1;
+  if (s > max_by_pages) s = max_by_pages;
+  if (s > NVFP4KV_MAX_SPLITS) s = NVFP4KV_MAX_SPLITS;
+  if (s < 1) s = 1;
+  return (int32_t)s;
+}
+
+size_t nvfp4_paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_splits) {
+  if (batch < 0 || num_q_heads < 1 || num_splits < 1 || num_splits > NVFP4KV_MAX_SPLITS) return 0;
+  const size_t units = (size_t)batch * num_q_heads * num_splits;
+  const size_t o_bytes = units * NVFP4KV_HEAD_DIM * sizeof(float);
+  const size_t ml_bytes = units * 2 * sizeof(float);
+  return o_bytes + ((ml_bytes + 255) & ~(size_t)255);
+}
+
+int32_t nvfp4_paged_decode_attn(const void* q, const int32_t* page_table, int64_t page_table_stride,
+                                const int32_t* seq_lens, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
+                                const nvfp4kv_pool* pool, float sm_scale, int32_t num_splits, void* workspace,
+                                size_t workspace_bytes, void* out, int32_t out_dtype, float* lse, void* stream) {
+  if (int32_t e = check_pool(pool)) return e;
+  if (out_dtype != NVFP4KV_F32 && out_dtype != NVFP4KV_BF16) return NVFP4KV_ERR_DTYPE;
+  if (batch < 0 || num_q_heads < 1 || max_seq_len < 0 || page_table_stride < 1) return NVFP4KV_ERR_SHAPE;
+  const int32_t hkv = pool->num_kv_heads;
+  if (num_q_heads % hkv != 0) return NVFP4KV_ERR_SHAPE;
+  const int32_t group = num_q_heads / hkv;
+  if (group < 1 || group > NVFP4KV_MAX_GROUP) return NVFP4KV_ERR_SHAPE;
+  if ((int64_t)max_seq_len > page_table_stride * NVFP4KV_PAGE_SIZE) return NVFP4KV_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > NVFP4KV_MAX_SPLITS) return NVFP4KV_ERR_SHAPE;
+  if (batch > 65535 || hkv > 65535) return NVFP4KV_ERR_SHAPE;  // grid limits of the split kernel
+  if (!isfinite(sm_scale)) return NVFP4KV_ERR_VALUE;
+  if (batch == 0) return NVFP4KV_OK;
+  if (!q || !page_table || !seq_lens || !out || !workspace) return NVFP4KV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(page_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return NVFP4KV_ERR_ALIGN;
+  if (num_splits == 0) num_splits = nvfp4_paged_decode_attn_default_splits(batch, hkv, max_seq_len, 0);
+  const size_t need = nvfp4_paged_decode_attn_workspace_bytes(batch, num_q_heads, num_splits);
+  if (need == 0 || workspace_bytes < need) return NVFP4KV_ERR_WORKSPACE;
+
+  nvfp4kv::DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.page_table = page_table;
+  a.pt_stride = page_table_stride;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = hkv;
+  a.group = group;
+  a.max_seq_len = max_seq_len;
+  a.pool = static_cast<const uint8_t*>(pool->data);
+  a.qk_scale_log2 = (float)((double)sm_scale * 1.4426950408889634 * (double)pool->global_scale);
+  a.v_scale = pool->global_scale;
+  a.num_splits = num_splits;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = a.part_o + (size_t)batch * num_q_heads * num_splits * NVFP4KV_HEAD_DIM;
+  a.out = out;
+  a.out_bf16 = out_dtype == NVFP4KV_BF16;
+  a.lse = lse;
+  return hip_status(nvfp4kv::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page_table, int64_t page_table_stride,
+                                   const int32_t* seq_lens, const int64_t* row_offsets, int32_t n_seqs,
+                                   int32_t max_seq_len, void* k_out, void* v_out, int32_t out_dtype, void* stream) {
+  if (int32_t e = check_pool(pool)) return e;
+  if (out_dtype != NVFP4KV_F32 && out_dtype != NVFP4KV_BF16) return NVFP4KV_ERR_DTYPE;
+  if (n_seqs < 0 || max_seq_len < 0 || page_table_stride < 1) return NVFP4KV_ERR_SHAPE;
+  if ((int64_t)max_seq_len > page_table_stride * NVFP4KV_PAGE_SIZE) return NVFP4KV_ERR_SHAPE;
+  if (n_seqs > 65535 || pool->num_kv_heads > 65535) return NVFP4KV_ERR_SHAPE;
+  if (n_seqs == 0 || max_seq_len == 0) return NVFP4KV_OK;
+  if (!page_table || !seq_lens || !row_offsets || !k_out || !v_out) return NVFP4KV_ERR_NULL;
+  if (!aligned16(k_out) || !aligned16(v_out) || (reinterpret_cast<uintptr_t>(page_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(row_offsets) & 7u))
+    return NVFP4KV_ERR_ALIGN;
+  nvfp4kv::DequantArgs a;
+  a.pool = static_cast<const uint8_t*>(pool->data);
+  a.num_kv_heads = pool->num_kv_heads;
+  a.g = pool->global_scale;
+  a.page_table = page_table;
+  a.pt_stride = page_table_stride;
+  a.seq_lens = seq_lens;
+  a.row_offsets = row_offsets;
+  a.n_seqs = n_seqs;
+  a.max_seq_len = max_seq_len;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.out_bf16 = out_dtype == NVFP4KV_BF16;
+  return hip_status(nvfp4kv::launch_dequant(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// Extend-path dequantization of a cached NVFP4 prefix into a dense workspace
+// (gfx950).
+//
+// Page "SGLang stores KV cache in 4 bits ..." (section Interpretation): for
+// chunked prefill the cached prefix is dequantized into one workspace shared by
+// the layers and attended together with the current chunk.
+//
+// One wave per (page, KV head, sequence). K: lane (t, G) reads channels
+// 32G..32G+31 of token t (16 code bytes) and their two scale bytes; V: lane
+// (n, G) reads its 16-byte chunk (tokens 4G..4G+3 of pairs n, 16+n, 32+n, 48+n)
+// and the matching scale bytes. Values E2M1(c) * E4M3(s) * g are exact in fp32
+// and in bf16 (at most 6 significant bits), so the workspace is bit-exact.
+#include "nvfp4kv_device.h"
+
+namespace nvfp4kv {
+namespace {
+
+__device__ __forceinline__ void store2(void* base, size_t idx, float x, float y, bool bf16) {
+  if (bf16) {
+    const uint32_t p = (uint32_t)f32_to_bf16_bits(x) | ((uint32_t)f32_to_bf16_bits(y) << 16);
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(base) + idx) = p;
+  } else {
+    *reinterpret_cast<float2*>(static_cast<float*>(base) + idx) = make_float2(x, y);
+  }
+}
+
+template <int SEL>
+__device__ __forceinline__ f32x2 dq2(uint32_t w, float scale) {
+  f32x2 v = fp4x2_to_f32x2<SEL>(w);
+  return v * scale;
+}
+
+__global__ __launch_bounds__(64) void k_dequant(DequantArgs a) {
+  const int pg = blockIdx.x;
+  const int h = blockIdx.y;
+  const int s = blockIdx.z;
+  const int L = a.seq_lens[s];
+  if (pg * kPage >= L) return;
+  const int lane = threadIdx.x;
+  const int n = lane & 15;
+  const int G = lane >> 4;
+  const int64_t pid = a.page_table[(int64_t)s * a.pt_stride + pg];
+  const uint8_t* kslab = a.pool + (pid * a.num_kv_heads + h) * (int64_t)(2 * kSlab);
+  const uint8_t* vslab = kslab + kSlab;
+  const int64_t row0 = a.row_offsets[s] + (int64_t)pg * kPage;
+  const int H = a.num_kv_heads;
+  const bool bf16 = a.out_bf16 != 0;
+
+  // ---- K: token n, channels 32G..32G+31 ----
+  if (pg * kPage + n < L) {
+    const uint4 kc = *reinterpret_cast<const uint4*>(kslab + n * 64 + G * 16);
+    const uint32_t ks = *reinterpret_cast<const uint16_t*>(kslab + kCodeBytes + n * 8 + G * 2);
+    const float sc0 = e4m3_to_f32(ks & 0xFFu) * a.g;
+    const float sc1 = e4m3_to_f32(ks >> 8) * a.g;
+    const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
+    const size_t base = ((size_t)(row0 + n) * H + h) * kHeadDim + 32 * G;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float sc = w < 2 ? sc0 : sc1;
+      const f32x2 v0 = dq2<0>(kw[w], sc), v1 = dq2<1>(kw[w], sc), v2 = dq2<2>(kw[w], sc), v3 = dq2<3>(kw[w], sc);
+      store2(a.k_out, base + 8 * w + 0, v0[0], v0[1], bf16);
+      store2(a.k_out, base + 8 * w + 2, v1[0], v1[1], bf16);
+      store2(a.k_out, base + 8 * w + 4, v2[0], v2[1], bf16);
+      store2(a.k_out, base + 8 * w + 6, v3[0], v3[1], bf16);
+    }
+  }
+
+  // ---- V: tokens 4G..4G+3, channel pairs 16q + n ----
+  {
+    const uint4 vc = *reinterpret_cast<const uint4*>(vslab + (n * 4 + G) * 16);
+    const uint4 vs = *reinterpret_cast<const uint4*>(vslab + kCodeBytes + (G * 2 + (n >> 3)) * 16);
+    const uint32_t vw[4] = {vc.x, vc.y, vc.z, vc.w};
+    const uint32_t vsw[4] = {vs.x, vs.y, vs.z, vs.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = 32 * q + 2 * n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 4 * G + i;
+        if (pg * kPage + tok >= L) continue;
+        const float sc = e4m3_to_f32((vsw[q] >> (8 * i)) & 0xFFu) * a.g;
+        f32x2 v;
+        switch (i) {
+          case 0: v = dq2<0>(vw[q], sc); break;
+          case 1: v = dq2<1>(vw[q], sc); break;
+          case 2: v = dq2<2>(vw[q], sc); break;
+          default: v = dq2<3>(vw[q], sc); break;
+        }
+        store2(a.v_out, ((size_t)(row0 + tok) * H + h) * kHeadDim + d, v[0], v[1], bf16);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream) {
+  const int max_pages = (a.max_seq_len + kPage - 1) / kPage;
+  if (a.n_seqs == 0 || max_pages == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_dequant, dim3(max_pages, a.num_kv_heads, a.n_seqs), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4kv

@@ -1,0 +1,110 @@
+// Internal declarations shared by the HIP sources of libnvfp4kv (not part of the
+// public C ABI, see include/nvfp4kv.h for the contract and the pool layout).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4kv {
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 16;
+constexpr int kSlab = 1152;     // bytes of one (page, head, K|V) slab
+constexpr int kCodeBytes = 1024;
+constexpr int kMaxGroup = 16;
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+struct QuantizeArgs {
+  const void* k;
+  const void* v;
+  int32_t bf16;            // 1: sources are bfloat16, 0: float32
+  int64_t token_stride;    // elements
+  int64_t head_stride;     // elements
+  const int32_t* slots;
+  int64_t num_tokens;
+  uint8_t* pool;
+  int32_t num_kv_heads;
+  float g;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;       // bf16 bits [B][Hq][128]
+  const int32_t* page_table;
+  int64_t pt_stride;
+  const int32_t* seq_lens;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;           // Hq / Hkv
+  int32_t max_seq_len;
+  const uint8_t* pool;
+  float qk_scale_log2;     // sm_scale * log2(e) * g
+  float v_scale;           // g
+  int32_t num_splits;
+  float* part_o;           // [B][Hq][S][128]
+  float* part_ml;          // [B][Hq][S][2]: running max (log2 units), sum
+  void* out;
+  int32_t out_bf16;
+  float* lse;
+};
+
+struct DequantArgs {
+  const uint8_t* pool;
+  int32_t num_kv_heads;
+  float g;
+  const int32_t* page_table;
+  int64_t pt_stride;
+  const int32_t* seq_lens;
+  const int64_t* row_offsets;
+  int32_t n_seqs;
+  int32_t max_seq_len;
+  void* k_out;
+  void* v_out;
+  int32_t out_bf16;
+};
+
+hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
+
+// ---- device helpers --------------------------------------------------------
+
+// Decode of an E4M3 (OCP fn) byte held in bits 0..7 of `b` to float (exact).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  return __builtin_amdgcn_cvt_f32_fp8(b, 0);
+}
+
+// f16 bit pattern of E4M3(b) / 256 for a non-negative finite byte b (0..0x7E):
+// the byte's exponent and mantissa fields land in the f16 fields unchanged, which
+// re-biases the exponent by 8 (normal bytes) and maps subnormal bytes onto f16
+// subnormals with the same factor. Exact for every byte 0..0x7E.
+__device__ __forceinline__ uint32_t e4m3_f16bits_div256(uint32_t b) { return b << 7; }
+
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+
+// Two E2M1 codes (byte `sel` of w: low nibble first) to two f16 values, unscaled.
+template <int SEL>
+__device__ __forceinline__ f16x2 fp4x2_to_f16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+template <int SEL>
+__device__ __forceinline__ f32x2 fp4x2_to_f32x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+}  // namespace nvfp4kv

@@ -1,0 +1,130 @@
+// Quantize-on-write of K/V rows into the NVFP4 page pool (gfx950).
+//
+// Page "SGLang stores KV cache in 4 bits ..." (section Interpretation): initial
+// prefill quantizes the prompt's keys and values into the NVFP4 cache; each block
+// of 16 values keeps 8 bytes of packed codes and 1 byte of scale. Page
+// "NVFP4-KV-Cache auf der NVIDIA RTX PRO 6000 Blackwell Server Edition" (section
+// "Bytes pro Token"): E2M1 values, one E4M3 scale per 16 values, one FP32 scale
+// per tensor.
+//
+// One thread encodes one 16-value block (token, KV head, K|V, block). Every
+// rounding decision is taken by exact comparisons in fp32: the thresholds are
+// products of numbers with few significant bits and a power-of-two global scale,
+// so no quotient is ever rounded. This realizes "nearest, ties to even" on the
+// exact real quotients amax/(6g) and x/(E4M3(s) g).
+#include "nvfp4kv_device.h"
+
+namespace nvfp4kv {
+namespace {
+
+// E4M3 value of a non-negative finite byte k (0..126), exact in fp32.
+__device__ __forceinline__ float e4m3_value(int k) {
+  return k < 8 ? (float)k * 0x1p-9f : __builtin_ldexpf((float)(8 + (k & 7)), (k >> 3) - 10);
+}
+
+// Byte of the E4M3 value nearest to amax / six_g (six_g = 6 g), ties to the even
+// byte, clamped to 448 (0x7E). Binary search for the first midpoint between
+// consecutive E4M3 values that amax does not pass; a tie passes the midpoint
+// only when its lower neighbour is odd.
+__device__ __forceinline__ int scale_byte(float amax, float six_g) {
+  int lo = 0, hi = 126;
+#pragma unroll
+  for (int it = 0; it < 7; ++it) {
+    if (lo < hi) {
+      const int k = (lo + hi) >> 1;
+      const float thr = (0.5f * (e4m3_value(k) + e4m3_value(k + 1))) * six_g;
+      const bool pass = amax > thr || (amax == thr && (k & 1));
+      lo = pass ? k + 1 : lo;
+      hi = pass ? hi : k;
+    }
+  }
+  return lo;
+}
+
+// E2M1 code of x for block divisor D = E4M3(s) g: count of the magnitude
+// midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 (times D) that |x| passes, where
+// a tie passes only midpoints whose lower code is odd; sign bit from x.
+__device__ __forceinline__ uint32_t e2m1_code(float x, float D, bool zero_scale) {
+  const uint32_t sign = (__float_as_uint(x) >> 28) & 8u;
+  const float ax = __builtin_fabsf(x);
+  uint32_t c = (uint32_t)(ax > 0.25f * D) + (uint32_t)(ax >= 0.75f * D) + (uint32_t)(ax > 1.25f * D) +
+               (uint32_t)(ax >= 1.75f * D) + (uint32_t)(ax > 2.5f * D) + (uint32_t)(ax >= 3.5f * D) +
+               (uint32_t)(ax > 5.0f * D);
+  c = zero_scale ? 0u : c;
+  return sign | c;
+}
+
+__global__ __launch_bounds__(256) void k_quantize(QuantizeArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_token = (int64_t)a.num_kv_heads * 16;
+  if (idx >= a.num_tokens * per_token) return;
+  const int64_t t = idx / per_token;
+  const int rem = (int)(idx - t * per_token);
+  const int h = rem >> 4;
+  const int kind = (rem >> 3) & 1;
+  const int j = rem & 7;
+  const int32_t slot = a.slots[t];
+  if (slot < 0) return;
+
+  const int64_t off = t * a.token_stride + (int64_t)h * a.head_stride + j * 16;
+  float x[16];
+  if (a.bf16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(kind ? a.v : a.k) + off);
+    const uint4 u0 = p[0], u1 = p[1];
+    const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(kind ? a.v : a.k) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 f = p[i];
+      x[4 * i] = f.x;
+      x[4 * i + 1] = f.y;
+      x[4 * i + 2] = f.z;
+      x[4 * i + 3] = f.w;
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+
+  const int s = scale_byte(amax, 6.0f * a.g);
+  const float D = e4m3_value(s) * a.g;
+  const bool zs = (s == 0);
+  uint32_t bytes[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bytes[i] = e2m1_code(x[2 * i], D, zs) | (e2m1_code(x[2 * i + 1], D, zs) << 4);
+
+  const int64_t page = slot >> 4;
+  const int row = slot & 15;
+  uint8_t* slab = a.pool + ((page * a.num_kv_heads + h) * 2 + kind) * (int64_t)kSlab;
+  if (kind == 0) {
+    const uint32_t lo = bytes[0] | (bytes[1] << 8) | (bytes[2] << 16) | (bytes[3] << 24);
+    const uint32_t hi = bytes[4] | (bytes[5] << 8) | (bytes[6] << 16) | (bytes[7] << 24);
+    *reinterpret_cast<uint2*>(slab + row * 64 + j * 8) = make_uint2(lo, hi);
+    slab[kCodeBytes + row * 8 + j] = (uint8_t)s;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int pair = 8 * j + k;
+      slab[((pair & 15) * 4 + (row >> 2)) * 16 + (pair >> 4) * 4 + (row & 3)] = (uint8_t)bytes[k];
+    }
+    slab[kCodeBytes + ((row >> 2) * 2 + (j & 1)) * 16 + (j >> 1) * 4 + (row & 3)] = (uint8_t)s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
+  const int64_t threads = a.num_tokens * a.num_kv_heads * 16;
+  if (threads == 0) return hipSuccess;
+  const int64_t blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL(k_quantize, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4kv

@@ -1,0 +1,200 @@
+/*
+ * nvfp4kv.h — C ABI of the NVFP4 paged-KV attention library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Pages cited (by title and section):
+ *   [LMSYS]  "SGLang stores KV cache in 4 bits: long-context decode throughput
+ *            rises 26-30%, and FP8 stalls first under agent concurrency"
+ *            (summary of the LMSYS post "Accelerating Long-Context and Agentic
+ *            Inference with NVFP4 KV Cache").
+ *   [EUROK]  "NVFP4-KV-Cache auf der NVIDIA RTX PRO 6000 Blackwell Server
+ *            Edition: Genauigkeit, Nutzer".
+ *
+ * The library computes three things on the GPU, each in hand-written HIP:
+ *   - nvfp4_kv_quantize: quantize-on-write of K/V rows into the NVFP4 pool
+ *     ([LMSYS] "Interpretation": initial prefill quantizes the prompt's keys and
+ *     values into the NVFP4 cache).
+ *   - nvfp4_paged_decode_attn: grouped-query decode attention that reads the
+ *     paged NVFP4 cache and dequantizes it inside the kernel ([LMSYS]
+ *     "Interpretation"; [EUROK] "Geschwindigkeit": the decode kernel takes 16-bit
+ *     queries and NVFP4 keys and values).
+ *   - nvfp4_kv_dequant_workspace: the extend path's dequantization of a cached
+ *     prefix into a dense workspace ([LMSYS] "Interpretation").
+ *
+ * NVFP4 ([EUROK] "Bytes pro Token"; [LMSYS] "Interpretation", "Perspective"):
+ * each value is E2M1 (1 sign, 2 exponent, 1 mantissa bit; magnitudes 0, 0.5, 1,
+ * 1.5, 2, 3, 4, 6); each 16 contiguous values of a head row share one E4M3 (OCP
+ * "fn", max 448) block scale s; a per-tensor float global scale g sits above
+ * (1.0 in every experiment the pages report). A value decodes to
+ * E2M1(c) * E4M3(s) * g. Encoding: s = E4M3 nearest to amax/(6 g), ties to
+ * even, clamped to 448; c = E2M1 nearest to x/(E4M3(s) g), ties to even,
+ * saturating at 6, sign bit = sign bit of x; a zero scale gives magnitude-0
+ * codes. 8 code bytes + 1 scale byte per 16 values.
+ *
+ * Pool layout (NVFP4KV_SLAB_BYTES = 1152 per slab):
+ *   slab(page p, KV head h, kind k) starts at byte ((p*Hkv + h)*2 + k) * 1152,
+ *   k = 0 for K, 1 for V. A slab holds the 16 token rows r of page p for head h:
+ *   1024 code bytes, then 128 scale bytes. Code byte of pair i (channels 2i in
+ *   the low nibble, 2i+1 in the high nibble) and scale byte of block j
+ *   (channels 16j..16j+15):
+ *     K:  code (r, i) at r*64 + i            scale (r, j) at 1024 + r*8 + j
+ *     V:  code (r, i) at ((i%16)*4 + r/4)*16 + (i/16)*4 + r%4
+ *         scale (r, j) at 1024 + ((r/4)*2 + j%2)*16 + (j/2)*4 + r%4
+ *   K rows are token-major. V is grouped so that each 16-byte chunk holds four
+ *   consecutive tokens of four channel pairs, the shape the decode kernel's
+ *   matrix-core operands take; every byte still belongs to one token, so
+ *   writing a token never touches another token's bytes.
+ *   Token t of a sequence lives at page page_table[t/16], row t%16.
+ *
+ * Conventions for every entry point:
+ *   - The caller owns all memory; the library allocates nothing, keeps no
+ *     global mutable state, and is reentrant.
+ *   - Arguments named *device* are device pointers; the pool descriptor is a
+ *     host pointer to a struct whose data member is a device pointer.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and returns without synchronizing.
+ *   - Every host-side check runs before any HIP call; on error nothing is
+ *     enqueued and a status > 0 is returned. Device-side data errors (a page id
+ *     outside the pool, seq_lens[b] > max_seq_len or beyond the page table row,
+ *     a slot outside the pool) are undefined behaviour.
+ */
+#ifndef NVFP4KV_H_
+#define NVFP4KV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4KV_HEAD_DIM 128
+#define NVFP4KV_PAGE_SIZE 16
+#define NVFP4KV_SLAB_BYTES 1152
+#define NVFP4KV_MAX_GROUP 16     /* query heads per KV head */
+#define NVFP4KV_MAX_SPLITS 4096
+#define NVFP4KV_ALIGN 16         /* required alignment (bytes) of every device pointer */
+
+enum nvfp4kv_status {
+  NVFP4KV_OK = 0,
+  NVFP4KV_ERR_NULL = 1,      /* a required pointer is NULL */
+  NVFP4KV_ERR_SHAPE = 2,     /* a size, count or stride is out of range */
+  NVFP4KV_ERR_ALIGN = 3,     /* a pointer or stride breaks the 16-byte rule */
+  NVFP4KV_ERR_DTYPE = 4,     /* unsupported dtype code */
+  NVFP4KV_ERR_WORKSPACE = 5, /* workspace smaller than required */
+  NVFP4KV_ERR_VALUE = 6,     /* a float argument is not allowed (e.g. global scale) */
+  NVFP4KV_ERR_HIP = 7        /* a HIP runtime call failed */
+};
+
+enum nvfp4kv_dtype { NVFP4KV_F32 = 0, NVFP4KV_BF16 = 1 };
+
+/* NVFP4 KV pool of one layer. */
+typedef struct nvfp4kv_pool {
+  void* data;            /* device, 16-byte aligned, num_pages*num_kv_heads*2*1152 bytes */
+  int64_t num_pages;     /* >= 1 */
+  int32_t num_kv_heads;  /* >= 1 */
+  float global_scale;    /* g: a power of two in [2^-64, 2^64] (1.0 in all workloads) */
+} nvfp4kv_pool;
+
+/* Bytes of a pool of num_pages pages and num_kv_heads heads. */
+int64_t nvfp4kv_pool_bytes(int64_t num_pages, int32_t num_kv_heads);
+
+/* Static string for a status code (never NULL). */
+const char* nvfp4kv_status_string(int32_t status);
+
+/* Library ABI version (incremented on any signature or layout change). */
+int32_t nvfp4kv_version(void);
+
+/*
+ * Quantize-on-write ([LMSYS] "Interpretation"; format per [EUROK] "Bytes pro
+ * Token"). For each token t < num_tokens with slot_mapping[t] >= 0 and each KV
+ * head h, encodes K[t][h][0..127] and V[t][h][0..127] as 8 NVFP4 blocks each and
+ * writes codes and scales to page slot/16, row slot%16 of `pool` (layout above).
+ * Tokens with a negative slot are skipped. Output bytes are a deterministic
+ * function of the inputs (no atomics); distinct tokens must map to distinct slots.
+ *   k_src, v_src    device; element (t, h, d) at t*token_stride + h*head_stride + d
+ *                   (elements), float32 or bfloat16 per src_dtype
+ *   src_dtype       NVFP4KV_F32 or NVFP4KV_BF16
+ *   token_stride,
+ *   head_stride     elements; multiples of 4 (F32) or 8 (BF16)
+ *   slot_mapping    device int32 [num_tokens]
+ *   num_tokens      >= 0 (0 is a no-op)
+ * Errors: NULL pointers (ERR_NULL); bad dtype (ERR_DTYPE); unaligned pointer or
+ * stride (ERR_ALIGN); negative sizes, a non-positive page or head count
+ * (ERR_SHAPE); global scale not a power of two in range (ERR_VALUE).
+ */
+int32_t nvfp4_kv_quantize(const void* k_src, const void* v_src, int32_t src_dtype, int64_t token_stride,
+                          int64_t head_stride, const int32_t* slot_mapping, int64_t num_tokens,
+                          const nvfp4kv_pool* pool, void* stream);
+
+/*
+ * Split count the decode call uses when passed num_splits = 0: enough
+ * (sequence, KV head, split) work items to fill num_cus compute units, at least
+ * 4 pages per split, at most NVFP4KV_MAX_SPLITS. num_cus <= 0 asks the current
+ * HIP device for its compute-unit count (the only HIP call of this function).
+ * Returns >= 1.
+ */
+int32_t nvfp4_paged_decode_attn_default_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
+                                               int32_t num_cus);
+
+/* Workspace bytes the decode call needs for the given sizes (num_splits >= 1;
+ * pass the resolved split count). Returns 0 for invalid sizes. */
+size_t nvfp4_paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_splits);
+
+/*
+ * Decode attention over the paged NVFP4 cache ([LMSYS] "Interpretation": decode
+ * dequantizes inside the attention kernel; [EUROK] "Geschwindigkeit"; grouped-
+ * query attention per [EUROK] "Unterstuetzung in den Engines"). For each
+ * sequence b and query head qh (KV head h = qh / (num_q_heads / num_kv_heads)):
+ *   out[b][qh] = sum_t softmax_t(sm_scale * q[b][qh] . K^[t]) V^[t],
+ *   t < seq_lens[b], K^/V^ the dequantized cache of head h,
+ *   lse[b][qh] = natural-log log-sum-exp of the scaled logits.
+ * Split-K flash decoding: num_splits ranges of pages per (b, h) are reduced with
+ * an online softmax into the workspace, then combined. A sequence of length 0
+ * yields out = 0 and lse = -inf.
+ *   q               device bf16 [batch][num_q_heads][128], row-major
+ *   page_table      device int32 [batch][page_table_stride] physical page ids
+ *   seq_lens        device int32 [batch], each in [0, max_seq_len]
+ *   max_seq_len     host upper bound of seq_lens (<= page_table_stride*16)
+ *   pool            host pointer to the pool descriptor
+ *   sm_scale        finite softmax scale (1/sqrt(128) in the workloads)
+ *   num_splits      0 = nvfp4_paged_decode_attn_default_splits(..., 0), or 1..4096
+ *   workspace       device scratch of >= nvfp4_paged_decode_attn_workspace_bytes
+ *                   bytes for the resolved split count; contents are overwritten
+ *   out             device [batch][num_q_heads][128], bf16 or f32 per out_dtype
+ *   lse             device f32 [batch][num_q_heads], or NULL
+ * Limits: num_q_heads % num_kv_heads == 0, 1 <= num_q_heads/num_kv_heads <= 16.
+ * Errors: ERR_NULL, ERR_SHAPE (sizes, group, splits, strides), ERR_ALIGN,
+ * ERR_DTYPE (out_dtype), ERR_WORKSPACE, ERR_VALUE (sm_scale not finite, global
+ * scale), ERR_HIP (launch failure, or the CU-count query when num_splits = 0).
+ */
+int32_t nvfp4_paged_decode_attn(const void* q, const int32_t* page_table, int64_t page_table_stride,
+                                const int32_t* seq_lens, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
+                                const nvfp4kv_pool* pool, float sm_scale, int32_t num_splits, void* workspace,
+                                size_t workspace_bytes, void* out, int32_t out_dtype, float* lse, void* stream);
+
+/*
+ * Extend-path dequantization ([LMSYS] "Interpretation": the cached prefix is
+ * dequantized into one workspace shared across layers and attended alongside the
+ * current chunk). For each listed sequence s and t < seq_lens[s], writes the
+ * dequantized K and V rows of every KV head to row row_offsets[s] + t of the
+ * dense workspaces k_out / v_out, shaped [rows][num_kv_heads][128]. The values
+ * are exact in both output dtypes (at most 6 significant bits).
+ *   page_table      device int32 [n_seqs][page_table_stride]
+ *   seq_lens        device int32 [n_seqs], prefix tokens to dequantize, each in
+ *                   [0, max_seq_len]
+ *   row_offsets     device int64 [n_seqs], first workspace row of each sequence
+ *   max_seq_len     host upper bound of seq_lens (<= page_table_stride*16)
+ *   k_out, v_out    device, bf16 or f32 per out_dtype
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_VALUE (global scale),
+ * ERR_HIP.
+ */
+int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page_table, int64_t page_table_stride,
+                                   const int32_t* seq_lens, const int64_t* row_offsets, int32_t n_seqs,
+                                   int32_t max_seq_len, void* k_out, void* v_out, int32_t out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4KV_H_ */

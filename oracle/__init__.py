@@ -70,7 +70,8 @@ def _load(path: str) -> ctypes.CDLL:
     L.orc_scale_byte_offset.restype = c.c_int
     L.orc_pool_bytes.argtypes = [c.c_int64, c.c_int]
     L.orc_pool_bytes.restype = c.c_int64
-    L.orc_quantize_to_pool.argtypes = [P, P, c.c_int, c.c_int64, c.c_int64, P, c.c_int, c.c_int, c.c_float, P]
+    L.orc_quantize_to_pool.argtypes = [P, P, c.c_int, c.c_int64, c.c_int64, P, c.c_int64, c.c_int, c.c_float, P,
+                                       c.c_int]
     L.orc_quantize_to_pool.restype = None
     L.orc_dequant_row.argtypes = [P, c.c_int64, c.c_int, c.c_int, c.c_int, c.c_int, c.c_float, P]
     L.orc_dequant_row.restype = None
@@ -174,7 +175,7 @@ def slab_offset(page: int, head: int, kind: int, num_kv_heads: int) -> int:
 
 # ---- pool-level functions --------------------------------------------------
 def quantize_to_pool(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray, num_pages: int,
-                     g: float = 1.0, pool: np.ndarray | None = None) -> np.ndarray:
+                     g: float = 1.0, pool: np.ndarray | None = None, n_threads: int = 1) -> np.ndarray:
     """K, V: [T, Hkv, 128] float32 or bf16 bits (np.uint16). Returns/updates a
     uint8 pool of num_pages pages."""
     assert k.shape == v.shape and k.ndim == 3 and k.shape[2] == HEAD_DIM
@@ -192,7 +193,7 @@ def quantize_to_pool(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray, num
         pool = np.zeros(pool_bytes(num_pages, hkv), dtype=np.uint8)
     assert pool.nbytes == pool_bytes(num_pages, hkv)
     lib().orc_quantize_to_pool(_ptr(k), _ptr(v), dt, hkv * HEAD_DIM, HEAD_DIM, _ptr(sm), T, hkv,
-                               float(g), _ptr(pool))
+                               float(g), _ptr(pool), int(n_threads))
     return pool
 
 

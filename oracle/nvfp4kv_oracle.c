@@ -86,6 +86,15 @@ double orc_e4m3_value(int byte) {
   return sign ? -mag : mag;
 }
 
+/* Tables of the step-1 and step-2 values, filled once at load time. */
+static double orc_e4m3_table[127];
+static double orc_e2m1_table[8];
+__attribute__((constructor)) static void orc_fill_tables(void) {
+  int k;
+  for (k = 0; k < 127; ++k) orc_e4m3_table[k] = orc_e4m3_value(k);
+  for (k = 0; k < 8; ++k) orc_e2m1_table[k] = orc_e2m1_value(k);
+}
+
 /* ---- 3. block scale: nearest E4M3 to amax / den, ties even, satfinite ---- */
 /* Walks the 127 non-negative finite E4M3 values upward; the result moves past
  * value k exactly when amax/den lies above the midpoint of k and k+1, or on it
@@ -94,7 +103,7 @@ double orc_e4m3_value(int byte) {
 int orc_e4m3_nearest_of_quotient(double amax, double den) {
   int k = 0;
   while (k < 126) {
-    double mid = 0.5 * (orc_e4m3_value(k) + orc_e4m3_value(k + 1));
+    double mid = 0.5 * (orc_e4m3_table[k] + orc_e4m3_table[k + 1]);
     double thr = den * mid;
     if (amax > thr || (amax == thr && (k & 1)))
       ++k;
@@ -115,7 +124,7 @@ int orc_e2m1_code(float x, double D) {
   int k = 0;
   if (D == 0.0) return sign; /* zero scale: magnitude 0, sign kept */
   while (k < 7) {
-    double mid = 0.5 * (orc_e2m1_value(k) + orc_e2m1_value(k + 1));
+    double mid = 0.5 * (orc_e2m1_table[k] + orc_e2m1_table[k + 1]);
     double thr = D * mid;
     if (ax > thr || (ax == thr && (k & 1)))
       ++k;
@@ -168,35 +177,78 @@ static float orc_bf16_to_float(uint16_t b) {
 
 /* Quantize-on-write of T tokens of K and V ([T][Hkv][128], element strides
  * given) into the pool at slot_mapping[t] = page*16 + row (negative = skip).
- * src_dtype 0 = float32, 1 = bfloat16 bits. */
-void orc_quantize_to_pool(const void* k_src, const void* v_src, int src_dtype, int64_t token_stride,
-                          int64_t head_stride, const int32_t* slot_mapping, int num_tokens,
-                          int num_kv_heads, float g, uint8_t* pool) {
-  int t, h, kind, j, i;
-  for (t = 0; t < num_tokens; ++t) {
-    int32_t slot = slot_mapping[t];
+ * src_dtype 0 = float32, 1 = bfloat16 bits. Tokens are spread over n_threads
+ * threads; each token's bytes are computed the same way by any thread. */
+typedef struct {
+  const void *k_src, *v_src;
+  int src_dtype;
+  int64_t token_stride, head_stride;
+  const int32_t* slot_mapping;
+  int64_t t_begin, t_end;
+  int num_kv_heads;
+  float g;
+  uint8_t* pool;
+} orc_quant_job;
+
+static void* orc_quant_worker(void* arg) {
+  orc_quant_job* J = (orc_quant_job*)arg;
+  int64_t t;
+  int h, kind, j, i;
+  for (t = J->t_begin; t < J->t_end; ++t) {
+    int32_t slot = J->slot_mapping[t];
     if (slot < 0) continue;
     int64_t page = slot / ORC_PAGE;
     int row = slot % ORC_PAGE;
-    for (h = 0; h < num_kv_heads; ++h) {
+    for (h = 0; h < J->num_kv_heads; ++h) {
       for (kind = 0; kind < 2; ++kind) {
-        const void* src = kind == 0 ? k_src : v_src;
-        uint8_t* slab = pool + orc_slab_offset(page, h, kind, num_kv_heads);
+        const void* src = kind == 0 ? J->k_src : J->v_src;
+        uint8_t* slab = J->pool + orc_slab_offset(page, h, kind, J->num_kv_heads);
         for (j = 0; j < 8; ++j) {
           float x[16];
           uint8_t codes[8], s;
           for (i = 0; i < 16; ++i) {
-            int64_t idx = t * token_stride + h * head_stride + 16 * j + i;
-            x[i] = src_dtype == 0 ? ((const float*)src)[idx]
-                                  : orc_bf16_to_float(((const uint16_t*)src)[idx]);
+            int64_t idx = t * J->token_stride + h * J->head_stride + 16 * j + i;
+            x[i] = J->src_dtype == 0 ? ((const float*)src)[idx]
+                                     : orc_bf16_to_float(((const uint16_t*)src)[idx]);
           }
-          orc_quantize_block16(x, g, codes, &s);
+          orc_quantize_block16(x, J->g, codes, &s);
           for (i = 0; i < 8; ++i) slab[orc_code_byte_offset(kind, row, 8 * j + i)] = codes[i];
           slab[orc_scale_byte_offset(kind, row, j)] = s;
         }
       }
     }
   }
+  return NULL;
+}
+
+void orc_quantize_to_pool(const void* k_src, const void* v_src, int src_dtype, int64_t token_stride,
+                          int64_t head_stride, const int32_t* slot_mapping, int64_t num_tokens,
+                          int num_kv_heads, float g, uint8_t* pool, int n_threads) {
+  orc_quant_job jobs[256];
+  pthread_t th[256];
+  int i;
+  if (n_threads < 1) n_threads = 1;
+  if (n_threads > 256) n_threads = 256;
+  for (i = 0; i < n_threads; ++i) {
+    orc_quant_job* J = &jobs[i];
+    J->k_src = k_src;
+    J->v_src = v_src;
+    J->src_dtype = src_dtype;
+    J->token_stride = token_stride;
+    J->head_stride = head_stride;
+    J->slot_mapping = slot_mapping;
+    J->t_begin = num_tokens * i / n_threads;
+    J->t_end = num_tokens * (i + 1) / n_threads;
+    J->num_kv_heads = num_kv_heads;
+    J->g = g;
+    J->pool = pool;
+  }
+  if (n_threads == 1) {
+    orc_quant_worker(&jobs[0]);
+    return;
+  }
+  for (i = 0; i < n_threads; ++i) pthread_create(&th[i], NULL, orc_quant_worker, &jobs[i]);
+  for (i = 0; i < n_threads; ++i) pthread_join(th[i], NULL);
 }
 
 /* ---- 6. dequantize one token row of one head ------------------------------ */

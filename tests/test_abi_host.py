@@ -1,0 +1,140 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every symbol the header
+declares, and its host validation rejects bad arguments before any HIP call (no
+compute call is made here; device pointers are fake, never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_paged_kv_nvfp4_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4kv.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_VALUE, ERR_HIP = range(8)
+FAKE = 0x10000  # 16-byte aligned, never dereferenced by validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(nvfp4[a-z_0-9]*)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        import bit_paged_kv_nvfp4_amd.build as bld
+
+        bld.build()
+    return B.lib()
+
+
+def pool(num_pages=4, hkv=1, g=1.0, data=FAKE):
+    return B.PoolDesc(data, num_pages, hkv, g)
+
+
+def test_exports_every_declared_symbol(L):
+    decl = declared_functions()
+    assert set(decl) == set(B.EXPORTED), decl
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_constants_and_strings(L):
+    assert L.nvfp4kv_version() == 1
+    assert L.nvfp4kv_pool_bytes(10, 8) == 10 * 8 * 2 * 1152
+    for s in range(8):
+        assert len(B.status_string(s)) > 0
+    assert B.status_string(99) == "unknown status"
+
+
+def test_default_splits_and_workspace_size(L):
+    assert L.nvfp4_paged_decode_attn_default_splits(44, 8, 32768, 256) >= 8
+    assert L.nvfp4_paged_decode_attn_default_splits(1, 1, 16, 256) == 1
+    assert L.nvfp4_paged_decode_attn_default_splits(2, 8, 1048576, 256) <= 4096
+    s = L.nvfp4_paged_decode_attn_default_splits(15, 8, 163840, 256)
+    assert 1 <= s <= 163840 // 16 // 4
+    ws = L.nvfp4_paged_decode_attn_workspace_bytes(3, 16, 5)
+    assert ws >= 3 * 16 * 5 * 130 * 4
+    assert L.nvfp4_paged_decode_attn_workspace_bytes(3, 16, 0) == 0
+    assert L.nvfp4_paged_decode_attn_workspace_bytes(3, 16, 5000) == 0
+
+
+def q_call(L, p, k=FAKE, v=FAKE, dt=0, ts=1024, hs=128, slots=FAKE, T=16):
+    return L.nvfp4_kv_quantize(k, v, dt, ts, hs, slots, T, ctypes.byref(p) if p is not None else None, None)
+
+
+def test_quantize_validation(L):
+    assert q_call(L, None) == ERR_NULL
+    assert q_call(L, pool(data=0)) == ERR_NULL
+    assert q_call(L, pool(data=FAKE + 8)) == ERR_ALIGN
+    assert q_call(L, pool(num_pages=0)) == ERR_SHAPE
+    assert q_call(L, pool(hkv=0)) == ERR_SHAPE
+    assert q_call(L, pool(g=3.0)) == ERR_VALUE
+    assert q_call(L, pool(g=float("nan"))) == ERR_VALUE
+    assert q_call(L, pool(g=2.0 ** 70)) == ERR_VALUE
+    assert q_call(L, pool(), dt=2) == ERR_DTYPE
+    assert q_call(L, pool(), T=-1) == ERR_SHAPE
+    assert q_call(L, pool(), T=0) == OK  # no-op, no HIP call
+    assert q_call(L, pool(), k=None) == ERR_NULL
+    assert q_call(L, pool(), slots=None) == ERR_NULL
+    assert q_call(L, pool(), k=FAKE + 4) == ERR_ALIGN
+    assert q_call(L, pool(), ts=1026) == ERR_ALIGN
+    assert q_call(L, pool(), dt=1, hs=132) == ERR_ALIGN
+    assert q_call(L, pool(), slots=FAKE + 2) == ERR_ALIGN
+
+
+def d_call(L, p, q=FAKE, pt=FAKE, stride=8, sl=FAKE, B_=2, hq=8, maxlen=100, sm=0.088, splits=2, ws=FAKE,
+           wsb=1 << 30, out=FAKE, odt=1, lse=None):
+    return L.nvfp4_paged_decode_attn(q, pt, stride, sl, B_, hq, maxlen, ctypes.byref(p) if p is not None else None,
+                                     sm, splits, ws, wsb, out, odt, lse, None)
+
+
+def test_decode_validation(L):
+    assert d_call(L, None) == ERR_NULL
+    assert d_call(L, pool(g=0.3)) == ERR_VALUE
+    assert d_call(L, pool(), odt=2) == ERR_DTYPE
+    assert d_call(L, pool(), B_=-1) == ERR_SHAPE
+    assert d_call(L, pool(), hq=0) == ERR_SHAPE
+    assert d_call(L, pool(hkv=3), hq=8) == ERR_SHAPE  # 8 % 3
+    assert d_call(L, pool(hkv=1), hq=17) == ERR_SHAPE  # group > 16
+    assert d_call(L, pool(), maxlen=8 * 16 + 1) == ERR_SHAPE  # beyond the page-table row
+    assert d_call(L, pool(), splits=4097) == ERR_SHAPE
+    assert d_call(L, pool(), splits=-1) == ERR_SHAPE
+    assert d_call(L, pool(), sm=float("inf")) == ERR_VALUE
+    assert d_call(L, pool(), B_=0) == OK  # no-op, no HIP call
+    assert d_call(L, pool(), q=None) == ERR_NULL
+    assert d_call(L, pool(), ws=None) == ERR_NULL
+    assert d_call(L, pool(), out=None) == ERR_NULL
+    assert d_call(L, pool(), q=FAKE + 2) == ERR_ALIGN
+    assert d_call(L, pool(), out=FAKE + 4) == ERR_ALIGN
+    assert d_call(L, pool(), lse=FAKE + 1) == ERR_ALIGN
+    need = L.nvfp4_paged_decode_attn_workspace_bytes(2, 8, 2)
+    assert d_call(L, pool(), wsb=need - 1) == ERR_WORKSPACE
+
+
+def x_call(L, p, pt=FAKE, stride=8, sl=FAKE, ro=FAKE, n=2, maxlen=64, k=FAKE, v=FAKE, odt=1):
+    return L.nvfp4_kv_dequant_workspace(ctypes.byref(p) if p is not None else None, pt, stride, sl, ro, n, maxlen,
+                                        k, v, odt, None)
+
+
+def test_dequant_validation(L):
+    assert x_call(L, None) == ERR_NULL
+    assert x_call(L, pool(g=-1.0)) == ERR_VALUE
+    assert x_call(L, pool(), odt=5) == ERR_DTYPE
+    assert x_call(L, pool(), n=-1) == ERR_SHAPE
+    assert x_call(L, pool(), maxlen=8 * 16 + 1) == ERR_SHAPE
+    assert x_call(L, pool(), n=0) == OK
+    assert x_call(L, pool(), maxlen=0) == OK
+    assert x_call(L, pool(), ro=None) == ERR_NULL
+    assert x_call(L, pool(), k=FAKE + 2) == ERR_ALIGN
+    assert x_call(L, pool(), ro=FAKE + 4) == ERR_ALIGN
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        B.lib()

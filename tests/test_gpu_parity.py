@@ -1,0 +1,245 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle on seeded
+inputs small enough for the oracle: several pages, ragged tails, edge cases.
+
+Bars: quantized bytes and the dequantized workspace are bit-exact; attention
+outputs pass |gpu - ref| <= 2e-3 + 1e-2 |ref| against the fp64 oracle over the
+dequantized cache."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_paged_kv_nvfp4_amd import binding as B
+from bit_paged_kv_nvfp4_amd import workload as W
+from tests.gpu_common import (assert_close, bf16_bits, gpu_pool_from_kv, oracle_pool_from_kv, run_decode)
+
+pytestmark = pytest.mark.gpu
+
+
+def _kv(w, dtype=torch.float32):
+    return [tuple(x.to(dtype) for x in W.kv(w, b, 0, int(L))) if L > 0 else
+            (torch.zeros((0, w.num_kv_heads, 128), dtype=dtype), torch.zeros((0, w.num_kv_heads, 128), dtype=dtype))
+            for b, L in enumerate(w.seq_lens)]
+
+
+def _oracle_attn(w, opool, q, sm_scale=None, g=1.0):
+    return oracle.decode_attn(bf16_bits(q), w.page_table, w.seq_lens, opool, w.num_kv_heads,
+                              w.sm_scale if sm_scale is None else sm_scale, g=g, n_threads=8)
+
+
+CASES = [
+    # name, Hq, Hkv, lengths, splits
+    ("tiny_gqa8_2k", 8, 1, [2048], 0),
+    ("ragged_tails", 8, 2, [1, 15, 16, 17, 33, 100], 3),
+    ("llama_shape", 64, 8, [300, 1000], 0),
+    ("group16", 16, 1, [77], 4),
+    ("group1", 4, 4, [50], 2),
+    ("group3", 12, 4, [65, 2], 0),
+    ("many_splits", 8, 1, [4096], 64),
+    ("one_split", 16, 2, [513], 1),
+]
+
+
+@pytest.mark.parametrize("name,hq,hkv,lens,splits", CASES, ids=[c[0] for c in CASES])
+def test_quantize_and_decode_match_oracle(name, hq, hkv, lens, splits):
+    w = W.small_workload(100 + len(name), len(lens), hq, hkv, lens, num_splits=splits, name=name)
+    print(f"case {name}: Hq={hq} Hkv={hkv} lens={lens} splits={splits}", flush=True)
+    kv = _kv(w)
+    gpool = gpu_pool_from_kv(w, kv)
+    opool = oracle_pool_from_kv(w, kv)
+    gbytes = gpool.data.cpu().numpy()
+    assert np.array_equal(gbytes, opool), f"pool bytes differ at {np.flatnonzero(gbytes != opool)[:8]}"
+    q = W.query(w)
+    out, lse = run_decode(w, gpool, q, num_splits=splits)
+    ref, ref_lse = _oracle_attn(w, opool, q)
+    err = assert_close(out.cpu().numpy(), ref, what=name)
+    assert_close(lse.cpu().numpy(), ref_lse, atol=1e-3, rtol=1e-4, what=name + " lse")
+    print(f"  max abs err {err:.3e}")
+
+
+def test_bf16_output_and_bf16_source():
+    w = W.small_workload(200, 3, 16, 2, [40, 129, 7], name="bf16")
+    kv = _kv(w, torch.bfloat16)
+    gpool = gpu_pool_from_kv(w, kv)
+    opool = oracle_pool_from_kv(w, kv)
+    assert np.array_equal(gpool.data.cpu().numpy(), opool)
+    q = W.query(w)
+    out, _ = run_decode(w, gpool, q, out_dtype=torch.bfloat16)
+    ref, _ = _oracle_attn(w, opool, q)
+    assert out.dtype == torch.bfloat16
+    assert_close(out.float().cpu().numpy(), ref, what="bf16 out")
+
+
+def _threshold_blocks():
+    """Rows of 128 fp32 values whose 16-value blocks sit on every rounding edge:
+    amax on each E4M3 midpoint of amax/6 and one ulp either side, and elements on
+    each E2M1 midpoint (times the block scale) and one ulp either side."""
+    vals = [oracle.e4m3_value(k) for k in range(127)]
+    blocks = []
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    for s in range(1, 127):
+        D = vals[s]
+        amax = np.float32(6 * D)
+        elems = []
+        for m in mids:
+            t = np.float32(m * D)
+            elems += [t, np.nextafter(t, np.float32(0)), np.nextafter(t, np.float32(np.inf))]
+        elems.append(np.float32(0.0))  # 22 elements: two blocks of amax + 11 + 4 negated
+        for part in range(2):
+            blk = [amax] + elems[part * 11:(part + 1) * 11]
+            blk += [-x for x in blk[1:5]]
+            blocks.append(np.array(blk[:16], dtype=np.float32))
+    for k in range(126):
+        t = np.float32(3 * (vals[k] + vals[k + 1]))  # 6 * midpoint, exact
+        for a in (t, np.nextafter(t, np.float32(0)), np.nextafter(t, np.float32(np.inf))):
+            blk = np.full(16, np.float32(0.3) * a, dtype=np.float32)
+            blk[3] = -a
+            blocks.append(blk)
+    # specials: zeros, negative zeros, tiny (scale rounds to 0 or subnormal), saturation
+    blocks.append(np.zeros(16, np.float32))
+    blocks.append(np.full(16, -0.0, np.float32))
+    blocks.append(np.array([1e-5, -2e-5] * 8, np.float32))
+    blocks.append(np.linspace(-0.004, 0.003, 16).astype(np.float32))
+    blocks.append(np.linspace(-5e4, 7e4, 16).astype(np.float32))
+    blocks.append(np.array([3e38, -1.0] * 8, np.float32))
+    n = len(blocks)
+    pad = (-n) % 8
+    blocks += [blocks[i % n] * np.float32(1.5) for i in range(pad)]
+    return np.stack(blocks).reshape(-1, 1, 128)
+
+
+def test_quantize_rounding_edges_bitexact():
+    rows = _threshold_blocks()  # [T, 1, 128]
+    T = rows.shape[0]
+    w = W.small_workload(300, 1, 1, 1, [T], name="edges")
+    k = torch.from_numpy(rows)
+    v = torch.from_numpy(rows[::-1].copy())
+    gpool = gpu_pool_from_kv(w, [(k, v)])
+    opool = oracle_pool_from_kv(w, [(k, v)])
+    g = gpool.data.cpu().numpy()
+    assert np.array_equal(g, opool), f"{int((g != opool).sum())} bytes differ"
+
+
+@pytest.mark.parametrize("g", [0.5, 4.0])
+def test_power_of_two_global_scale(g):
+    w = W.small_workload(400, 2, 8, 1, [70, 33], name="gscale")
+    kv = [(k * g, v * g) for k, v in _kv(w)]
+    gpool = gpu_pool_from_kv(w, kv, g=g)
+    opool = oracle_pool_from_kv(w, kv, g=g)
+    assert np.array_equal(gpool.data.cpu().numpy(), opool)
+    q = W.query(w)
+    out, lse = run_decode(w, gpool, q, sm_scale=w.sm_scale / g)
+    ref, _ = _oracle_attn(w, opool, q, sm_scale=w.sm_scale / g, g=g)
+    assert_close(out.cpu().numpy(), ref, atol=2e-3 * g, what=f"g={g}")
+    # the same bytes under g = 1 give exactly 1/g of the output (logits kept equal)
+    pool1 = B.Pool(w.num_pages, 1, global_scale=1.0, data=gpool.data)
+    out1, _ = run_decode(w, pool1, q)
+    assert torch.equal(out, out1 * g)
+
+
+def test_dequant_workspace_bitexact():
+    lens = [37, 16, 200]
+    w = W.small_workload(500, 3, 8, 2, lens, name="dequant")
+    kv = _kv(w)
+    gpool = gpu_pool_from_kv(w, kv)
+    opool = oracle_pool_from_kv(w, kv)
+    ko, vo = oracle.dequant_workspace(opool, 2, w.page_table, w.seq_lens)
+    rows = int(sum(lens))
+    pt = torch.as_tensor(w.page_table, device="cuda")
+    sl = torch.as_tensor(w.seq_lens, device="cuda")
+    ro = torch.as_tensor(np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64), device="cuda")
+    for dt in (torch.float32, torch.bfloat16):
+        k_out = torch.full((rows, 2, 128), float("nan"), dtype=dt, device="cuda")
+        v_out = torch.full_like(k_out, float("nan"))
+        B.nvfp4_kv_dequant_workspace(gpool, pt, sl, ro, max(lens), k_out, v_out)
+        torch.cuda.synchronize()
+        for got, ref in ((k_out, ko), (v_out, vo)):
+            want = torch.from_numpy(ref).to(dt)  # exact: at most 6 significant bits
+            assert torch.equal(want.double(), torch.from_numpy(ref))
+            assert torch.equal(got.cpu().view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                               want.view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+
+
+def test_split_count_and_page_permutation_invariance_and_reproducibility():
+    lens = [700, 333]
+    w1 = W.small_workload(600, 2, 16, 2, lens, name="inv1")
+    w2 = W.small_workload(601, 2, 16, 2, lens, name="inv2")
+    kv = _kv(w1)
+    p1 = gpu_pool_from_kv(w1, kv)
+    p2 = gpu_pool_from_kv(w2, kv)
+    q = W.query(w1)
+    a, la = run_decode(w1, p1, q, num_splits=3)
+    b, lb = run_decode(w2, p2, q, num_splits=3)
+    assert torch.equal(a, b) and torch.equal(la, lb)  # physical placement does not matter
+    for _ in range(3):
+        c, lc = run_decode(w1, p1, q, num_splits=3)
+        assert torch.equal(a, c) and torch.equal(la, lc)  # bit-reproducible
+    for s in (1, 2, 7, 11, 0):
+        d, ld = run_decode(w1, p1, q, num_splits=s)
+        # splits round P to f16 against different running maxima: |dP|/P <= 2^-11
+        assert torch.allclose(a, d, atol=1e-3, rtol=1e-3), s
+        assert torch.allclose(la, ld, atol=1e-5, rtol=1e-5), s
+
+
+def test_empty_and_single_token_sequences():
+    lens = [0, 1, 16, 0]
+    w = W.small_workload(700, 4, 8, 1, lens, name="empty")
+    kv = _kv(w)
+    gpool = gpu_pool_from_kv(w, kv)
+    opool = oracle_pool_from_kv(w, kv)
+    q = W.query(w)
+    out, lse = run_decode(w, gpool, q, num_splits=4)
+    o, l = out.cpu(), lse.cpu()
+    assert torch.all(o[0] == 0) and torch.all(o[3] == 0)
+    assert torch.all(torch.isneginf(l[0])) and torch.all(torch.isneginf(l[3]))
+    ref, _ = _oracle_attn(w, opool, q)
+    assert_close(o[1:3].numpy(), ref[1:3], what="len 1/16")
+    vrow = oracle.dequant_row(opool, w.page_table[1, 0], 0, 0, 1, 1)
+    assert np.allclose(o[1].numpy(), np.broadcast_to(vrow, (8, 128)), rtol=1e-6, atol=1e-7)
+
+
+def test_representable_kv_against_dense_attention():
+    """K/V built from representable blocks: the NVFP4 cache holds them exactly, so the
+    GPU output must match dense fp64 attention over the original values."""
+    rng = np.random.default_rng(5)
+    lens = [333, 64]
+    w = W.small_workload(800, 2, 16, 2, lens, name="repr")
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    kv = []
+    for L in lens:
+        pair = []
+        for _ in range(2):
+            codes = rng.integers(0, 16, size=(L, 2, 8, 16))
+            codes[..., 0] = 7
+            vals = mags[codes & 7] * np.where(codes & 8, -1, 1)
+            sc = np.array([oracle.e4m3_value(int(b)) for b in rng.integers(0x28, 0x48, size=L * 16)]).reshape(L, 2, 8)
+            pair.append(torch.from_numpy((vals * sc[..., None]).reshape(L, 2, 128).astype(np.float32)))
+        kv.append(tuple(pair))
+    gpool = gpu_pool_from_kv(w, kv)
+    q = W.query(w)
+    out, _ = run_decode(w, gpool, q)
+    for b, (k, v) in enumerate(kv):
+        qq = q[b].double().unsqueeze(1)
+        kk = k.double().permute(1, 0, 2).repeat_interleave(8, 0)
+        vv = v.double().permute(1, 0, 2).repeat_interleave(8, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=w.sm_scale).squeeze(1)
+        assert_close(out[b].cpu().numpy(), ref.numpy(), what=f"dense seq {b}")
+
+
+@pytest.mark.parametrize("kscale,qscale", [(3e-3, 1.0), (1.0, 3e3), (1.0, 1e-6), (50.0, 1.0)])
+def test_extreme_magnitudes(kscale, qscale):
+    """Tiny K/V (subnormal E4M3 scales and f16 subnormals in the dequantized
+    values), large or tiny queries (the query rescale), large K/V."""
+    lens = [90, 31]
+    w = W.small_workload(900, 2, 8, 1, lens, name="mag")
+    kv = [(k * kscale, v * kscale) for k, v in _kv(w)]
+    gpool = gpu_pool_from_kv(w, kv)
+    opool = oracle_pool_from_kv(w, kv)
+    assert np.array_equal(gpool.data.cpu().numpy(), opool)
+    q = (W.query(w).float() * qscale).to(torch.bfloat16)
+    out, lse = run_decode(w, gpool, q)
+    ref, ref_lse = _oracle_attn(w, opool, q)
+    assert_close(out.cpu().numpy(), ref, atol=2e-3 * kscale, what=f"k x{kscale} q x{qscale}")
+    assert_close(lse.cpu().numpy(), ref_lse, atol=1e-3, rtol=1e-4, what="lse")

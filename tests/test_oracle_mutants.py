@@ -17,6 +17,7 @@ MUTANTS = [
     ("scale_ties_to_odd", "if (amax > thr || (amax == thr && (k & 1)))",
      "if (amax > thr || (amax == thr && !(k & 1)))"),
     ("scale_ties_up", "if (amax > thr || (amax == thr && (k & 1)))", "if (amax >= thr)"),
+    ("scale_table_shifted", "orc_e4m3_table[k] = orc_e4m3_value(k);", "orc_e4m3_table[k] = orc_e4m3_value(k + 1);"),
     ("scale_divisor_4", "6.0 * (double)g", "4.0 * (double)g"),
     ("scale_clamps_too_low", "while (k < 126) {", "while (k < 125) {"),
     ("code_ties_to_odd", "if (ax > thr || (ax == thr && (k & 1)))", "if (ax > thr || (ax == thr && !(k & 1)))"),
