@@ -37,6 +37,10 @@ namespace {
 
 constexpr float kLazyRescaleLog2 = 8.0f;
 
+#ifndef NVFP4KV_V_EARLY
+#define NVFP4KV_V_EARLY 0
+#endif
+
 __device__ __forceinline__ float xor16_max(float v) {
   const uint32_t u = __float_as_uint(v);
   auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
@@ -71,59 +75,202 @@ struct PageRegs {
   uint4 vs;     // the matching V scale bytes
 };
 
-struct LaneOffsets {
-  int k, ks, v, vs;  // byte offsets inside a (page, head) K+V slab pair
+// LDS ring of pages, per wave. A slot holds one (page, head) K+V slab pair as
+// the lanes will consume it: [K code chunk of lane 0..63 | V code chunk of lane
+// 0..63 | 128 K scale bytes | 128 V scale bytes].
+constexpr int kSlotBytes = 2 * kSlab;  // 2304
+#ifndef NVFP4KV_DECODE_WAVES
+#define NVFP4KV_DECODE_WAVES 4
+#endif
+#ifndef NVFP4KV_DECODE_PAIRS_AHEAD
+#define NVFP4KV_DECODE_PAIRS_AHEAD 1
+#endif
+constexpr int kPairsAhead = NVFP4KV_DECODE_PAIRS_AHEAD;  // pairs of pages in flight while one is computed
+constexpr int kRing = 2 * (kPairsAhead + 1);              // LDS slots (pages) per wave
+// Independent waves per workgroup: each owns one split and its own LDS region;
+// several waves per workgroup keep the per-CU workgroup count low.
+constexpr int kWaves = NVFP4KV_DECODE_WAVES;
+constexpr int kDmaPerPage = 3;
+
+// One asynchronous 16-byte-per-lane copy global -> LDS (gfx950 global_load_lds
+// dwordx4): lane i reads base + voff and writes LDS address lds + 16 i. It is
+// issued from inline assembly so that the compiler, which cannot tell which LDS
+// bytes such a copy writes, does not drain all outstanding copies before every
+// LDS read; completion is awaited explicitly with wait_dma().
+// A wave-uniform copy of a pointer, held in SGPRs (readfirstlane is free when the
+// value already is scalar); the copy instructions take their base from SGPRs.
+template <typename T>
+__device__ __forceinline__ const T* sgpr_ptr(const T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sgpr_ptr(base)),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// Same with 4 bytes per lane (lane i writes LDS address lds + 4 i).
+__device__ __forceinline__ void dma4(const int32_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(sgpr_ptr(base)),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_dma() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+struct DmaOffsets {
+  uint32_t k, v, s;  // per-lane source offsets inside a (page, head) K+V slab pair
 };
 
-__device__ __forceinline__ LaneOffsets lane_offsets(int n, int G) {
-  LaneOffsets o;
-  o.k = n * 64 + G * 16;
-  o.ks = kCodeBytes + n * 8 + G * 2;
-  o.v = kSlab + (n * 4 + G) * 16;
-  o.vs = kSlab + kCodeBytes + (G * 2 + (n >> 3)) * 16;
+__device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
+  const int n = lane & 15, G = lane >> 4;
+  DmaOffsets o;
+  o.k = n * 64 + G * 16;                          // 32 K channels of token n
+  o.v = kSlab + (n * 4 + G) * 16;                 // V chunk of tokens 4G.., pairs n, 16+n, ..
+  o.s = lane < 8 ? kCodeBytes + 16 * lane         // lanes 0..7: K scale bytes
+                 : kSlab + kCodeBytes + 16 * (lane - 8);  // lanes 8..15: V scale bytes
   return o;
 }
 
-__device__ __forceinline__ void load_page(PageRegs& r, const uint8_t* base, const LaneOffsets& o) {
-  r.kc = *reinterpret_cast<const uint4*>(base + o.k);
-  r.ks = *reinterpret_cast<const uint16_t*>(base + o.ks);
-  r.vc = *reinterpret_cast<const uint4*>(base + o.v);
-  r.vs = *reinterpret_cast<const uint4*>(base + o.vs);
+// Issue the copies of one (page, head) slab pair into an LDS slot (3 vmcnt events).
+__device__ __forceinline__ void issue_page(const uint8_t* slab, const DmaOffsets& o, uint32_t slot, int lane) {
+  dma16(slab, o.k, slot);
+  dma16(slab, o.v, slot + kCodeBytes);
+  if (lane < 16) dma16(slab, o.s, slot + 2 * kCodeBytes);
 }
 
-// One page of 16 tokens: S^T = K^ Q^T, online softmax, O^T += V^T P^T.
-__device__ __forceinline__ void page_step(const PageRegs& r, int pg, int L, int G, const f16x8 (&qf)[4], float c,
-                                          float& m_ref, float& lsum, f32x4 (&acc)[8]) {
-  // ---- S^T = K^ Q^T over 4 steps of 32 channels ----
+// Page ids reach the wave the same way as page bytes: 64 at a time, copied into
+// one of two LDS id buffers one chunk ahead of use. When the issue pointer enters
+// a chunk, each lane loads one id of it into a register, and the id of a page is
+// then taken with v_readlane (no memory round trip per page). A plain table load
+// inside the loop would be a vector load that the compiler drains together with
+// every copy in flight.
+constexpr int kIdChunk = 64;
+
+// Copy the ids of split-relative pages [64 k, 64 k + 64) (clamped to the split's
+// last page) into id buffer k & 1. One vmcnt event.
+__device__ __forceinline__ void issue_ids(const int32_t* pt_split, int k, int n_pages, uint32_t ids_lds, int lane) {
+  const int rel = min(k * kIdChunk + lane, n_pages - 1);
+  dma4(pt_split, (uint32_t)rel * 4u, ids_lds + (k & 1) * (kIdChunk * 4));
+}
+
+__device__ __forceinline__ const uint8_t* slab_of(const uint8_t* pool_h, int ids_v, int rel, int64_t page_bytes) {
+  const int pid = __builtin_amdgcn_readlane(ids_v, rel % kIdChunk);
+  return pool_h + (int64_t)pid * page_bytes;
+}
+
+__device__ __forceinline__ PageRegs read_page(const uint8_t* slot, int lane) {
+  const int n = lane & 15, G = lane >> 4;
+  PageRegs r;
+  r.kc = *reinterpret_cast<const uint4*>(slot + 16 * lane);
+  r.vc = *reinterpret_cast<const uint4*>(slot + kCodeBytes + 16 * lane);
+  r.ks = *reinterpret_cast<const uint16_t*>(slot + 2 * kCodeBytes + n * 8 + G * 2);
+  r.vs = *reinterpret_cast<const uint4*>(slot + 2 * kCodeBytes + 128 + (G * 2 + (n >> 3)) * 16);
+  return r;
+}
+
+// K^ rows of one MFMA step: channels 32G + 8s .. +7 of the lane's token, exact f16
+// (E2M1 code times E4M3 scale / 256).
+__device__ __forceinline__ f16x8 k_operand(uint32_t w, uint32_t scale_f16x2) {
+  const f16x2 x0 = pk_mul(as_u32(fp4x2_to_f16x2<0>(w)), scale_f16x2);
+  const f16x2 x1 = pk_mul(as_u32(fp4x2_to_f16x2<1>(w)), scale_f16x2);
+  const f16x2 x2 = pk_mul(as_u32(fp4x2_to_f16x2<2>(w)), scale_f16x2);
+  const f16x2 x3 = pk_mul(as_u32(fp4x2_to_f16x2<3>(w)), scale_f16x2);
+  return f16x8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+}
+
+// V^ of one 16-byte chunk word q (tokens 4G..4G+3 of channel pair 16q + n) as two
+// k-slot quartets ordered tokens 4G+0, +2, +1, +3: the even channel (`ev`) and
+// the odd channel (`od`) of the pair.
+__device__ __forceinline__ void v_operands(uint32_t w, uint32_t sc, f16x2& e02, f16x2& e13, f16x2& o02,
+                                           f16x2& o13) {
+  const uint32_t r0 = as_u32(fp4x2_to_f16x2<0>(w));
+  const uint32_t r1 = as_u32(fp4x2_to_f16x2<1>(w));
+  const uint32_t r2 = as_u32(fp4x2_to_f16x2<2>(w));
+  const uint32_t r3 = as_u32(fp4x2_to_f16x2<3>(w));
+  const uint32_t s02 = (sc << 7) & 0x3F803F80u;  // scales of tokens 4G+0, 4G+2
+  const uint32_t s13 = (sc >> 1) & 0x3F803F80u;  // scales of tokens 4G+1, 4G+3
+  e02 = pk_mul(pack_lo(r0, r2), s02);
+  e13 = pk_mul(pack_lo(r1, r3), s13);
+  o02 = pk_mul(pack_hi(r0, r2), s02);
+  o13 = pk_mul(pack_hi(r1, r3), s13);
+}
+
+// Two pages (32 tokens) per step: S^T = K^ Q^T for each page (two independent
+// MFMA chains), one online-softmax update over the 32 tokens, and O^T += V^T P^T
+// with the 32 tokens as the MFMA reduction (k slots 8G..8G+7 = page A tokens
+// 4G+0, +2, +1, +3, then the same of page B). Tokens at or past `lim` (the end of
+// the split or of the sequence) are masked.
+__device__ __forceinline__ void pair_step(const PageRegs& ra, const PageRegs& rb, int tok_a, int lim, int G,
+                                          const f16x8 (&qf)[4], float c, float& m_ref, float& lsum,
+                                          f32x4 (&acc)[8]) {
+  // ---- S^T = K^ Q^T ----
   // scale bytes of finite E4M3 values are <= 0x7E; bit 7 is dropped so that even
   // bytes of never-written (masked) rows decode to finite values
-  const uint32_t sk0 = e4m3_f16bits_div256((r.ks & 0x7Fu) * 0x00010001u);
-  const uint32_t sk1 = e4m3_f16bits_div256(((r.ks >> 8) & 0x7Fu) * 0x00010001u);
-  const uint32_t kw[4] = {r.kc.x, r.kc.y, r.kc.z, r.kc.w};
-  f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t ska0 = e4m3_f16bits_div256((ra.ks & 0x7Fu) * 0x00010001u);
+  const uint32_t ska1 = e4m3_f16bits_div256(((ra.ks >> 8) & 0x7Fu) * 0x00010001u);
+  const uint32_t skb0 = e4m3_f16bits_div256((rb.ks & 0x7Fu) * 0x00010001u);
+  const uint32_t skb1 = e4m3_f16bits_div256(((rb.ks >> 8) & 0x7Fu) * 0x00010001u);
+  const uint32_t kwa[4] = {ra.kc.x, ra.kc.y, ra.kc.z, ra.kc.w};
+  const uint32_t kwb[4] = {rb.kc.x, rb.kc.y, rb.kc.z, rb.kc.w};
+  f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const uint32_t sc = s < 2 ? sk0 : sk1;
-    const f16x2 x0 = pk_mul(as_u32(fp4x2_to_f16x2<0>(kw[s])), sc);
-    const f16x2 x1 = pk_mul(as_u32(fp4x2_to_f16x2<1>(kw[s])), sc);
-    const f16x2 x2 = pk_mul(as_u32(fp4x2_to_f16x2<2>(kw[s])), sc);
-    const f16x2 x3 = pk_mul(as_u32(fp4x2_to_f16x2<3>(kw[s])), sc);
-    const f16x8 kf = {x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
-    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[s], sacc, 0, 0, 0);
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(kwa[s], s < 2 ? ska0 : ska1), qf[s], sa, 0, 0, 0);
+    sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(kwb[s], s < 2 ? skb0 : skb1), qf[s], sb, 0, 0, 0);
   }
 
-  // ---- online softmax (base 2), tokens 4G..4G+3 of head n ----
-  float z[4];
+#if NVFP4KV_V_EARLY
+  // V operands are built before the softmax so that the scheduler can overlap
+  // their VALU work with the QK^T MFMA chains and the softmax reductions.
+  f16x8 ve[4], vo[4];
+  {
+    const uint32_t vwa[4] = {ra.vc.x, ra.vc.y, ra.vc.z, ra.vc.w};
+    const uint32_t vsa[4] = {ra.vs.x, ra.vs.y, ra.vs.z, ra.vs.w};
+    const uint32_t vwb[4] = {rb.vc.x, rb.vc.y, rb.vc.z, rb.vc.w};
+    const uint32_t vsb[4] = {rb.vs.x, rb.vs.y, rb.vs.z, rb.vs.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) z[i] = sacc[i] * c;
-  if ((pg + 1) * kPage > L) {  // only the last page of a sequence has rows past its end
-    const int tok0 = pg * kPage + 4 * G;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) z[i] = (tok0 + i < L) ? z[i] : -__builtin_inff();
+    for (int q = 0; q < 4; ++q) {
+      f16x2 ae02, ae13, ao02, ao13, be02, be13, bo02, bo13;
+      v_operands(vwa[q], vsa[q], ae02, ae13, ao02, ao13);
+      v_operands(vwb[q], vsb[q], be02, be13, bo02, bo13);
+      ve[q] = f16x8{ae02[0], ae02[1], ae13[0], ae13[1], be02[0], be02[1], be13[0], be13[1]};
+      vo[q] = f16x8{ao02[0], ao02[1], ao13[0], ao13[1], bo02[0], bo02[1], bo13[0], bo13[1]};
+    }
   }
-  float mx = __builtin_fmaxf(__builtin_fmaxf(z[0], z[1]), __builtin_fmaxf(z[2], z[3]));
+#endif
+
+  // ---- online softmax (base 2) over tokens 4G..4G+3 of both pages, head n ----
+  // Logits are z = s * c with c > 0 (the query sign absorbs the sign of the
+  // softmax scale), so the maximum is taken on the raw scores s and each weight
+  // is exp2(fma(s, c, -m)).
+  float z[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    z[i] = sa[i];
+    z[4 + i] = sb[i];
+  }
+  const bool tail = tok_a + 2 * kPage > lim;  // only the last pair of a split has rows to mask
+  const int t0 = tok_a + 4 * G;
+  if (tail) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = (t0 + i < lim) ? z[i] : -__builtin_inff();
+      z[4 + i] = (t0 + kPage + i < lim) ? z[4 + i] : -__builtin_inff();
+    }
+  }
+  float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(z[0], z[1]), __builtin_fmaxf(z[2], z[3])),
+                             __builtin_fmaxf(__builtin_fmaxf(z[4], z[5]), __builtin_fmaxf(z[6], z[7])));
   mx = xor16_max(mx);
-  mx = xor32_max(mx);
+  mx = xor32_max(mx) * c;
   const bool need = mx > m_ref + kLazyRescaleLog2;
   if (__builtin_amdgcn_ballot_w64(need) != 0) {
     const float m_new = need ? mx : m_ref;
@@ -133,43 +280,56 @@ __device__ __forceinline__ void page_step(const PageRegs& r, int pg, int L, int 
     for (int i = 0; i < 8; ++i) acc[i] *= alpha;
     m_ref = m_new;
   }
-  float p[4];
+  float p[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - m_ref);
-  lsum += (p[0] + p[1]) + (p[2] + p[3]);
-  const f16x4 pf = {(_Float16)p[0], (_Float16)p[2], (_Float16)p[1], (_Float16)p[3]};
+  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[i], c, -m_ref));
+  if (tail) {  // exact zeros for masked rows, also when c == 0
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = (t0 + i < lim) ? p[i] : 0.0f;
+      p[4 + i] = (t0 + kPage + i < lim) ? p[4 + i] : 0.0f;
+    }
+  }
+  lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  const f16x8 pf = {(_Float16)p[0], (_Float16)p[2], (_Float16)p[1], (_Float16)p[3],
+                    (_Float16)p[4], (_Float16)p[6], (_Float16)p[5], (_Float16)p[7]};
 
-  // ---- O^T += V^T P^T ----
-  const uint32_t vw[4] = {r.vc.x, r.vc.y, r.vc.z, r.vc.w};
-  const uint32_t vsw[4] = {r.vs.x, r.vs.y, r.vs.z, r.vs.w};
+  // ---- O^T += V^T P^T, 32 tokens per MFMA ----
+#if NVFP4KV_V_EARLY
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t r0 = as_u32(fp4x2_to_f16x2<0>(vw[q]));
-    const uint32_t r1 = as_u32(fp4x2_to_f16x2<1>(vw[q]));
-    const uint32_t r2 = as_u32(fp4x2_to_f16x2<2>(vw[q]));
-    const uint32_t r3 = as_u32(fp4x2_to_f16x2<3>(vw[q]));
-    const uint32_t s02 = (vsw[q] << 7) & 0x3F803F80u;  // scales of tokens 4G+0, 4G+2
-    const uint32_t s13 = (vsw[q] >> 1) & 0x3F803F80u;  // scales of tokens 4G+1, 4G+3
-    const f16x2 e0 = pk_mul(pack_lo(r0, r2), s02);
-    const f16x2 e1 = pk_mul(pack_lo(r1, r3), s13);
-    const f16x2 o0 = pk_mul(pack_hi(r0, r2), s02);
-    const f16x2 o1 = pk_mul(pack_hi(r1, r3), s13);
-    const f16x4 ve = {e0[0], e0[1], e1[0], e1[1]};
-    const f16x4 vo = {o0[0], o0[1], o1[0], o1[1]};
-    acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(ve, pf, acc[2 * q], 0, 0, 0);
-    acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vo, pf, acc[2 * q + 1], 0, 0, 0);
+    acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ve[q], pf, acc[2 * q], 0, 0, 0);
+    acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo[q], pf, acc[2 * q + 1], 0, 0, 0);
   }
+#else
+  const uint32_t vwa[4] = {ra.vc.x, ra.vc.y, ra.vc.z, ra.vc.w};
+  const uint32_t vsa[4] = {ra.vs.x, ra.vs.y, ra.vs.z, ra.vs.w};
+  const uint32_t vwb[4] = {rb.vc.x, rb.vc.y, rb.vc.z, rb.vc.w};
+  const uint32_t vsb[4] = {rb.vs.x, rb.vs.y, rb.vs.z, rb.vs.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f16x2 ae02, ae13, ao02, ao13, be02, be13, bo02, bo13;
+    v_operands(vwa[q], vsa[q], ae02, ae13, ao02, ao13);
+    v_operands(vwb[q], vsb[q], be02, be13, bo02, bo13);
+    const f16x8 ve = {ae02[0], ae02[1], ae13[0], ae13[1], be02[0], be02[1], be13[0], be13[1]};
+    const f16x8 vo = {ao02[0], ao02[1], ao13[0], ao13[1], bo02[0], bo02[1], bo13[0], bo13[1]};
+    acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ve, pf, acc[2 * q], 0, 0, 0);
+    acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo, pf, acc[2 * q + 1], 0, 0, 0);
+  }
+#endif
 }
 
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_decode_split(DecodeArgs a) {
-  const int split = blockIdx.x;
+__global__ __launch_bounds__(64 * kWaves) void k_decode_split(DecodeArgs a) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform by construction
+  const int split = blockIdx.x * kWaves + wave;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int G = lane >> 4;
   const int S = a.num_splits;
 
+  if (split >= S) return;  // waves never synchronize, so a spare wave may leave
   const int L = a.seq_lens[b];
   const int npages = (L + kPage - 1) / kPage;
   const int pps = (npages + S - 1) / S;
@@ -204,14 +364,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     (void)__builtin_frexpf(qmax, &e2);  // qmax = m * 2^e2, m in [0.5, 1)
     qexp = e2 - 15;                      // qmax * 2^-qexp in [2^14, 2^15)
   }
-  const float qmul = __builtin_ldexpf(1.0f, -qexp);
+  // A negative softmax scale is carried by the query's sign (exact), so that the
+  // logit multiplier c below is positive.
+  const float qmul = a.qk_scale_log2 < 0.0f ? -__builtin_ldexpf(1.0f, -qexp) : __builtin_ldexpf(1.0f, -qexp);
   f16x8 qf[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int e = 0; e < 8; ++e) qf[s][e] = (_Float16)(qv[8 * s + e] * qmul);
   // z (base-2 logit) = S_acc * c: undoes the Q rescale and the 1/256 of the K scales
-  const float c = __builtin_ldexpf(a.qk_scale_log2, qexp + 8);
+  const float c = __builtin_ldexpf(__builtin_fabsf(a.qk_scale_log2), qexp + 8);
 
   float m_ref = -__builtin_inff();
   float lsum = 0.0f;
@@ -222,24 +384,51 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void
   const int32_t* pt_row = a.page_table + (int64_t)b * a.pt_stride;
   const uint8_t* pool_h = a.pool + (int64_t)h * (2 * kSlab);
   const int64_t page_bytes = (int64_t)a.num_kv_heads * (2 * kSlab);
-  const LaneOffsets off = lane_offsets(n, G);
+  __shared__ __attribute__((aligned(16))) uint8_t ring_all[kWaves][kRing * kSlotBytes];
+  uint8_t* const ring = ring_all[wave];
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+  const DmaOffsets off = dma_offsets(lane);
 
-  // Two register sets of raw page bytes in ping-pong: the next page is fetched
-  // while the current one is computed, so every wave keeps two pages of loads in
-  // flight without register copies between iterations.
-  // The prefetch is unconditional (past the split's end it re-reads its last
-  // page) so that no branch sits between a load and the wait for older loads.
-  PageRegs A, Bq;
-  const int last = pg1 - 1;
-  if (pg0 < pg1) load_page(A, pool_h + (int64_t)pt_row[pg0] * page_bytes, off);
-  for (int pg = pg0; pg < pg1; pg += 2) {
-    load_page(Bq, pool_h + (int64_t)pt_row[min(pg + 1, last)] * page_bytes, off);
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this page's math
-    page_step(A, pg, L, G, qf, c, m_ref, lsum, acc);
-    if (pg + 1 >= pg1) break;
-    load_page(A, pool_h + (int64_t)pt_row[min(pg + 2, last)] * page_bytes, off);
-    __builtin_amdgcn_sched_barrier(0);
-    page_step(Bq, pg + 1, L, G, qf, c, m_ref, lsum, acc);
+  __shared__ __attribute__((aligned(16))) int32_t ids_all[kWaves][2 * kIdChunk];
+  int32_t* const ids = ids_all[wave];
+  const uint32_t ids_lds = (uint32_t)(uintptr_t)ids;
+  if (pg0 < pg1) {
+    const int n_pages = pg1 - pg0;
+    const int n_pairs = (n_pages + 1) / 2;
+    const int lim = min(L, pg1 * kPage);  // tokens of this split end here
+    const int32_t* pt_split = pt_row + pg0;
+    issue_ids(pt_split, 0, n_pages, ids_lds, lane);
+    issue_ids(pt_split, 1, n_pages, ids_lds, lane);
+    wait_dma<0>();
+    int ids_v = ids[lane];  // chunk 0
+    // The ring holds kPairsAhead + 1 pairs: one being computed, the others in
+    // flight. Pages past the split's end re-read its last page (masked by `lim`),
+    // so every iteration issues the same number of copies and the wait count is
+    // a constant.
+#pragma unroll
+    for (int j = 0; j < 2 * kPairsAhead; ++j)
+      issue_page(slab_of(pool_h, ids_v, min(j, n_pages - 1), page_bytes), off, ring_lds + j * kSlotBytes, lane);
+    int cur = 0;  // ring slot of the current pair's first page
+    for (int i = 0; i < n_pairs; ++i) {
+      const int ahead = 2 * (i + kPairsAhead);  // first page of the pair to fetch now
+      if (ahead % kIdChunk == 0 && ahead < n_pages) {
+        // Entering id chunk k = ahead / 64: its buffer has landed long ago; take
+        // its ids into the register and refill the other buffer with chunk k + 1.
+        ids_v = ids[((ahead / kIdChunk) & 1) * kIdChunk + lane];
+        issue_ids(pt_split, ahead / kIdChunk + 1, n_pages, ids_lds, lane);
+      }
+      const int nxt = cur == 0 ? kRing - 2 : cur - 2;  // the slot pair freed last iteration
+      issue_page(slab_of(pool_h, ids_v, min(ahead, n_pages - 1), page_bytes), off, ring_lds + nxt * kSlotBytes,
+                 lane);
+      issue_page(slab_of(pool_h, ids_v, min(ahead + 1, n_pages - 1), page_bytes), off,
+                 ring_lds + (nxt + 1) * kSlotBytes, lane);
+      wait_dma<2 * kPairsAhead * kDmaPerPage>();  // the current pair's copies have landed
+      const PageRegs ra = read_page(ring + cur * kSlotBytes, lane);
+      const PageRegs rb = read_page(ring + (cur + 1) * kSlotBytes, lane);
+      pair_step(ra, rb, (pg0 + 2 * i) * kPage, lim, G, qf, c, m_ref, lsum, acc);
+      cur = cur + 2 == kRing ? 0 : cur + 2;
+    }
+    wait_dma<0>();  // no copy may outlive the wave's LDS
   }
 
   // ---- partial result of this split ----
@@ -298,7 +487,8 @@ __global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_decode_split, dim3(a.num_splits, a.num_kv_heads, a.batch), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(k_decode_split, dim3((a.num_splits + kWaves - 1) / kWaves, a.num_kv_heads, a.batch),
+                     dim3(64 * kWaves), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_decode_combine, dim3(a.batch * a.num_q_heads), dim3(64), 0, stream, a);
