@@ -1,17 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of NVFP4 paged decode attention on one MI355X.
 
-One step = one decode step of one layer for the whole batch: the split-K decode
-kernel plus the split combine, reading the batch's entire NVFP4 K/V cache.
-Inputs (pool, Q, page table) are resident in HBM before the timed region; the
-pool is filled once by the library's quantize-on-write kernel from seeded
-synthetic K/V.
+One step = one decode step of one layer for the whole batch, every row of the
+hot path: quantize-on-write of the step's new K/V token of every sequence into
+the NVFP4 pool, the split-K decode kernel that reads the batch's whole NVFP4
+cache and dequantizes it in registers, and the split combine. Inputs (pool, Q,
+page table, the new tokens) are resident in HBM before the timed region; the
+pool is filled once beforehand by the same quantize kernel from seeded
+synthetic K/V. The new token of sequence b is its last token (index L_b - 1),
+so each step rewrites the same bytes and every step attends over L_b tokens.
 
-Prints one JSON line (rank 0, N = 1):
-  value      KV-read GB/s = algorithmic NVFP4 KV bytes per step / time per step
-  roofline   HBM roofline of the dominant kernel (decode split kernel), timed
-             live with HIP events on the stream it runs on
+Prints one JSON line:
+  value         KV-read GB/s = algorithmic NVFP4 K+V bytes read per step / time per step
+  roofline      the decode split kernel (the dominant kernel) against MI355X HBM peak:
+                algorithmic bytes per launch / its average duration, both from HIP
+                events recorded on its stream inside the timed region
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+With --config 5 it also times the extend step (quantize-write of the 8192-token
+bf16 chunk, dequant of the 163840-token prefix into a bf16 workspace).
 """
 from __future__ import annotations
 
@@ -31,16 +37,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = batch 44 x 32K, the metric's workload)")
-    ap.add_argument("--splits", type=int, default=-1, help="-1 = workload setting / library default")
+    ap.add_argument("--splits", type=int, default=-1, help="-1 = the workload's setting, else the library default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=2)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=24)
     return ap.parse_args()
 
 
-def fill_pool(w, pool, B, W, torch):
-    """Quantize-on-write every sequence's K/V into the pool (library kernel)."""
-    step = 65536
-    for b in range(w.batch):
+def fill_pool(w, pool, B, W, torch, seqs=None, step=65536):
+    """Quantize-on-write every listed sequence's K/V into the pool (library kernel)."""
+    for b in (range(w.batch) if seqs is None else seqs):
         L = int(w.seq_lens[b])
         for t0 in range(0, L, step):
             t1 = min(L, t0 + step)
@@ -52,8 +57,8 @@ def fill_pool(w, pool, B, W, torch):
 
 def cpu_baseline(w, n_seqs, W, torch):
     """The oracle (fp64 attention over its own NVFP4 quantization of the same
-    seeded K/V) on the first n_seqs sequences, all heads. Only the attention is
-    timed; the sample's KV bytes over that time give a GB/s-equivalent."""
+    seeded K/V) on the first n_seqs sequences, all heads. Only the decode
+    attention is timed; the sample's KV bytes over that time give a GB/s figure."""
     import numpy as np
 
     import oracle
@@ -66,19 +71,66 @@ def cpu_baseline(w, n_seqs, W, torch):
                      outlier_channels=w.outlier_channels)
     pool = np.zeros(oracle.pool_bytes(w.num_pages, w.num_kv_heads), dtype=np.uint8)
     for b in range(n_seqs):
-        k, v = W.kv(w, b, 0, int(lens[b]), device="cuda")
-        oracle.quantize_to_pool(k.cpu().numpy(), v.cpu().numpy(), W.slots(w, b, 0, int(lens[b])), w.num_pages,
-                                pool=pool, n_threads=cores)
-        del k, v
-    q = W.query(w)[:n_seqs].contiguous().view(torch.int16).numpy().view(np.uint16)
+        L = int(lens[b])
+        for t0 in range(0, L, 65536):
+            t1 = min(L, t0 + 65536)
+            k, v = W.kv(w, b, t0, t1, device="cuda")
+            oracle.quantize_to_pool(k.cpu().numpy(), v.cpu().numpy(), W.slots(w, b, t0, t1), w.num_pages,
+                                    pool=pool, n_threads=cores)
+            del k, v
+    q = W.query(w, device="cuda")[:n_seqs].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
     t0 = time.perf_counter()
     oracle.decode_attn(q, sub.page_table, lens, pool, w.num_kv_heads, w.sm_scale, n_threads=cores)
     dt = time.perf_counter() - t0
     kv_bytes = sub.kv_bytes_per_step()
     return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_seqs} of {w.batch} sequences x all {w.num_kv_heads} KV heads "
-                      f"({int(lens.sum())} tokens, {kv_bytes} KV bytes), fp64 attention only, {dt:.2f} s",
-            "seconds": round(dt, 3), "decode_steps_per_s_equiv": round(dt and (kv_bytes / w.kv_bytes_per_step()) / dt, 6)}
+            "sample": f"{n_seqs} of {w.batch} sequences, all {w.num_q_heads} query heads ({int(lens.sum())} tokens, "
+                      f"{kv_bytes} KV bytes): fp64 decode attention over the oracle's own NVFP4 cache, {dt:.2f} s",
+            "seconds": round(dt, 3),
+            "decode_steps_per_s_per_layer_equiv": round((kv_bytes / w.kv_bytes_per_step()) / dt, 6)}
+
+
+def extend_step(w, pool, B, W, torch, steps, warmup):
+    """Config 5's chunked-prefill step: quantize-write the 8192-token bf16 chunk
+    into the extend request's pages, dequantize its 163840-token prefix into a
+    bf16 workspace. Events on the stream bracket each kernel."""
+    row = w.extend_row
+    # the prefix must be resident: fill it once (untimed)
+    P, C = w.extend_prefix, w.extend_chunk
+    for t0 in range(0, P, 65536):
+        t1 = min(P, t0 + 65536)
+        k, v = W.kv(w, row, t0, t1, device="cuda")
+        B.nvfp4_kv_quantize(k, v, torch.as_tensor(W.slots(w, row, t0, t1), device="cuda"), pool)
+    kc, vc = W.extend_chunk_kv(w, device="cuda")
+    cslots = torch.as_tensor(W.slots(w, row, P, P + C), device="cuda")
+    pt = torch.as_tensor(w.page_table[row:row + 1], device="cuda").contiguous()
+    sl = torch.tensor([P], dtype=torch.int32, device="cuda")
+    ro = torch.zeros(1, dtype=torch.int64, device="cuda")
+    k_ws = torch.empty((P, w.num_kv_heads, 128), dtype=torch.bfloat16, device="cuda")
+    v_ws = torch.empty_like(k_ws)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        B.nvfp4_kv_quantize(kc, vc, cslots, pool, stream=stream)
+        B.nvfp4_kv_dequant_workspace(pool, pt, sl, ro, P, k_ws, v_ws, stream=stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        B.nvfp4_kv_quantize(kc, vc, cslots, pool, stream=stream)
+        ev[i][1].record(stream)
+        B.nvfp4_kv_dequant_workspace(pool, pt, sl, ro, P, k_ws, v_ws, stream=stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    q_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    d_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    q_bytes = C * w.num_kv_heads * 128 * 2 * 2 + C * w.num_kv_heads * 2 * 8 * 9  # bf16 in + NVFP4 out
+    d_bytes = P * w.num_kv_heads * 2 * 8 * 9 + P * w.num_kv_heads * 128 * 2 * 2  # NVFP4 in + bf16 out
+    return {"quantize_chunk_ms": round(q_ms, 5), "quantize_chunk_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+            "quantize_chunk_bytes": q_bytes, "dequant_prefix_ms": round(d_ms, 5),
+            "dequant_prefix_GBps": round(d_bytes / (d_ms * 1e-3) / 1e9, 1), "dequant_prefix_bytes": d_bytes,
+            "chunk_tokens": C, "prefix_tokens": P,
+            "note": "the 189 MB prefix read may be served partly from the 256 MB last-level cache between repeats"}
 
 
 def main():
@@ -105,30 +157,50 @@ def main():
     q = W.query(w, device="cuda")
     pt = torch.as_tensor(w.page_table[:w.batch], device="cuda").contiguous()
     sl = torch.as_tensor(w.seq_lens, device="cuda")
+    # the step's new token of every sequence (its last one)
+    new_k, new_v, new_slots = [], [], []
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        k, v = W.kv(w, b, L - 1, L, device="cuda")
+        new_k.append(k)
+        new_v.append(v)
+        new_slots.append(int(W.slots(w, b, L - 1, L)[0]))
+    new_k = torch.cat(new_k).contiguous()
+    new_v = torch.cat(new_v).contiguous()
+    new_slots = torch.tensor(new_slots, dtype=torch.int32, device="cuda")
     ws = torch.empty(B.nvfp4_paged_decode_attn_workspace_bytes(w.batch, w.num_q_heads, splits), dtype=torch.uint8,
                      device="cuda")
     out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step():
-        B.nvfp4_paged_decode_attn(q, pt, sl, pool, w.sm_scale, w.max_seq_len, num_splits=splits, workspace=ws,
-                                  out=out, stream=stream)
+    def step(evs=None):
+        B.nvfp4_kv_quantize(new_k, new_v, new_slots, pool, stream=stream)
+        if evs:
+            evs[0].record(stream)
+        B.nvfp4_paged_decode_attn_partial(q, pt, sl, pool, w.sm_scale, w.max_seq_len, splits, ws, stream=stream)
+        if evs:
+            evs[1].record(stream)
+        B.nvfp4_decode_combine(ws, w.batch, w.num_q_heads, splits, out, stream=stream)
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(kev[i])
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
+    k_ms = sum(a.elapsed_time(b) for a, b in kev) / args.steps
     kv_bytes = w.kv_bytes_per_step()
     gbs = kv_bytes / (ms * 1e-3) / 1e9
+    k_gbs = kv_bytes / (k_ms * 1e-3) / 1e9
     steps_per_s = 1e3 / ms
+    ragged = len(set(w.seq_lens.tolist())) > 1
     res = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -141,19 +213,23 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
-        "data": "synthetic (seeded N(0,1) Q/K/V, 4 K channels x8, shuffled pages)",
-        "config": {"workload": w.name, "batch": w.batch, "seq_lens": "ragged" if len(set(w.seq_lens.tolist())) > 1
-                   else int(w.seq_lens[0]), "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
-                   "head_dim": 128, "page_size": 16, "num_splits": splits, "kv_bytes_per_step": kv_bytes},
+        "data": "synthetic (seeded N(0,1) Q/K/V, 4 K channels x8 per KV head, shuffled pages)",
+        "config": {"workload": w.name, "batch": w.batch,
+                   "seq_len": f"U[{int(w.seq_lens.min())},{int(w.seq_lens.max())}]" if ragged else int(w.seq_lens[0]),
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": 128, "page_size": 16,
+                   "num_splits": splits, "kv_bytes_per_step": kv_bytes},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "decode_steps_per_s_per_layer": round(steps_per_s, 2),
         "tokens_per_s_per_layer": round(steps_per_s * w.batch, 1),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode step (split kernel + combine kernel), HIP events over the timed region"},
+        "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_decode_split", "kernel_ms": round(k_ms, 5),
+                     "bytes_per_launch": kv_bytes},
         "wall_s_timed": round(wall, 3),
         "pool_fill_s": round(t_fill, 2),
     }
+    if w.extend_prefix:
+        res["extend"] = extend_step(w, pool, B, W, torch, max(3, args.steps // 5), 2)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, W, torch)
     print(json.dumps(res), flush=True)

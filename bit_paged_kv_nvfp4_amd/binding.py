@@ -29,6 +29,8 @@ EXPORTED = [
     "nvfp4_paged_decode_attn_default_splits",
     "nvfp4_paged_decode_attn_workspace_bytes",
     "nvfp4_paged_decode_attn",
+    "nvfp4_paged_decode_attn_partial",
+    "nvfp4_decode_combine",
     "nvfp4_kv_dequant_workspace",
 ]
 
@@ -66,6 +68,11 @@ def lib() -> ctypes.CDLL:
                                               c.POINTER(PoolDesc), c.c_float, c.c_int32, P, c.c_size_t, P,
                                               c.c_int32, P, P]
         L.nvfp4_paged_decode_attn.restype = c.c_int32
+        L.nvfp4_paged_decode_attn_partial.argtypes = [P, P, c.c_int64, P, c.c_int32, c.c_int32, c.c_int32,
+                                                      c.POINTER(PoolDesc), c.c_float, c.c_int32, P, c.c_size_t, P]
+        L.nvfp4_paged_decode_attn_partial.restype = c.c_int32
+        L.nvfp4_decode_combine.argtypes = [P, c.c_size_t, c.c_int32, c.c_int32, c.c_int32, P, c.c_int32, P, P]
+        L.nvfp4_decode_combine.restype = c.c_int32
         L.nvfp4_kv_dequant_workspace.argtypes = [c.POINTER(PoolDesc), P, c.c_int64, P, P, c.c_int32, c.c_int32,
                                                  P, P, c.c_int32, P]
         L.nvfp4_kv_dequant_workspace.restype = c.c_int32
@@ -169,6 +176,32 @@ def nvfp4_paged_decode_attn(q: torch.Tensor, page_table: torch.Tensor, seq_lens:
                                          int(max_seq_len), ctypes.byref(d), float(sm_scale), int(num_splits),
                                          _ptr(workspace), workspace.numel(), _ptr(out), odt, _ptr(lse),
                                          _stream(stream)))
+    return out
+
+
+def nvfp4_paged_decode_attn_partial(q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor, pool: Pool,
+                                    sm_scale: float, max_seq_len: int, num_splits: int, workspace: torch.Tensor,
+                                    stream=None):
+    """Phase 1: per-split online-softmax states into ``workspace`` (layout in the C header)."""
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [B, Hq, 128] tensor")
+    B, hq, _ = q.shape
+    d = pool.desc()
+    _check("nvfp4_paged_decode_attn_partial",
+           lib().nvfp4_paged_decode_attn_partial(_ptr(q), _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, hq,
+                                                 int(max_seq_len), ctypes.byref(d), float(sm_scale), int(num_splits),
+                                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def nvfp4_decode_combine(workspace: torch.Tensor, batch: int, num_q_heads: int, num_splits: int, out: torch.Tensor,
+                         lse: torch.Tensor | None = None, stream=None):
+    """Phase 2: merge the split states into ``out`` (float32 or bfloat16 [B, Hq, 128])."""
+    odt = {torch.float32: F32, torch.bfloat16: BF16}.get(out.dtype)
+    if odt is None or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 or bfloat16")
+    _check("nvfp4_decode_combine",
+           lib().nvfp4_decode_combine(_ptr(workspace), workspace.numel(), int(batch), int(num_q_heads), int(num_splits),
+                                      _ptr(out), odt, _ptr(lse), _stream(stream)))
     return out
 
 

@@ -96,7 +96,9 @@ int32_t nvfp4_paged_decode_attn_default_splits(int32_t batch, int32_t num_kv_hea
   }
   const int64_t pages = (max_seq_len + NVFP4KV_PAGE_SIZE - 1) / NVFP4KV_PAGE_SIZE;
   const int64_t units = (int64_t)batch * num_kv_heads;
-  const int64_t target_waves = (int64_t)num_cus * 16;  // resident one-wave work items per CU
+  // About 22 one-wave work items per CU: 1.375 rounds of the 16 resident waves a
+  // CU holds, so the scheduler can even out waves that finish at different times.
+  const int64_t target_waves = (int64_t)num_cus * 22;
   int64_t s = (target_waves + units - 1) / units;
   const int64_t max_by_pages = pages / 4 > 1 ? pages / 4 : 1;
   if (s > max_by_pages) s = max_by_pages;
@@ -113,32 +115,33 @@ size_t nvfp4_paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_head
   return o_bytes + ((ml_bytes + 255) & ~(size_t)255);
 }
 
-int32_t nvfp4_paged_decode_attn(const void* q, const int32_t* page_table, int64_t page_table_stride,
-                                const int32_t* seq_lens, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
-                                const nvfp4kv_pool* pool, float sm_scale, int32_t num_splits, void* workspace,
-                                size_t workspace_bytes, void* out, int32_t out_dtype, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared validation of the decode phases; fills `a` (without out/lse).
+int32_t prepare_decode(const void* q, const int32_t* page_table, int64_t page_table_stride, const int32_t* seq_lens,
+                       int32_t batch, int32_t num_q_heads, int32_t max_seq_len, const nvfp4kv_pool* pool,
+                       float sm_scale, int32_t* num_splits, void* workspace, size_t workspace_bytes,
+                       nvfp4kv::DecodeArgs& a) {
   if (int32_t e = check_pool(pool)) return e;
-  if (out_dtype != NVFP4KV_F32 && out_dtype != NVFP4KV_BF16) return NVFP4KV_ERR_DTYPE;
   if (batch < 0 || num_q_heads < 1 || max_seq_len < 0 || page_table_stride < 1) return NVFP4KV_ERR_SHAPE;
   const int32_t hkv = pool->num_kv_heads;
   if (num_q_heads % hkv != 0) return NVFP4KV_ERR_SHAPE;
   const int32_t group = num_q_heads / hkv;
   if (group < 1 || group > NVFP4KV_MAX_GROUP) return NVFP4KV_ERR_SHAPE;
   if ((int64_t)max_seq_len > page_table_stride * NVFP4KV_PAGE_SIZE) return NVFP4KV_ERR_SHAPE;
-  if (num_splits < 0 || num_splits > NVFP4KV_MAX_SPLITS) return NVFP4KV_ERR_SHAPE;
+  if (*num_splits < 0 || *num_splits > NVFP4KV_MAX_SPLITS) return NVFP4KV_ERR_SHAPE;
   if (batch > 65535 || hkv > 65535) return NVFP4KV_ERR_SHAPE;  // grid limits of the split kernel
   if (!isfinite(sm_scale)) return NVFP4KV_ERR_VALUE;
   if (batch == 0) return NVFP4KV_OK;
-  if (!q || !page_table || !seq_lens || !out || !workspace) return NVFP4KV_ERR_NULL;
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) ||
-      (reinterpret_cast<uintptr_t>(page_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
-      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+  if (!q || !page_table || !seq_lens || !workspace) return NVFP4KV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(workspace) || (reinterpret_cast<uintptr_t>(page_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
     return NVFP4KV_ERR_ALIGN;
-  if (num_splits == 0) num_splits = nvfp4_paged_decode_attn_default_splits(batch, hkv, max_seq_len, 0);
-  const size_t need = nvfp4_paged_decode_attn_workspace_bytes(batch, num_q_heads, num_splits);
+  if (*num_splits == 0) *num_splits = nvfp4_paged_decode_attn_default_splits(batch, hkv, max_seq_len, 0);
+  const size_t need = nvfp4_paged_decode_attn_workspace_bytes(batch, num_q_heads, *num_splits);
   if (need == 0 || workspace_bytes < need) return NVFP4KV_ERR_WORKSPACE;
-
-  nvfp4kv::DecodeArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.page_table = page_table;
   a.pt_stride = page_table_stride;
@@ -151,13 +154,82 @@ int32_t nvfp4_paged_decode_attn(const void* q, const int32_t* page_table, int64_
   a.pool = static_cast<const uint8_t*>(pool->data);
   a.qk_scale_log2 = (float)((double)sm_scale * 1.4426950408889634 * (double)pool->global_scale);
   a.v_scale = pool->global_scale;
-  a.num_splits = num_splits;
+  a.num_splits = *num_splits;
   a.part_o = static_cast<float*>(workspace);
+  a.part_ml = a.part_o + (size_t)batch * num_q_heads * *num_splits * NVFP4KV_HEAD_DIM;
+  a.out = nullptr;
+  a.out_bf16 = 0;
+  a.lse = nullptr;
+  return NVFP4KV_OK;
+}
+
+int32_t prepare_combine(const void* workspace, size_t workspace_bytes, int32_t batch, int32_t num_q_heads,
+                        int32_t num_splits, void* out, int32_t out_dtype, float* lse, nvfp4kv::DecodeArgs& a) {
+  if (out_dtype != NVFP4KV_F32 && out_dtype != NVFP4KV_BF16) return NVFP4KV_ERR_DTYPE;
+  if (batch < 0 || num_q_heads < 1 || num_splits < 1 || num_splits > NVFP4KV_MAX_SPLITS) return NVFP4KV_ERR_SHAPE;
+  if ((int64_t)batch * num_q_heads > 0x7FFFFFFF) return NVFP4KV_ERR_SHAPE;
+  if (batch == 0) return NVFP4KV_OK;
+  if (!workspace || !out) return NVFP4KV_ERR_NULL;
+  if (!aligned16(workspace) || !aligned16(out) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return NVFP4KV_ERR_ALIGN;
+  const size_t need = nvfp4_paged_decode_attn_workspace_bytes(batch, num_q_heads, num_splits);
+  if (need == 0 || workspace_bytes < need) return NVFP4KV_ERR_WORKSPACE;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_splits = num_splits;
+  a.part_o = static_cast<float*>(const_cast<void*>(workspace));
   a.part_ml = a.part_o + (size_t)batch * num_q_heads * num_splits * NVFP4KV_HEAD_DIM;
   a.out = out;
   a.out_bf16 = out_dtype == NVFP4KV_BF16;
   a.lse = lse;
-  return hip_status(nvfp4kv::launch_decode(a, static_cast<hipStream_t>(stream)));
+  return NVFP4KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t nvfp4_paged_decode_attn_partial(const void* q, const int32_t* page_table, int64_t page_table_stride,
+                                        const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                        int32_t max_seq_len, const nvfp4kv_pool* pool, float sm_scale,
+                                        int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_splits < 1) return NVFP4KV_ERR_SHAPE;  // the caller sizes the workspace for a known count
+  nvfp4kv::DecodeArgs a;
+  if (int32_t e = prepare_decode(q, page_table, page_table_stride, seq_lens, batch, num_q_heads, max_seq_len, pool,
+                                 sm_scale, &num_splits, workspace, workspace_bytes, a))
+    return e;
+  if (batch == 0) return NVFP4KV_OK;
+  return hip_status(nvfp4kv::launch_decode_partial(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t nvfp4_decode_combine(const void* workspace, size_t workspace_bytes, int32_t batch, int32_t num_q_heads,
+                             int32_t num_splits, void* out, int32_t out_dtype, float* lse, void* stream) {
+  nvfp4kv::DecodeArgs a;
+  if (int32_t e = prepare_combine(workspace, workspace_bytes, batch, num_q_heads, num_splits, out, out_dtype, lse, a))
+    return e;
+  if (batch == 0) return NVFP4KV_OK;
+  return hip_status(nvfp4kv::launch_decode_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t nvfp4_paged_decode_attn(const void* q, const int32_t* page_table, int64_t page_table_stride,
+                                const int32_t* seq_lens, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
+                                const nvfp4kv_pool* pool, float sm_scale, int32_t num_splits, void* workspace,
+                                size_t workspace_bytes, void* out, int32_t out_dtype, float* lse, void* stream) {
+  nvfp4kv::DecodeArgs a;
+  if (out_dtype != NVFP4KV_F32 && out_dtype != NVFP4KV_BF16) {
+    if (int32_t e = check_pool(pool)) return e;
+    return NVFP4KV_ERR_DTYPE;
+  }
+  if (int32_t e = prepare_decode(q, page_table, page_table_stride, seq_lens, batch, num_q_heads, max_seq_len, pool,
+                                 sm_scale, &num_splits, workspace, workspace_bytes, a))
+    return e;
+  if (batch == 0) return NVFP4KV_OK;
+  nvfp4kv::DecodeArgs c;
+  if (int32_t e = prepare_combine(workspace, workspace_bytes, batch, num_q_heads, num_splits, out, out_dtype, lse, c))
+    return e;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (int32_t e = hip_status(nvfp4kv::launch_decode_partial(a, st))) return e;
+  return hip_status(nvfp4kv::launch_decode_combine(c, st));
 }
 
 int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page_table, int64_t page_table_stride,

@@ -437,11 +437,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_split(DecodeArgs a) {
   if (head_ok) {
     const size_t unit = ((size_t)b * a.num_q_heads + qh) * S + split;
     float* po = a.part_o + unit * kHeadDim;
-    // acc[2q + par][r] is O^T[channel 32q + 2(4G + r) + par][head n]
+    // acc[2q + par][r] is O^T[channel 32q + 2(4G + r) + par][head n], in units of
+    // 1/256 of the value scale (the V scales were carried as E4M3/256)
+    const float vs = a.v_scale * 256.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 v0 = make_float4(acc[2 * q][0], acc[2 * q + 1][0], acc[2 * q][1], acc[2 * q + 1][1]);
-      const float4 v1 = make_float4(acc[2 * q][2], acc[2 * q + 1][2], acc[2 * q][3], acc[2 * q + 1][3]);
+      const float4 v0 = make_float4(acc[2 * q][0] * vs, acc[2 * q + 1][0] * vs, acc[2 * q][1] * vs, acc[2 * q + 1][1] * vs);
+      const float4 v1 = make_float4(acc[2 * q][2] * vs, acc[2 * q + 1][2] * vs, acc[2 * q][3] * vs, acc[2 * q + 1][3] * vs);
       *reinterpret_cast<float4*>(po + 32 * q + 8 * G) = v0;
       *reinterpret_cast<float4*>(po + 32 * q + 8 * G + 4) = v1;
     }
@@ -467,7 +469,7 @@ __global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
       o0 += w * v.x;
       o1 += w * v.y;
     }
-    const float inv = (a.v_scale * 256.0f) / Ls;  // V scales were carried as E4M3/256
+    const float inv = 1.0f / Ls;
     o0 *= inv;
     o1 *= inv;
   }
@@ -485,12 +487,15 @@ __global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   hipLaunchKernelGGL(k_decode_split, dim3((a.num_splits + kWaves - 1) / kWaves, a.num_kv_heads, a.batch),
                      dim3(64 * kWaves), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
   hipLaunchKernelGGL(k_decode_combine, dim3(a.batch * a.num_q_heads), dim3(64), 0, stream, a);
   return hipGetLastError();
 }

@@ -44,7 +44,7 @@ struct DecodeArgs {
   int32_t max_seq_len;
   const uint8_t* pool;
   float qk_scale_log2;     // sm_scale * log2(e) * g
-  float v_scale;           // g
+  float v_scale;           // g (the partial states carry V in true units)
   int32_t num_splits;
   float* part_o;           // [B][Hq][S][128]
   float* part_ml;          // [B][Hq][S][2]: running max (log2 units), sum
@@ -69,7 +69,8 @@ struct DequantArgs {
 };
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
 
 // ---- device helpers --------------------------------------------------------

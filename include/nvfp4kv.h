@@ -128,9 +128,10 @@ int32_t nvfp4_kv_quantize(const void* k_src, const void* v_src, int32_t src_dtyp
                           const nvfp4kv_pool* pool, void* stream);
 
 /*
- * Split count the decode call uses when passed num_splits = 0: enough
- * (sequence, KV head, split) work items to fill num_cus compute units, at least
- * 4 pages per split, at most NVFP4KV_MAX_SPLITS. num_cus <= 0 asks the current
+ * Split count the decode call uses when passed num_splits = 0: about 22
+ * (sequence, KV head, split) work items per compute unit (1.375 rounds of the
+ * waves a CU keeps resident), at least 4 pages per split, at most
+ * NVFP4KV_MAX_SPLITS. num_cus <= 0 asks the current
  * HIP device for its compute-unit count (the only HIP call of this function).
  * Returns >= 1.
  */
@@ -172,6 +173,37 @@ int32_t nvfp4_paged_decode_attn(const void* q, const int32_t* page_table, int64_
                                 const int32_t* seq_lens, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
                                 const nvfp4kv_pool* pool, float sm_scale, int32_t num_splits, void* workspace,
                                 size_t workspace_bytes, void* out, int32_t out_dtype, float* lse, void* stream);
+
+/*
+ * The two phases of nvfp4_paged_decode_attn, for callers that time, overlap or
+ * distribute them (for example, merging states computed on several devices).
+ *
+ * Phase 1, nvfp4_paged_decode_attn_partial: same inputs and checks as
+ * nvfp4_paged_decode_attn, num_splits >= 1 (resolved by the caller). Split s of
+ * sequence b covers logical pages [s*P, min((s+1)*P, n_b)), P = ceil(n_b / S),
+ * n_b = ceil(seq_lens[b] / 16). For every (b, qh, s) it writes an online-softmax
+ * state into the workspace:
+ *   M[b][qh][s]      reference exponent (base 2) of the split's logits, -inf
+ *                    for an empty split; not necessarily their maximum,
+ *   Z[b][qh][s]      sum over the split's tokens of 2^(x_t log2(e) - M),
+ *   O[b][qh][s][128] sum over the split's tokens of 2^(x_t log2(e) - M) v^_t,
+ * with x_t = sm_scale q . k^_t (natural-log logits). Workspace layout: O as f32
+ * [B][Hq][S][128] at byte 0, then (M, Z) as f32 pairs [B][Hq][S][2] at byte
+ * B*Hq*S*128*4.
+ *
+ * Phase 2, nvfp4_decode_combine: for every (b, qh) merges the S states:
+ *   M* = max_s M, Z* = sum_s 2^(M_s - M*) Z_s, out = sum_s 2^(M_s - M*) O_s / Z*,
+ *   lse = (M* + log2 Z*) ln 2; all states empty: out = 0, lse = -inf.
+ * Errors: as nvfp4_paged_decode_attn (ERR_SHAPE for num_splits outside
+ * 1..4096, ERR_WORKSPACE when the workspace is smaller than the layout above).
+ */
+int32_t nvfp4_paged_decode_attn_partial(const void* q, const int32_t* page_table, int64_t page_table_stride,
+                                        const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                        int32_t max_seq_len, const nvfp4kv_pool* pool, float sm_scale,
+                                        int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+int32_t nvfp4_decode_combine(const void* workspace, size_t workspace_bytes, int32_t batch, int32_t num_q_heads,
+                             int32_t num_splits, void* out, int32_t out_dtype, float* lse, void* stream);
 
 /*
  * Extend-path dequantization ([LMSYS] "Interpretation": the cached prefix is
