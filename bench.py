@@ -40,7 +40,54 @@ def parse():
     ap.add_argument("--splits", type=int, default=-1, help="-1 = the workload's setting, else the library default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=24)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="calibration only: time a plain device copy of this many bytes instead of the decode step "
+                         "(the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes, steps):
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_bytes": src.numel() * 4, "ms": round(ms, 4),
+                      "GBps_read_plus_write": round(2 * src.numel() * 4 / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def committed_traffic(workload, splits):
+    """HBM bytes per split-kernel launch from the committed rocprofv3 counter
+    summary in profiles/, or None when there is none for this workload and split
+    count or when the kernel source has changed since the counters were taken."""
+    import glob
+    import hashlib
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    for path in glob.glob(os.path.join(here, "profiles", "k_decode_split_*_traffic.md")):
+        fields = {}
+        for line in open(path):
+            if ":" in line and line.startswith("    "):
+                k, v = line.strip().split(":", 1)
+                fields[k.strip()] = v.strip()
+        if fields.get("workload") != workload or fields.get("num_splits") != str(splits):
+            continue
+        src = os.path.join(here, fields.get("kernel_source", ""))
+        if not os.path.isfile(src):
+            continue
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields.get("kernel_source_sha256"):
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    return None
 
 
 def fill_pool(w, pool, B, W, torch, seqs=None, step=65536):
@@ -139,6 +186,9 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes, args.steps)
+        return
     import torch
 
     from bit_paged_kv_nvfp4_amd import binding as B
@@ -222,7 +272,7 @@ def main():
         "decode_steps_per_s_per_layer": round(steps_per_s, 2),
         "tokens_per_s_per_layer": round(steps_per_s * w.batch, 1),
         "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": committed_traffic(w.name, splits),
                      "kernel": "k_decode_split", "kernel_ms": round(k_ms, 5),
                      "bytes_per_launch": kv_bytes},
         "wall_s_timed": round(wall, 3),

@@ -451,40 +451,6 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_split(DecodeArgs a) {
   }
 }
 
-// One wave per (sequence, query head): merge the splits' partials.
-__global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
-  const int unit = blockIdx.x;  // b * Hq + qh
-  const int lane = threadIdx.x;
-  const int S = a.num_splits;
-  const float* ml = a.part_ml + (size_t)unit * S * 2;
-  const float* po = a.part_o + (size_t)unit * S * kHeadDim;
-  float M = -__builtin_inff();
-  for (int i = 0; i < S; ++i) M = __builtin_fmaxf(M, ml[2 * i]);
-  float o0 = 0.0f, o1 = 0.0f, Ls = 0.0f;
-  if (M != -__builtin_inff()) {
-    for (int i = 0; i < S; ++i) {
-      const float w = __builtin_amdgcn_exp2f(ml[2 * i] - M);
-      const float2 v = *reinterpret_cast<const float2*>(po + (size_t)i * kHeadDim + 2 * lane);
-      Ls += w * ml[2 * i + 1];
-      o0 += w * v.x;
-      o1 += w * v.y;
-    }
-    const float inv = 1.0f / Ls;
-    o0 *= inv;
-    o1 *= inv;
-  }
-  const size_t o = (size_t)unit * kHeadDim + 2 * lane;
-  if (a.out_bf16) {
-    uint16_t* out = static_cast<uint16_t*>(a.out);
-    const uint32_t packed = (uint32_t)f32_to_bf16_bits(o0) | ((uint32_t)f32_to_bf16_bits(o1) << 16);
-    *reinterpret_cast<uint32_t*>(out + o) = packed;
-  } else {
-    *reinterpret_cast<float2*>(static_cast<float*>(a.out) + o) = make_float2(o0, o1);
-  }
-  if (a.lse && lane == 0)
-    a.lse[unit] = (M == -__builtin_inff()) ? -__builtin_inff() : (M + __builtin_log2f(Ls)) * 0.69314718055994530942f;
-}
-
 }  // namespace
 
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
@@ -494,10 +460,5 @@ hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream) {
-  if (a.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_decode_combine, dim3(a.batch * a.num_q_heads), dim3(64), 0, stream, a);
-  return hipGetLastError();
-}
 
 }  // namespace nvfp4kv
