@@ -12,14 +12,17 @@
 // so every K/V byte is read once per decode step and shared by the group through
 // the matrix cores:
 //   S^T[16 tok x 16 heads] = K^[16 x 128] Q^T      4 x v_mfma_f32_16x16x32_f16
-//   O^T[128 x 16 heads]   += V^T[128 x 16] P^T     8 x v_mfma_f32_16x16x16_f16
+//   O^T[128 x 16 heads]   += V^T[128 x 32] P^T     8 x v_mfma_f32_16x16x32_f16
+// (the PV product takes two pages, 32 tokens, per MFMA).
 // Lane (n = lane%16, G = lane/16):
 //   K: loads 16 B = channels 32G..32G+31 of token n; MFMA step s uses channels
 //      32G+8s..+7, and Q is loaded in the same channel order.
 //   S^T fragment: head n, tokens 4G..4G+3, which is exactly the P^T operand the
 //      PV product needs (k slots ordered tokens 4G+0, +2, +1, +3).
-//   V: loads one 16-B chunk = tokens 4G..4G+3 of channel pairs n, 16+n, 32+n,
-//      48+n; pair 16q+n feeds two 16-row tiles (even / odd channel of the pair).
+//   V: loads one 16-B chunk = channels 8n..8n+7 (half of scale block n/2) of
+//      tokens 4G..4G+3, two codes of one channel per byte (tokens 4G+0|4G+2 and
+//      4G+1|4G+3), so a conversion yields two k slots directly and the lane needs
+//      one word of scales per page; row n of PV tile q is channel 8n + q.
 // Dequant: v_cvt_scalef32_pk_f16_fp4 turns two codes into exact f16 values (its
 // scale operand only carries a power of two, so it is left at 1.0); one
 // v_pk_mul_f16 by the E4M3 block scale (as f16, divided by 256 so that every
@@ -37,9 +40,6 @@ namespace {
 
 constexpr float kLazyRescaleLog2 = 8.0f;
 
-#ifndef NVFP4KV_V_EARLY
-#define NVFP4KV_V_EARLY 0
-#endif
 
 __device__ __forceinline__ float xor16_max(float v) {
   const uint32_t u = __float_as_uint(v);
@@ -62,17 +62,13 @@ __device__ __forceinline__ float xor32_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Low halves of a and b -> (a.lo, b.lo); high halves -> (a.hi, b.hi).
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-
 __device__ __forceinline__ f16x2 pk_mul(uint32_t a, uint32_t b) { return as_f16x2(a) * as_f16x2(b); }
 
 struct PageRegs {
   uint4 kc;     // K codes: 32 channels of one token
   uint32_t ks;  // its two K scale bytes
-  uint4 vc;     // V codes: 4 tokens x 4 channel pairs
-  uint4 vs;     // the matching V scale bytes
+  uint4 vc;     // V codes: 8 channels (one half block) x 4 tokens
+  uint32_t vs;  // the block's scale bytes of those 4 tokens
 };
 
 // LDS ring of pages, per wave. A slot holds one (page, head) K+V slab pair as
@@ -91,6 +87,8 @@ constexpr int kRing = 2 * (kPairsAhead + 1);              // LDS slots (pages) p
 // several waves per workgroup keep the per-CU workgroup count low.
 constexpr int kWaves = NVFP4KV_DECODE_WAVES;
 constexpr int kDmaPerPage = 3;
+constexpr int kQDmas = 4;  // 1 KB copies of the group's queries (up to 16 heads x 256 B)
+static_assert(kRing >= 4, "the query staging area takes the ring's last two slots");
 
 // One asynchronous 16-byte-per-lane copy global -> LDS (gfx950 global_load_lds
 // dwordx4): lane i reads base + voff and writes LDS address lds + 16 i. It is
@@ -134,7 +132,7 @@ __device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
   const int n = lane & 15, G = lane >> 4;
   DmaOffsets o;
   o.k = n * 64 + G * 16;                          // 32 K channels of token n
-  o.v = kSlab + (n * 4 + G) * 16;                 // V chunk of tokens 4G.., pairs n, 16+n, ..
+  o.v = kSlab + 16 * lane;                        // V chunk: channels 8n..8n+7, tokens 4G..4G+3
   o.s = lane < 8 ? kCodeBytes + 16 * lane         // lanes 0..7: K scale bytes
                  : kSlab + kCodeBytes + 16 * (lane - 8);  // lanes 8..15: V scale bytes
   return o;
@@ -173,7 +171,7 @@ __device__ __forceinline__ PageRegs read_page(const uint8_t* slot, int lane) {
   r.kc = *reinterpret_cast<const uint4*>(slot + 16 * lane);
   r.vc = *reinterpret_cast<const uint4*>(slot + kCodeBytes + 16 * lane);
   r.ks = *reinterpret_cast<const uint16_t*>(slot + 2 * kCodeBytes + n * 8 + G * 2);
-  r.vs = *reinterpret_cast<const uint4*>(slot + 2 * kCodeBytes + 128 + (G * 2 + (n >> 3)) * 16);
+  r.vs = *reinterpret_cast<const uint32_t*>(slot + 2 * kCodeBytes + 128 + (n >> 1) * 16 + G * 4);
   return r;
 }
 
@@ -187,21 +185,37 @@ __device__ __forceinline__ f16x8 k_operand(uint32_t w, uint32_t scale_f16x2) {
   return f16x8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
 }
 
-// V^ of one 16-byte chunk word q (tokens 4G..4G+3 of channel pair 16q + n) as two
-// k-slot quartets ordered tokens 4G+0, +2, +1, +3: the even channel (`ev`) and
-// the odd channel (`od`) of the pair.
-__device__ __forceinline__ void v_operands(uint32_t w, uint32_t sc, f16x2& e02, f16x2& e13, f16x2& o02,
-                                           f16x2& o13) {
-  const uint32_t r0 = as_u32(fp4x2_to_f16x2<0>(w));
-  const uint32_t r1 = as_u32(fp4x2_to_f16x2<1>(w));
-  const uint32_t r2 = as_u32(fp4x2_to_f16x2<2>(w));
-  const uint32_t r3 = as_u32(fp4x2_to_f16x2<3>(w));
-  const uint32_t s02 = (sc << 7) & 0x3F803F80u;  // scales of tokens 4G+0, 4G+2
-  const uint32_t s13 = (sc >> 1) & 0x3F803F80u;  // scales of tokens 4G+1, 4G+3
-  e02 = pk_mul(pack_lo(r0, r2), s02);
-  e13 = pk_mul(pack_lo(r1, r3), s13);
-  o02 = pk_mul(pack_hi(r0, r2), s02);
-  o13 = pk_mul(pack_hi(r1, r3), s13);
+// Both halves of a K scale pair: E4M3 byte SEL of ks as f16 bits (value / 256).
+// Rows of never-written bytes may decode to NaN here: their scores are masked.
+template <int SEL>
+__device__ __forceinline__ uint32_t k_scale_pair(uint32_t ks) {
+  return __builtin_amdgcn_perm(0u, ks, SEL == 0 ? 0x0C000C00u : 0x0C010C01u) << 7;
+}
+
+// V scale pairs of tokens (4G+0, 4G+2) and (4G+1, 4G+3), as f16 bits (value / 256).
+// Bit 7 of each byte is dropped so that never-written bytes of masked rows still
+// decode to finite values (their weight is an exact zero, and 0 * inf is NaN).
+__device__ __forceinline__ uint32_t v_scales02(uint32_t vs) { return (vs << 7) & 0x3F803F80u; }
+__device__ __forceinline__ uint32_t v_scales13(uint32_t vs) { return (vs >> 1) & 0x3F803F80u; }
+
+// V^ of channel 8n + q (q = 0..7) for one page: code bytes 2q (tokens 4G+0 | 4G+2)
+// and 2q + 1 (tokens 4G+1 | 4G+3) of the lane's chunk, i.e. k slots ordered
+// tokens 4G+0, +2, +1, +3.
+template <int Q>
+__device__ __forceinline__ void v_operand(const uint4& vc, uint32_t s02, uint32_t s13, f16x2& x02, f16x2& x13) {
+  const uint32_t w = Q < 2 ? vc.x : Q < 4 ? vc.y : Q < 6 ? vc.z : vc.w;
+  x02 = pk_mul(as_u32(fp4x2_to_f16x2<2 * (Q & 1)>(w)), s02);
+  x13 = pk_mul(as_u32(fp4x2_to_f16x2<2 * (Q & 1) + 1>(w)), s13);
+}
+
+template <int Q>
+__device__ __forceinline__ void pv_tile(const uint4& va, const uint4& vb, uint32_t sa02, uint32_t sa13, uint32_t sb02,
+                                        uint32_t sb13, const f16x8& pf, f32x4& acc) {
+  f16x2 a02, a13, b02, b13;
+  v_operand<Q>(va, sa02, sa13, a02, a13);
+  v_operand<Q>(vb, sb02, sb13, b02, b13);
+  const f16x8 v = {a02[0], a02[1], a13[0], a13[1], b02[0], b02[1], b13[0], b13[1]};
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, pf, acc, 0, 0, 0);
 }
 
 // Two pages (32 tokens) per step: S^T = K^ Q^T for each page (two independent
@@ -215,10 +229,8 @@ __device__ __forceinline__ void pair_step(const PageRegs& ra, const PageRegs& rb
   // ---- S^T = K^ Q^T ----
   // scale bytes of finite E4M3 values are <= 0x7E; bit 7 is dropped so that even
   // bytes of never-written (masked) rows decode to finite values
-  const uint32_t ska0 = e4m3_f16bits_div256((ra.ks & 0x7Fu) * 0x00010001u);
-  const uint32_t ska1 = e4m3_f16bits_div256(((ra.ks >> 8) & 0x7Fu) * 0x00010001u);
-  const uint32_t skb0 = e4m3_f16bits_div256((rb.ks & 0x7Fu) * 0x00010001u);
-  const uint32_t skb1 = e4m3_f16bits_div256(((rb.ks >> 8) & 0x7Fu) * 0x00010001u);
+  const uint32_t ska0 = k_scale_pair<0>(ra.ks), ska1 = k_scale_pair<1>(ra.ks);
+  const uint32_t skb0 = k_scale_pair<0>(rb.ks), skb1 = k_scale_pair<1>(rb.ks);
   const uint32_t kwa[4] = {ra.kc.x, ra.kc.y, ra.kc.z, ra.kc.w};
   const uint32_t kwb[4] = {rb.kc.x, rb.kc.y, rb.kc.z, rb.kc.w};
   f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -228,25 +240,6 @@ __device__ __forceinline__ void pair_step(const PageRegs& ra, const PageRegs& rb
     sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(kwb[s], s < 2 ? skb0 : skb1), qf[s], sb, 0, 0, 0);
   }
 
-#if NVFP4KV_V_EARLY
-  // V operands are built before the softmax so that the scheduler can overlap
-  // their VALU work with the QK^T MFMA chains and the softmax reductions.
-  f16x8 ve[4], vo[4];
-  {
-    const uint32_t vwa[4] = {ra.vc.x, ra.vc.y, ra.vc.z, ra.vc.w};
-    const uint32_t vsa[4] = {ra.vs.x, ra.vs.y, ra.vs.z, ra.vs.w};
-    const uint32_t vwb[4] = {rb.vc.x, rb.vc.y, rb.vc.z, rb.vc.w};
-    const uint32_t vsb[4] = {rb.vs.x, rb.vs.y, rb.vs.z, rb.vs.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f16x2 ae02, ae13, ao02, ao13, be02, be13, bo02, bo13;
-      v_operands(vwa[q], vsa[q], ae02, ae13, ao02, ao13);
-      v_operands(vwb[q], vsb[q], be02, be13, bo02, bo13);
-      ve[q] = f16x8{ae02[0], ae02[1], ae13[0], ae13[1], be02[0], be02[1], be13[0], be13[1]};
-      vo[q] = f16x8{ao02[0], ao02[1], ao13[0], ao13[1], bo02[0], bo02[1], bo13[0], bo13[1]};
-    }
-  }
-#endif
 
   // ---- online softmax (base 2) over tokens 4G..4G+3 of both pages, head n ----
   // Logits are z = s * c with c > 0 (the query sign absorbs the sign of the
@@ -294,29 +287,17 @@ __device__ __forceinline__ void pair_step(const PageRegs& ra, const PageRegs& rb
   const f16x8 pf = {(_Float16)p[0], (_Float16)p[2], (_Float16)p[1], (_Float16)p[3],
                     (_Float16)p[4], (_Float16)p[6], (_Float16)p[5], (_Float16)p[7]};
 
-  // ---- O^T += V^T P^T, 32 tokens per MFMA ----
-#if NVFP4KV_V_EARLY
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ve[q], pf, acc[2 * q], 0, 0, 0);
-    acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo[q], pf, acc[2 * q + 1], 0, 0, 0);
-  }
-#else
-  const uint32_t vwa[4] = {ra.vc.x, ra.vc.y, ra.vc.z, ra.vc.w};
-  const uint32_t vsa[4] = {ra.vs.x, ra.vs.y, ra.vs.z, ra.vs.w};
-  const uint32_t vwb[4] = {rb.vc.x, rb.vc.y, rb.vc.z, rb.vc.w};
-  const uint32_t vsb[4] = {rb.vs.x, rb.vs.y, rb.vs.z, rb.vs.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f16x2 ae02, ae13, ao02, ao13, be02, be13, bo02, bo13;
-    v_operands(vwa[q], vsa[q], ae02, ae13, ao02, ao13);
-    v_operands(vwb[q], vsb[q], be02, be13, bo02, bo13);
-    const f16x8 ve = {ae02[0], ae02[1], ae13[0], ae13[1], be02[0], be02[1], be13[0], be13[1]};
-    const f16x8 vo = {ao02[0], ao02[1], ao13[0], ao13[1], bo02[0], bo02[1], bo13[0], bo13[1]};
-    acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ve, pf, acc[2 * q], 0, 0, 0);
-    acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vo, pf, acc[2 * q + 1], 0, 0, 0);
-  }
-#endif
+  // ---- O^T += V^T P^T, 32 tokens per MFMA; tile q holds channels 8m + q ----
+  const uint32_t sa02 = v_scales02(ra.vs), sa13 = v_scales13(ra.vs);
+  const uint32_t sb02 = v_scales02(rb.vs), sb13 = v_scales13(rb.vs);
+  pv_tile<0>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[0]);
+  pv_tile<1>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[1]);
+  pv_tile<2>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[2]);
+  pv_tile<3>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[3]);
+  pv_tile<4>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[4]);
+  pv_tile<5>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[5]);
+  pv_tile<6>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[6]);
+  pv_tile<7>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[7]);
 }
 
 __global__ __launch_bounds__(64 * kWaves) void k_decode_split(DecodeArgs a) {
@@ -336,51 +317,14 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_split(DecodeArgs a) {
   const int pg0 = split * pps;
   const int pg1 = min(pg0 + pps, npages);
 
-  // ---- Q: head n of the group, channels 32G..32G+31, as f16 after rescale ----
-  const bool head_ok = n < a.group;
-  const int qh = h * a.group + n;
-  float qv[32];
-  {
-    const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.num_q_heads + (head_ok ? qh : 0)) * kHeadDim + 32 * G);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint4 u = head_ok ? qp[i] : make_uint4(0, 0, 0, 0);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qv[8 * i + 2 * e] = __uint_as_float(w[e] << 16);
-        qv[8 * i + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-      }
-    }
-  }
-  float qmax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) qmax = __builtin_fmaxf(qmax, __builtin_fabsf(qv[i]));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, off));
-  int qexp = 0;
-  if (qmax > 0.0f) {
-    int e2;
-    (void)__builtin_frexpf(qmax, &e2);  // qmax = m * 2^e2, m in [0.5, 1)
-    qexp = e2 - 15;                      // qmax * 2^-qexp in [2^14, 2^15)
-  }
-  // A negative softmax scale is carried by the query's sign (exact), so that the
-  // logit multiplier c below is positive.
-  const float qmul = a.qk_scale_log2 < 0.0f ? -__builtin_ldexpf(1.0f, -qexp) : __builtin_ldexpf(1.0f, -qexp);
-  f16x8 qf[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[s][e] = (_Float16)(qv[8 * s + e] * qmul);
-  // z (base-2 logit) = S_acc * c: undoes the Q rescale and the 1/256 of the K scales
-  const float c = __builtin_ldexpf(__builtin_fabsf(a.qk_scale_log2), qexp + 8);
-
   float m_ref = -__builtin_inff();
   float lsum = 0.0f;
   f32x4 acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const bool head_ok = n < a.group;
+  const int qh = h * a.group + n;
   const int32_t* pt_row = a.page_table + (int64_t)b * a.pt_stride;
   const uint8_t* pool_h = a.pool + (int64_t)h * (2 * kSlab);
   const int64_t page_bytes = (int64_t)a.num_kv_heads * (2 * kSlab);
@@ -397,9 +341,23 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_split(DecodeArgs a) {
     const int n_pairs = (n_pages + 1) / 2;
     const int lim = min(L, pg1 * kPage);  // tokens of this split end here
     const int32_t* pt_split = pt_row + pg0;
+    // Start-up: the first two id chunks and the group's queries are copied at
+    // once, the first pages go out as soon as the ids have landed, and the
+    // queries are converted while those pages are in flight. The queries are
+    // staged in the ring's last two slots, which the loop's first refill
+    // overwrites only after they have been read.
     issue_ids(pt_split, 0, n_pages, ids_lds, lane);
     issue_ids(pt_split, 1, n_pages, ids_lds, lane);
-    wait_dma<0>();
+    const uint32_t q_lds = ring_lds + (kRing - 2) * kSlotBytes;
+    {
+      const uint8_t* qsrc =
+          reinterpret_cast<const uint8_t*>(a.q + ((size_t)b * a.num_q_heads + (size_t)h * a.group) * kHeadDim);
+      const uint32_t qbytes = (uint32_t)a.group * (kHeadDim * 2);  // 256 .. 4096
+#pragma unroll
+      for (int k = 0; k < kQDmas; ++k)
+        dma16(qsrc, min((uint32_t)(k * 1024 + 16 * lane), qbytes - 16u), q_lds + k * 1024);
+    }
+    wait_dma<kQDmas>();  // the ids have landed
     int ids_v = ids[lane];  // chunk 0
     // The ring holds kPairsAhead + 1 pairs: one being computed, the others in
     // flight. Pages past the split's end re-read its last page (masked by `lim`),
@@ -408,6 +366,47 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_split(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 2 * kPairsAhead; ++j)
       issue_page(slab_of(pool_h, ids_v, min(j, n_pages - 1), page_bytes), off, ring_lds + j * kSlotBytes, lane);
+    wait_dma<2 * kPairsAhead * kDmaPerPage>();  // the queries have landed
+
+    // ---- Q: head n of the group, channels 32G..32G+31, as f16 after rescale ----
+    float qv[32];
+    {
+      const uint4* qp =
+          reinterpret_cast<const uint4*>(ring + (kRing - 2) * kSlotBytes + n * (kHeadDim * 2) + 64 * G);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 u = head_ok ? qp[i] : make_uint4(0, 0, 0, 0);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qv[8 * i + 2 * e] = __uint_as_float(w[e] << 16);
+          qv[8 * i + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // staging slots read: free for the refill
+    float qmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) qmax = __builtin_fmaxf(qmax, __builtin_fabsf(qv[i]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, o));
+    int qexp = 0;
+    if (qmax > 0.0f) {
+      int e2;
+      (void)__builtin_frexpf(qmax, &e2);  // qmax = m * 2^e2, m in [0.5, 1)
+      qexp = e2 - 15;                      // qmax * 2^-qexp in [2^14, 2^15)
+    }
+    // A negative softmax scale is carried by the query's sign (exact), so that the
+    // logit multiplier c below is positive.
+    const float qmul = a.qk_scale_log2 < 0.0f ? -__builtin_ldexpf(1.0f, -qexp) : __builtin_ldexpf(1.0f, -qexp);
+    f16x8 qf[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[st][e] = (_Float16)(qv[8 * st + e] * qmul);
+    // z (base-2 logit) = S_acc * c: undoes the Q rescale and the 1/256 of the K scales
+    const float c = __builtin_ldexpf(__builtin_fabsf(a.qk_scale_log2), qexp + 8);
+
     int cur = 0;  // ring slot of the current pair's first page
     for (int i = 0; i < n_pairs; ++i) {
       const int ahead = 2 * (i + kPairsAhead);  // first page of the pair to fetch now
@@ -437,15 +436,15 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_split(DecodeArgs a) {
   if (head_ok) {
     const size_t unit = ((size_t)b * a.num_q_heads + qh) * S + split;
     float* po = a.part_o + unit * kHeadDim;
-    // acc[2q + par][r] is O^T[channel 32q + 2(4G + r) + par][head n], in units of
-    // 1/256 of the value scale (the V scales were carried as E4M3/256)
+    // acc[q][r] is O^T[channel 8 (4G + r) + q][head n], in units of 1/256 of the
+    // value scale (the V scales were carried as E4M3/256)
     const float vs = a.v_scale * 256.0f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 v0 = make_float4(acc[2 * q][0] * vs, acc[2 * q + 1][0] * vs, acc[2 * q][1] * vs, acc[2 * q + 1][1] * vs);
-      const float4 v1 = make_float4(acc[2 * q][2] * vs, acc[2 * q + 1][2] * vs, acc[2 * q][3] * vs, acc[2 * q + 1][3] * vs);
-      *reinterpret_cast<float4*>(po + 32 * q + 8 * G) = v0;
-      *reinterpret_cast<float4*>(po + 32 * q + 8 * G + 4) = v1;
+    for (int r = 0; r < 4; ++r) {
+      const float4 v0 = make_float4(acc[0][r] * vs, acc[1][r] * vs, acc[2][r] * vs, acc[3][r] * vs);
+      const float4 v1 = make_float4(acc[4][r] * vs, acc[5][r] * vs, acc[6][r] * vs, acc[7][r] * vs);
+      *reinterpret_cast<float4*>(po + 32 * G + 8 * r) = v0;
+      *reinterpret_cast<float4*>(po + 32 * G + 8 * r + 4) = v1;
     }
     if (G == 0) *reinterpret_cast<float2*>(a.part_ml + unit * 2) = make_float2(m_ref, lsum);
   }

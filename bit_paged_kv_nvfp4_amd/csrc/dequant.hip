@@ -7,9 +7,10 @@
 //
 // One wave per (page, KV head, sequence). K: lane (t, G) reads channels
 // 32G..32G+31 of token t (16 code bytes) and their two scale bytes; V: lane
-// (n, G) reads its 16-byte chunk (tokens 4G..4G+3 of pairs n, 16+n, 32+n, 48+n)
-// and the matching scale bytes. Values E2M1(c) * E4M3(s) * g are exact in fp32
-// and in bf16 (at most 6 significant bits), so the workspace is bit-exact.
+// (n, G) reads its 16-byte chunk (channels 8n..8n+7 of tokens 4G..4G+3) and the
+// four scale bytes of block n/2 for those tokens. Values E2M1(c) * E4M3(s) * g
+// are exact in fp32 and in bf16 (at most 6 significant bits), so the workspace
+// is bit-exact.
 #include "nvfp4kv_device.h"
 
 namespace nvfp4kv {
@@ -65,29 +66,35 @@ __global__ __launch_bounds__(64) void k_dequant(DequantArgs a) {
     }
   }
 
-  // ---- V: tokens 4G..4G+3, channel pairs 16q + n ----
+  // ---- V: chunk `lane` = channels 8n..8n+7 of tokens 4G..4G+3 (block n/2) ----
   {
-    const uint4 vc = *reinterpret_cast<const uint4*>(vslab + (n * 4 + G) * 16);
-    const uint4 vs = *reinterpret_cast<const uint4*>(vslab + kCodeBytes + (G * 2 + (n >> 3)) * 16);
+    const uint4 vc = *reinterpret_cast<const uint4*>(vslab + 16 * lane);
+    const uint32_t vs = *reinterpret_cast<const uint32_t*>(vslab + kCodeBytes + (n >> 1) * 16 + 4 * G);
     const uint32_t vw[4] = {vc.x, vc.y, vc.z, vc.w};
-    const uint32_t vsw[4] = {vs.x, vs.y, vs.z, vs.w};
+    float val[4][8];  // [token 4G + i][channel 8n + e], unscaled
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int d = 32 * q + 2 * n;
+    for (int w = 0; w < 4; ++w) {
+      // byte 0: channel 2w of tokens 0|2, byte 1: channel 2w of tokens 1|3,
+      // bytes 2, 3: the same for channel 2w + 1
+      const f32x2 c0 = fp4x2_to_f32x2<0>(vw[w]), c1 = fp4x2_to_f32x2<1>(vw[w]);
+      const f32x2 c2 = fp4x2_to_f32x2<2>(vw[w]), c3 = fp4x2_to_f32x2<3>(vw[w]);
+      val[0][2 * w] = c0[0];
+      val[2][2 * w] = c0[1];
+      val[1][2 * w] = c1[0];
+      val[3][2 * w] = c1[1];
+      val[0][2 * w + 1] = c2[0];
+      val[2][2 * w + 1] = c2[1];
+      val[1][2 * w + 1] = c3[0];
+      val[3][2 * w + 1] = c3[1];
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = 4 * G + i;
-        if (pg * kPage + tok >= L) continue;
-        const float sc = e4m3_to_f32((vsw[q] >> (8 * i)) & 0xFFu) * a.g;
-        f32x2 v;
-        switch (i) {
-          case 0: v = dq2<0>(vw[q], sc); break;
-          case 1: v = dq2<1>(vw[q], sc); break;
-          case 2: v = dq2<2>(vw[q], sc); break;
-          default: v = dq2<3>(vw[q], sc); break;
-        }
-        store2(a.v_out, ((size_t)(row0 + tok) * H + h) * kHeadDim + d, v[0], v[1], bf16);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 4 * G + i;
+      if (pg * kPage + tok >= L) continue;
+      const float sc = e4m3_to_f32((vs >> (8 * i)) & 0xFFu) * a.g;
+      const size_t base = ((size_t)(row0 + tok) * H + h) * kHeadDim + 8 * n;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) store2(a.v_out, base + e, val[i][e] * sc, val[i][e + 1] * sc, bf16);
     }
   }
 }

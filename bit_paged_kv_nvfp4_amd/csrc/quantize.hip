@@ -95,25 +95,44 @@ __global__ __launch_bounds__(256) void k_quantize(QuantizeArgs a) {
   const int s = scale_byte(amax, 6.0f * a.g);
   const float D = e4m3_value(s) * a.g;
   const bool zs = (s == 0);
-  uint32_t bytes[8];
+  uint32_t code[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) bytes[i] = e2m1_code(x[2 * i], D, zs) | (e2m1_code(x[2 * i + 1], D, zs) << 4);
+  for (int i = 0; i < 16; ++i) code[i] = e2m1_code(x[i], D, zs);
 
   const int64_t page = slot >> 4;
   const int row = slot & 15;
   uint8_t* slab = a.pool + ((page * a.num_kv_heads + h) * 2 + kind) * (int64_t)kSlab;
   if (kind == 0) {
-    const uint32_t lo = bytes[0] | (bytes[1] << 8) | (bytes[2] << 16) | (bytes[3] << 24);
-    const uint32_t hi = bytes[4] | (bytes[5] << 8) | (bytes[6] << 16) | (bytes[7] << 24);
-    *reinterpret_cast<uint2*>(slab + row * 64 + j * 8) = make_uint2(lo, hi);
+    // K: the token's 8 code bytes of block j are contiguous, channel 2i in the low
+    // nibble of byte i
+    uint32_t w[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      w[half] = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[half] |= code[8 * half + i] << (4 * i);
+    }
+    *reinterpret_cast<uint2*>(slab + row * 64 + j * 8) = make_uint2(w[0], w[1]);
     slab[kCodeBytes + row * 8 + j] = (uint8_t)s;
   } else {
+    // V: channel 16j + e sits in 16-byte chunk (row/4)*16 + 2j + e/8, byte
+    // 2*(e%8) + row%2, high nibble for rows with row%4 >= 2; the other nibble of
+    // each byte is row r ^ 2 of the same page, which another thread (or another
+    // call) may be writing, so the block's nibbles are cleared and set with 32-bit
+    // atomics that leave every other bit alone.
+    const int sh = 8 * (row & 1) + 4 * ((row >> 1) & 1);
+    const uint32_t mask = (0xFu << sh) | (0xFu << (sh + 16));
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int pair = 8 * j + k;
-      slab[((pair & 15) * 4 + (row >> 2)) * 16 + (pair >> 4) * 4 + (row & 3)] = (uint8_t)bytes[k];
+    for (int c = 0; c < 2; ++c) {
+      uint32_t* chunk = reinterpret_cast<uint32_t*>(slab + ((row >> 2) * 16 + 2 * j + c) * 16);
+#pragma unroll
+      for (int wi = 0; wi < 4; ++wi) {
+        const uint32_t val = (code[8 * c + 2 * wi] << sh) | (code[8 * c + 2 * wi + 1] << (sh + 16));
+        __hip_atomic_fetch_and(chunk + wi, ~mask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(chunk + wi, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
-    slab[kCodeBytes + ((row >> 2) * 2 + (j & 1)) * 16 + (j >> 1) * 4 + (row & 3)] = (uint8_t)s;
+    slab[kCodeBytes + j * 16 + row] = (uint8_t)s;
   }
 }
 

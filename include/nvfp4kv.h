@@ -34,16 +34,20 @@
  * Pool layout (NVFP4KV_SLAB_BYTES = 1152 per slab):
  *   slab(page p, KV head h, kind k) starts at byte ((p*Hkv + h)*2 + k) * 1152,
  *   k = 0 for K, 1 for V. A slab holds the 16 token rows r of page p for head h:
- *   1024 code bytes, then 128 scale bytes. Code byte of pair i (channels 2i in
- *   the low nibble, 2i+1 in the high nibble) and scale byte of block j
- *   (channels 16j..16j+15):
- *     K:  code (r, i) at r*64 + i            scale (r, j) at 1024 + r*8 + j
- *     V:  code (r, i) at ((i%16)*4 + r/4)*16 + (i/16)*4 + r%4
- *         scale (r, j) at 1024 + ((r/4)*2 + j%2)*16 + (j/2)*4 + r%4
- *   K rows are token-major. V is grouped so that each 16-byte chunk holds four
- *   consecutive tokens of four channel pairs, the shape the decode kernel's
- *   matrix-core operands take; every byte still belongs to one token, so
- *   writing a token never touches another token's bytes.
+ *   1024 code bytes (one 4-bit code per value), then 128 scale bytes (block j =
+ *   channels 16j..16j+15):
+ *     K code (r, d):  byte r*64 + d/2, low nibble for even d, high for odd d
+ *     K scale (r, j): byte 1024 + r*8 + j
+ *     V code (r, d):  byte ((r/4)*16 + d/8)*16 + 2*(d%8) + r%2,
+ *                     low nibble for r%4 < 2, high nibble for r%4 >= 2
+ *     V scale (r, j): byte 1024 + j*16 + r
+ *   K rows are token-major. V is cut into 64 chunks of 16 bytes; chunk
+ *   (r/4)*16 + d/8 holds channels 8(d/8)..+7 of tokens 4(r/4)..+3, and each of
+ *   its bytes holds one channel of two tokens (r and r+2), the pairs the decode
+ *   kernel's matrix-core operands take along the token axis. A V byte is
+ *   therefore shared by two tokens: nvfp4_kv_quantize updates only the written
+ *   token's nibbles (atomically), so tokens of one page may be written by
+ *   different calls or by one call in any order.
  *   Token t of a sequence lives at page page_table[t/16], row t%16.
  *
  * Conventions for every entry point:

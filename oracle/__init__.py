@@ -64,8 +64,8 @@ def _load(path: str) -> ctypes.CDLL:
     L.orc_quantize_block16.restype = None
     L.orc_slab_offset.argtypes = [c.c_int64, c.c_int, c.c_int, c.c_int]
     L.orc_slab_offset.restype = c.c_int64
-    L.orc_code_byte_offset.argtypes = [c.c_int, c.c_int, c.c_int]
-    L.orc_code_byte_offset.restype = c.c_int
+    L.orc_code_nibble.argtypes = [c.c_int, c.c_int, c.c_int]
+    L.orc_code_nibble.restype = c.c_int
     L.orc_scale_byte_offset.argtypes = [c.c_int, c.c_int, c.c_int]
     L.orc_scale_byte_offset.restype = c.c_int
     L.orc_pool_bytes.argtypes = [c.c_int64, c.c_int]
@@ -126,8 +126,9 @@ def source_text() -> str:
         return f.read()
 
 
-def code_byte_offset(kind: int, row: int, pair: int) -> int:
-    return int(lib().orc_code_byte_offset(int(kind), int(row), int(pair)))
+def code_nibble(kind: int, row: int, channel: int) -> int:
+    """Place of the code of (row, channel) in a slab: 2 * byte + (1 for the high nibble)."""
+    return int(lib().orc_code_nibble(int(kind), int(row), int(channel)))
 
 
 def scale_byte_offset(kind: int, row: int, block: int) -> int:

@@ -30,9 +30,9 @@
  *      even code, saturating at 6; the sign bit is the sign bit of x. When the
  *      scale is zero every code has magnitude 0 (a reading; the pages are
  *      silent).
- *   5. Packing: byte i of a token's 64 code bytes holds element 2i in its low
- *      nibble and element 2i+1 in its high nibble; 8 data bytes plus 1 scale
- *      byte per 16 values ([LMSYS] "Interpretation").
+ *   5. Packing: each code is one nibble; 8 data bytes plus 1 scale byte per 16
+ *      values ([LMSYS] "Interpretation"). Where the nibbles sit is the pool
+ *      layout below (a storage choice the pages leave open).
  *   6. Dequantization: x^ = E2M1(c) * E4M3(s) * g ([LMSYS] "Interpretation":
  *      decode dequantizes inside the attention kernel).
  *   7. Attention for decode: softmax(sm_scale * q . k^_t) weighted sum of v^_t
@@ -46,11 +46,14 @@
  *   then a V slab of 1152 bytes each:  slab(p, h, kind) starts at byte
  *   ((p * Hkv + h) * 2 + kind) * 1152, kind 0 = K, 1 = V. A slab covers the 16
  *   token rows r of the page and the 128 channels d of the head: 1024 code
- *   bytes, then 128 scale bytes.
- *     K code byte (row r, pair i = d/2):  r*64 + i
- *     K scale byte (row r, block j = d/16): 1024 + r*8 + j
- *     V code byte (row r, pair i):  ((i%16)*4 + r/4)*16 + (i/16)*4 + r%4
- *     V scale byte (row r, block j): 1024 + ((r/4)*2 + j%2)*16 + (j/2)*4 + r%4
+ *   bytes, then 128 scale bytes. A code's place is a nibble index
+ *   2 * byte + (1 for the high nibble):
+ *     K code (row r, channel d): byte r*64 + d/2, high nibble iff d is odd
+ *     K scale (row r, block j = d/16): byte 1024 + r*8 + j
+ *     V code (row r, channel d): byte ((r/4)*16 + d/8)*16 + 2*(d%8) + r%2,
+ *                                high nibble iff r%4 >= 2
+ *     V scale (row r, block j): byte 1024 + j*16 + r
+ *   (a V code byte holds rows r and r+2 of one channel).
  *   Token t of a sequence lives at page page_table[t/16], row t%16.
  */
 #include <math.h>
@@ -156,13 +159,29 @@ void orc_quantize_block16(const float* x, float g, uint8_t* codes8, uint8_t* sca
 int64_t orc_slab_offset(int64_t page, int head, int kind, int num_kv_heads) {
   return ((page * num_kv_heads + head) * 2 + kind) * (int64_t)ORC_SLAB;
 }
-int orc_code_byte_offset(int kind, int row, int pair) {
-  if (kind == 0) return row * 64 + pair;
-  return ((pair % 16) * 4 + row / 4) * 16 + (pair / 16) * 4 + row % 4;
+int orc_code_nibble(int kind, int row, int d) {
+  int byte, high;
+  if (kind == 0) {
+    byte = row * 64 + d / 2;
+    high = d % 2;
+  } else {
+    byte = ((row / 4) * 16 + d / 8) * 16 + 2 * (d % 8) + row % 2;
+    high = (row % 4) >= 2;
+  }
+  return 2 * byte + high;
 }
 int orc_scale_byte_offset(int kind, int row, int block) {
   if (kind == 0) return 1024 + row * 8 + block;
-  return 1024 + ((row / 4) * 2 + block % 2) * 16 + (block / 2) * 4 + row % 4;
+  return 1024 + block * 16 + row;
+}
+static void orc_put_nibble(uint8_t* slab, int nibble, int code) {
+  uint8_t* b = slab + nibble / 2;
+  if (nibble % 2) *b = (uint8_t)((*b & 0x0F) | (code << 4));
+  else *b = (uint8_t)((*b & 0xF0) | code);
+}
+static int orc_get_nibble(const uint8_t* slab, int nibble) {
+  int b = slab[nibble / 2];
+  return (nibble % 2) ? (b >> 4) : (b & 15);
 }
 int64_t orc_pool_bytes(int64_t num_pages, int num_kv_heads) {
   return num_pages * num_kv_heads * 2 * (int64_t)ORC_SLAB;
@@ -177,8 +196,9 @@ static float orc_bf16_to_float(uint16_t b) {
 
 /* Quantize-on-write of T tokens of K and V ([T][Hkv][128], element strides
  * given) into the pool at slot_mapping[t] = page*16 + row (negative = skip).
- * src_dtype 0 = float32, 1 = bfloat16 bits. Tokens are spread over n_threads
- * threads; each token's bytes are computed the same way by any thread. */
+ * src_dtype 0 = float32, 1 = bfloat16 bits. Pages are spread over n_threads
+ * threads (a V code byte holds two rows of a page, so one page has one writer);
+ * each token's codes are computed the same way by any thread. */
 typedef struct {
   const void *k_src, *v_src;
   int src_dtype;
@@ -188,6 +208,7 @@ typedef struct {
   int num_kv_heads;
   float g;
   uint8_t* pool;
+  int part, n_parts; /* this worker writes the pages with page % n_parts == part */
 } orc_quant_job;
 
 static void* orc_quant_worker(void* arg) {
@@ -199,6 +220,7 @@ static void* orc_quant_worker(void* arg) {
     if (slot < 0) continue;
     int64_t page = slot / ORC_PAGE;
     int row = slot % ORC_PAGE;
+    if (page % J->n_parts != J->part) continue; /* V bytes are shared by two rows */
     for (h = 0; h < J->num_kv_heads; ++h) {
       for (kind = 0; kind < 2; ++kind) {
         const void* src = kind == 0 ? J->k_src : J->v_src;
@@ -212,7 +234,10 @@ static void* orc_quant_worker(void* arg) {
                                      : orc_bf16_to_float(((const uint16_t*)src)[idx]);
           }
           orc_quantize_block16(x, J->g, codes, &s);
-          for (i = 0; i < 8; ++i) slab[orc_code_byte_offset(kind, row, 8 * j + i)] = codes[i];
+          for (i = 0; i < 8; ++i) {
+            orc_put_nibble(slab, orc_code_nibble(kind, row, 16 * j + 2 * i), codes[i] & 15);
+            orc_put_nibble(slab, orc_code_nibble(kind, row, 16 * j + 2 * i + 1), codes[i] >> 4);
+          }
           slab[orc_scale_byte_offset(kind, row, j)] = s;
         }
       }
@@ -237,8 +262,10 @@ void orc_quantize_to_pool(const void* k_src, const void* v_src, int src_dtype, i
     J->token_stride = token_stride;
     J->head_stride = head_stride;
     J->slot_mapping = slot_mapping;
-    J->t_begin = num_tokens * i / n_threads;
-    J->t_end = num_tokens * (i + 1) / n_threads;
+    J->t_begin = 0;
+    J->t_end = num_tokens;
+    J->part = i;
+    J->n_parts = n_threads;
     J->num_kv_heads = num_kv_heads;
     J->g = g;
     J->pool = pool;
@@ -257,8 +284,7 @@ void orc_dequant_row(const uint8_t* pool, int64_t page, int row, int head, int k
   const uint8_t* slab = pool + orc_slab_offset(page, head, kind, num_kv_heads);
   int d;
   for (d = 0; d < ORC_D; ++d) {
-    int byte = slab[orc_code_byte_offset(kind, row, d / 2)];
-    int code = (d & 1) ? (byte >> 4) : (byte & 15);
+    int code = orc_get_nibble(slab, orc_code_nibble(kind, row, d));
     int s = slab[orc_scale_byte_offset(kind, row, d / 16)];
     out128[d] = orc_e2m1_value(code) * orc_e4m3_value(s) * (double)g;
   }

@@ -27,8 +27,10 @@ MUTANTS = [
     ("amax_misses_last", "for (i = 0; i < 16; ++i) {\n    float a", "for (i = 0; i < 15; ++i) {\n    float a"),
     ("dequant_drops_scale", "out128[d] = orc_e2m1_value(code) * orc_e4m3_value(s) * (double)g;",
      "out128[d] = orc_e2m1_value(code) * (double)g;"),
-    ("dequant_wrong_nibble", "int code = (d & 1) ? (byte >> 4) : (byte & 15);",
-     "int code = (d & 1) ? (byte & 15) : (byte >> 4);"),
+    ("dequant_wrong_nibble", "int code = orc_get_nibble(slab, orc_code_nibble(kind, row, d));",
+     "int code = orc_get_nibble(slab, orc_code_nibble(kind, row, d) ^ 1);"),
+    ("v_rows_share_a_nibble", "high = (row % 4) >= 2;", "high = 0;"),
+    ("put_nibble_clears_neighbour", "*b = (uint8_t)((*b & 0x0F) | (code << 4));", "*b = (uint8_t)(code << 4);"),
     ("dequant_wrong_block", "int s = slab[orc_scale_byte_offset(kind, row, d / 16)];",
      "int s = slab[orc_scale_byte_offset(kind, row, d / 32)];"),
     ("gqa_head_modulo", "int h = qh / group;", "int h = qh % J->num_kv_heads;"),
@@ -87,10 +89,22 @@ def test_unmutated_oracle_passes_all_mutation_pins():
 
 def test_pool_layout_is_a_bijection(oracle_lib):
     for kind in (0, 1):
-        codes = {oracle_lib.code_byte_offset(kind, r, i) for r in range(16) for i in range(64)}
+        codes = {oracle_lib.code_nibble(kind, r, d) for r in range(16) for d in range(128)}
         scales = {oracle_lib.scale_byte_offset(kind, r, j) for r in range(16) for j in range(8)}
-        assert codes == set(range(1024)) and scales == set(range(1024, 1152))
-    # K rows are token-major (64 contiguous code bytes, 8 contiguous scale bytes per token)
-    assert [oracle_lib.code_byte_offset(0, 3, i) for i in range(64)] == list(range(192, 256))
+        assert codes == set(range(2048)) and scales == set(range(1024, 1152))
+    # K rows are token-major (64 contiguous code bytes, low nibble = even channel;
+    # 8 contiguous scale bytes per token)
+    assert [oracle_lib.code_nibble(0, 3, d) for d in range(128)] == list(range(384, 512))
     assert [oracle_lib.scale_byte_offset(0, 3, j) for j in range(8)] == list(range(1048, 1056))
+    # V: 16-byte chunk c = 16 (r // 4) + d // 8 holds channels 8 (c % 16) .. +7 of
+    # rows 4 (c // 16) .. +3; a byte holds rows r and r + 2 of one channel
+    for c in range(64):
+        nib = {oracle_lib.code_nibble(1, 4 * (c // 16) + i, 8 * (c % 16) + e) for i in range(4) for e in range(8)}
+        assert nib == set(range(32 * c, 32 * c + 32))
+    for r in range(16):
+        for d in range(128):
+            lo, hi = oracle_lib.code_nibble(1, r, d), oracle_lib.code_nibble(1, r ^ 2, d)
+            assert lo // 2 == hi // 2 and (lo % 2) == (r % 4 >= 2)
+    # V scales: block-major, 16 rows per block
+    assert [oracle_lib.scale_byte_offset(1, r, 5) for r in range(16)] == list(range(1104, 1120))
     assert oracle_lib.slab_offset(2, 1, 1, 8) == ((2 * 8 + 1) * 2 + 1) * 1152
