@@ -96,11 +96,14 @@ int32_t nvfp4_paged_decode_attn_default_splits(int32_t batch, int32_t num_kv_hea
   }
   const int64_t pages = (max_seq_len + NVFP4KV_PAGE_SIZE - 1) / NVFP4KV_PAGE_SIZE;
   const int64_t units = (int64_t)batch * num_kv_heads;
-  // About 22 one-wave work items per CU: 1.375 rounds of the 16 resident waves a
-  // CU holds, so the scheduler can even out waves that finish at different times.
-  const int64_t target_waves = (int64_t)num_cus * 22;
-  int64_t s = (target_waves + units - 1) / units;
-  const int64_t max_by_pages = pages / 4 > 1 ? pages / 4 : 1;
+  const int64_t wps = nvfp4kv::decode_waves_per_split();
+  // About 44 waves per CU: 2.75 rounds of the 16 resident waves a CU holds, so
+  // the scheduler can even out workgroups that finish at different times (more
+  // splits add partial states, whose writes cost read bandwidth). Each split is
+  // one workgroup of `wps` waves; every wave keeps at least 4 pages.
+  const int64_t target_waves = (int64_t)num_cus * 44;
+  int64_t s = (target_waves + units * wps - 1) / (units * wps);
+  const int64_t max_by_pages = pages / (4 * wps) > 1 ? pages / (4 * wps) : 1;
   if (s > max_by_pages) s = max_by_pages;
   if (s > NVFP4KV_MAX_SPLITS) s = NVFP4KV_MAX_SPLITS;
   if (s < 1) s = 1;

@@ -83,12 +83,16 @@ constexpr int kSlotBytes = 2 * kSlab;  // 2304
 #endif
 constexpr int kPairsAhead = NVFP4KV_DECODE_PAIRS_AHEAD;  // pairs of pages in flight while one is computed
 constexpr int kRing = 2 * (kPairsAhead + 1);              // LDS slots (pages) per wave
-// Independent waves per workgroup: each owns one split and its own LDS region;
-// several waves per workgroup keep the per-CU workgroup count low.
+// Waves per workgroup. The workgroup owns one split; each wave takes a contiguous
+// quarter (for 4 waves) of its pages with its own LDS region, and the last wave
+// to finish merges the waves' online-softmax states in LDS, so a split writes
+// one partial state. Partial states are the only HBM writes of the kernel, and
+// written mid-stream they cost far more read bandwidth than their size.
 constexpr int kWaves = NVFP4KV_DECODE_WAVES;
 constexpr int kDmaPerPage = 3;
 constexpr int kQDmas = 4;  // 1 KB copies of the group's queries (up to 16 heads x 256 B)
 static_assert(kRing >= 4, "the query staging area takes the ring's last two slots");
+static_assert(kRing * kSlotBytes >= 8 * 64 * 16 + 16 * 8, "a wave's state must fit its ring region");
 
 // One asynchronous 16-byte-per-lane copy global -> LDS (gfx950 global_load_lds
 // dwordx4): lane i reads base + voff and writes LDS address lds + 16 i. It is
@@ -302,7 +306,7 @@ __device__ __forceinline__ void pair_step(const PageRegs& ra, const PageRegs& rb
 
 __global__ __launch_bounds__(64 * kWaves) void k_decode_split(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform by construction
-  const int split = blockIdx.x * kWaves + wave;
+  const int split = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
@@ -310,12 +314,20 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_split(DecodeArgs a) {
   const int G = lane >> 4;
   const int S = a.num_splits;
 
-  if (split >= S) return;  // waves never synchronize, so a spare wave may leave
+  __shared__ int waves_done;
+  if (threadIdx.x == 0) waves_done = 0;
+  __syncthreads();
+
   const int L = a.seq_lens[b];
   const int npages = (L + kPage - 1) / kPage;
   const int pps = (npages + S - 1) / S;
-  const int pg0 = split * pps;
-  const int pg1 = min(pg0 + pps, npages);
+  const int split_pg0 = min(split * pps, npages);
+  const int split_pg1 = min(split_pg0 + pps, npages);
+  // this wave's share: an even number of pages, so that only the last pair of the
+  // share can hold masked rows
+  const int share = (((split_pg1 - split_pg0 + kWaves - 1) / kWaves) + 1) & ~1;
+  const int pg0 = min(split_pg0 + wave * share, split_pg1);
+  const int pg1 = min(pg0 + share, split_pg1);
 
   float m_ref = -__builtin_inff();
   float lsum = 0.0f;
@@ -430,32 +442,76 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_split(DecodeArgs a) {
     wait_dma<0>();  // no copy may outlive the wave's LDS
   }
 
-  // ---- partial result of this split ----
+  // ---- merge the waves' states; the last wave to finish writes the split's ----
   lsum = xor16_sum(lsum);
-  lsum = xor32_sum(lsum);
+  lsum = xor32_sum(lsum);  // per head n, on every lane of head n
+  {
+    // own state into own ring region (its copies have all landed): acc as
+    // [q][lane] float4s, then (m, l) per head
+    float4* acc_lds = reinterpret_cast<float4*>(ring);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc_lds[q * 64 + lane] = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+    if (G == 0) reinterpret_cast<float2*>(ring + 8 * 64 * 16)[n] = make_float2(m_ref, lsum);
+  }
+  int prior = 0;
+  if (lane == 0) prior = __hip_atomic_fetch_add(&waves_done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+  prior = __builtin_amdgcn_readfirstlane(prior);
+  if (prior != kWaves - 1) return;  // not the last wave of the split
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+  float mw[kWaves], lw[kWaves];
+  float m_all = -__builtin_inff();
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float2 ml = reinterpret_cast<const float2*>(&ring_all[w][0] + 8 * 64 * 16)[n];
+    mw[w] = ml.x;
+    lw[w] = ml.y;
+    m_all = __builtin_fmaxf(m_all, ml.x);
+  }
+  float l_all = 0.0f;
+  f32x4 o_all[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) o_all[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    // an empty share has m = -inf and weight 0; so does everything when all are
+    const float f = (mw[w] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - m_all);
+    l_all += f * lw[w];
+    const float4* src = reinterpret_cast<const float4*>(&ring_all[w][0]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 v = src[q * 64 + lane];
+      o_all[q][0] += f * v.x;
+      o_all[q][1] += f * v.y;
+      o_all[q][2] += f * v.z;
+      o_all[q][3] += f * v.w;
+    }
+  }
+
   if (head_ok) {
     const size_t unit = ((size_t)b * a.num_q_heads + qh) * S + split;
     float* po = a.part_o + unit * kHeadDim;
-    // acc[q][r] is O^T[channel 8 (4G + r) + q][head n], in units of 1/256 of the
+    // o_all[q][r] is O^T[channel 8 (4G + r) + q][head n], in units of 1/256 of the
     // value scale (the V scales were carried as E4M3/256)
     const float vs = a.v_scale * 256.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float4 v0 = make_float4(acc[0][r] * vs, acc[1][r] * vs, acc[2][r] * vs, acc[3][r] * vs);
-      const float4 v1 = make_float4(acc[4][r] * vs, acc[5][r] * vs, acc[6][r] * vs, acc[7][r] * vs);
+      const float4 v0 = make_float4(o_all[0][r] * vs, o_all[1][r] * vs, o_all[2][r] * vs, o_all[3][r] * vs);
+      const float4 v1 = make_float4(o_all[4][r] * vs, o_all[5][r] * vs, o_all[6][r] * vs, o_all[7][r] * vs);
       *reinterpret_cast<float4*>(po + 32 * G + 8 * r) = v0;
       *reinterpret_cast<float4*>(po + 32 * G + 8 * r + 4) = v1;
     }
-    if (G == 0) *reinterpret_cast<float2*>(a.part_ml + unit * 2) = make_float2(m_ref, lsum);
+    if (G == 0) *reinterpret_cast<float2*>(a.part_ml + unit * 2) = make_float2(m_all, l_all);
   }
 }
 
 }  // namespace
 
+int decode_waves_per_split() { return kWaves; }
+
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_decode_split, dim3((a.num_splits + kWaves - 1) / kWaves, a.num_kv_heads, a.batch),
-                     dim3(64 * kWaves), 0, stream, a);
+  hipLaunchKernelGGL(k_decode_split, dim3(a.num_splits, a.num_kv_heads, a.batch), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 

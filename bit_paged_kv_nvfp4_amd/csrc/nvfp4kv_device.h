@@ -69,6 +69,8 @@ struct DequantArgs {
 };
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
+// Waves that share one split of the decode kernel (one workgroup per split).
+int decode_waves_per_split();
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);

@@ -132,10 +132,11 @@ int32_t nvfp4_kv_quantize(const void* k_src, const void* v_src, int32_t src_dtyp
                           const nvfp4kv_pool* pool, void* stream);
 
 /*
- * Split count the decode call uses when passed num_splits = 0: about 22
- * (sequence, KV head, split) work items per compute unit (1.375 rounds of the
- * waves a CU keeps resident), at least 4 pages per split, at most
- * NVFP4KV_MAX_SPLITS. num_cus <= 0 asks the current
+ * Split count the decode call uses when passed num_splits = 0. Each (sequence,
+ * KV head, split) is one workgroup of 4 waves that share the split's pages; the
+ * default gives about 44 waves per compute unit (2.75 rounds of the waves a CU
+ * keeps resident), at least 4 pages per wave, at most NVFP4KV_MAX_SPLITS.
+ * num_cus <= 0 asks the current
  * HIP device for its compute-unit count (the only HIP call of this function).
  * Returns >= 1.
  */
