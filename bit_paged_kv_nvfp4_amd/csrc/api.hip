@@ -95,15 +95,14 @@ int32_t nvfp4_paged_decode_attn_default_splits(int32_t batch, int32_t num_kv_hea
     num_cus = cus;
   }
   const int64_t pages = (max_seq_len + NVFP4KV_PAGE_SIZE - 1) / NVFP4KV_PAGE_SIZE;
-  const int64_t units = (int64_t)batch * num_kv_heads;
-  const int64_t wps = nvfp4kv::decode_waves_per_split();
-  // About 44 waves per CU: 2.75 rounds of the 16 resident waves a CU holds, so
-  // the scheduler can even out workgroups that finish at different times (more
-  // splits add partial states, whose writes cost read bandwidth). Each split is
-  // one workgroup of `wps` waves; every wave keeps at least 4 pages.
-  const int64_t target_waves = (int64_t)num_cus * 44;
-  int64_t s = (target_waves + units * wps - 1) / (units * wps);
-  const int64_t max_by_pages = pages / (4 * wps) > 1 ? pages / (4 * wps) : 1;
+  const int64_t segments = (int64_t)batch * num_kv_heads;
+  // Splits are the grain at which the persistent workgroups' page windows are
+  // cut: about 16 splits per window keeps the windows within about 6% of each
+  // other. Consecutive splits in one window share one state, so more splits do
+  // not mean more partial-state writes. At least 4 pages per split.
+  const int64_t windows = nvfp4kv::decode_resident_workgroups(num_cus);
+  int64_t s = (16 * windows + segments - 1) / segments;
+  const int64_t max_by_pages = pages / 4 > 1 ? pages / 4 : 1;
   if (s > max_by_pages) s = max_by_pages;
   if (s > NVFP4KV_MAX_SPLITS) s = NVFP4KV_MAX_SPLITS;
   if (s < 1) s = 1;
@@ -122,6 +121,22 @@ size_t nvfp4_paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_head
 
 namespace {
 
+bool query_cus(int* cus) {
+  int dev = 0;
+  return hipGetDevice(&dev) == hipSuccess &&
+         hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && *cus > 0;
+}
+
+// Sizes the persistent grid of the decode kernel from the current device (the
+// last step before a launch: every argument check has run by then).
+int32_t finish_decode(nvfp4kv::DecodeArgs& a) {
+  if (a.num_workgroups > 0) return NVFP4KV_OK;
+  int cus = 0;
+  if (!query_cus(&cus)) return NVFP4KV_ERR_HIP;
+  a.num_workgroups = nvfp4kv::decode_resident_workgroups(cus);
+  return NVFP4KV_OK;
+}
+
 // Shared validation of the decode phases; fills `a` (without out/lse).
 int32_t prepare_decode(const void* q, const int32_t* page_table, int64_t page_table_stride, const int32_t* seq_lens,
                        int32_t batch, int32_t num_q_heads, int32_t max_seq_len, const nvfp4kv_pool* pool,
@@ -135,14 +150,19 @@ int32_t prepare_decode(const void* q, const int32_t* page_table, int64_t page_ta
   if (group < 1 || group > NVFP4KV_MAX_GROUP) return NVFP4KV_ERR_SHAPE;
   if ((int64_t)max_seq_len > page_table_stride * NVFP4KV_PAGE_SIZE) return NVFP4KV_ERR_SHAPE;
   if (*num_splits < 0 || *num_splits > NVFP4KV_MAX_SPLITS) return NVFP4KV_ERR_SHAPE;
-  if (batch > 65535 || hkv > 65535) return NVFP4KV_ERR_SHAPE;  // grid limits of the split kernel
   if (!isfinite(sm_scale)) return NVFP4KV_ERR_VALUE;
   if (batch == 0) return NVFP4KV_OK;
   if (!q || !page_table || !seq_lens || !workspace) return NVFP4KV_ERR_NULL;
   if (!aligned16(q) || !aligned16(workspace) || (reinterpret_cast<uintptr_t>(page_table) & 3u) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
     return NVFP4KV_ERR_ALIGN;
-  if (*num_splits == 0) *num_splits = nvfp4_paged_decode_attn_default_splits(batch, hkv, max_seq_len, 0);
+  // the device's CU count sizes the persistent grid (finish_decode) and the
+  // default split count; with num_splits given, no HIP call happens here
+  int cus = 0;
+  if (*num_splits == 0) {
+    if (!query_cus(&cus)) return NVFP4KV_ERR_HIP;
+    *num_splits = nvfp4_paged_decode_attn_default_splits(batch, hkv, max_seq_len, cus);
+  }
   const size_t need = nvfp4_paged_decode_attn_workspace_bytes(batch, num_q_heads, *num_splits);
   if (need == 0 || workspace_bytes < need) return NVFP4KV_ERR_WORKSPACE;
   a.q = static_cast<const uint16_t*>(q);
@@ -158,6 +178,7 @@ int32_t prepare_decode(const void* q, const int32_t* page_table, int64_t page_ta
   a.qk_scale_log2 = (float)((double)sm_scale * 1.4426950408889634 * (double)pool->global_scale);
   a.v_scale = pool->global_scale;
   a.num_splits = *num_splits;
+  a.num_workgroups = cus > 0 ? nvfp4kv::decode_resident_workgroups(cus) : 0;  // 0: finish_decode sets it
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = a.part_o + (size_t)batch * num_q_heads * *num_splits * NVFP4KV_HEAD_DIM;
   a.out = nullptr;
@@ -202,6 +223,7 @@ int32_t nvfp4_paged_decode_attn_partial(const void* q, const int32_t* page_table
                                  sm_scale, &num_splits, workspace, workspace_bytes, a))
     return e;
   if (batch == 0) return NVFP4KV_OK;
+  if (int32_t e = finish_decode(a)) return e;
   return hip_status(nvfp4kv::launch_decode_partial(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -230,6 +252,7 @@ int32_t nvfp4_paged_decode_attn(const void* q, const int32_t* page_table, int64_
   nvfp4kv::DecodeArgs c;
   if (int32_t e = prepare_combine(workspace, workspace_bytes, batch, num_q_heads, num_splits, out, out_dtype, lse, c))
     return e;
+  if (int32_t e = finish_decode(a)) return e;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (int32_t e = hip_status(nvfp4kv::launch_decode_partial(a, st))) return e;
   return hip_status(nvfp4kv::launch_decode_combine(c, st));

@@ -4,14 +4,16 @@
 // the split kernel are merged: M* = max M_s, w_s = 2^(M_s - M*) (0 for an empty
 // split), out = sum w_s O_s / sum w_s Z_s, lse = (M* + log2 sum w_s Z_s) ln 2.
 // One wave per (sequence, query head); lane i owns output channels 2i and 2i+1.
-// Up to 32 splits, every load of the unit is issued before the first use, so
-// the merge costs one memory round trip; more splits run in chunks of 32.
+// The (M, Z) pairs are read first (lanes stride over the splits); O is read
+// only for splits of nonzero weight: an empty split's O is never written (its
+// pages were merged into another split's state), and at most 16 O rows are in
+// flight at once.
 #include "nvfp4kv_device.h"
 
 namespace nvfp4kv {
 namespace {
 
-constexpr int kChunk = 32;
+constexpr int kBatch = 16;
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -31,30 +33,39 @@ __global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
   const float2* __restrict__ ml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)unit * S;
   const float* __restrict__ po = a.part_o + (size_t)unit * S * kHeadDim + 2 * lane;
 
-  // pass over the (M, Z) pairs: lanes stride over the splits
   float M = -__builtin_inff();
   for (int i = lane; i < S; i += 64) M = __builtin_fmaxf(M, ml[i].x);
   M = wave_max(M);
   float o0 = 0.0f, o1 = 0.0f, Ls = 0.0f;
   if (M != -__builtin_inff()) {
-    for (int c0 = 0; c0 < S; c0 += kChunk) {
-      const int n = min(kChunk, S - c0);
-      float2 v[kChunk];
-      float2 st = make_float2(-__builtin_inff(), 0.0f);
-      // issue the chunk's loads together: each lane's two channels of every split,
-      // and (lanes < n) the split's (M, Z)
-#pragma unroll
-      for (int i = 0; i < kChunk; ++i)
-        v[i] = i < n ? *reinterpret_cast<const float2*>(po + (size_t)(c0 + i) * kHeadDim) : make_float2(0.f, 0.f);
-      if (lane < n) st = ml[c0 + lane];
-      const float wl = __builtin_amdgcn_exp2f(st.x - M);  // weight of split c0 + lane (0 if empty / absent)
+    for (int c0 = 0; c0 < S; c0 += 64) {
+      const float2 st = c0 + lane < S ? ml[c0 + lane] : make_float2(-__builtin_inff(), 0.0f);
+      const float wl = st.x == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(st.x - M);
       Ls += wl * st.y;
+      uint64_t live = __builtin_amdgcn_ballot_w64(wl > 0.0f);  // splits whose O contributes
+      while (live) {
+        int idx[kBatch];
+        float2 v[kBatch];
+        int cnt = 0;
 #pragma unroll
-      for (int i = 0; i < kChunk; ++i) {
-        if (i < n) {
-          const float wi = __shfl(wl, i);
-          o0 += wi * v[i].x;
-          o1 += wi * v[i].y;
+        for (int k = 0; k < kBatch; ++k) {
+          idx[k] = live ? __builtin_ctzll(live) : -1;
+          if (live) {
+            live &= live - 1;
+            ++cnt;
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+          v[k] = idx[k] >= 0 ? *reinterpret_cast<const float2*>(po + (size_t)(c0 + idx[k]) * kHeadDim)
+                             : make_float2(0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          if (k < cnt) {
+            const float wi = __shfl(wl, idx[k]);
+            o0 += wi * v[k].x;
+            o1 += wi * v[k].y;
+          }
         }
       }
     }

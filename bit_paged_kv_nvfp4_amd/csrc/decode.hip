@@ -304,204 +304,367 @@ __device__ __forceinline__ void pair_step(const PageRegs& ra, const PageRegs& rb
   pv_tile<7>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[7]);
 }
 
-__global__ __launch_bounds__(64 * kWaves) void k_decode_split(DecodeArgs a) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform by construction
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  const int lane = threadIdx.x & 63;
+// A value every lane holds the same copy of, moved to scalar registers so that
+// what is derived from it (loads of seq_lens, the page table) is scalar too.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// A load from read-only memory at an index every lane shares, through the
+// scalar path (constant address space): a vector load here would be awaited with
+// a wait that also drains every page copy in flight.
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p, int64_t idx) {
+  using const_i32 = const __attribute__((address_space(4))) int32_t;
+  return ((const_i32*)p)[uniform(idx)];  // address-space cast
+}
+
+// Pages of sequence b (0 for a sequence of length 0); b is the same on every lane.
+__device__ __forceinline__ int seq_pages(const DecodeArgs& a, int b) {
+  return (load_uniform(a.seq_lens, b) + kPage - 1) / kPage;
+}
+// The same for a per-lane b.
+__device__ __forceinline__ int seq_pages_lane(const DecodeArgs& a, int b) { return (a.seq_lens[b] + kPage - 1) / kPage; }
+
+// s_setprio level 3 while more than 3/4 of `quota` pages are left, down to 0
+// for the last quarter.
+__device__ __forceinline__ void set_priority(int left, int quota) {
+  const int level = quota > 0 ? min(3, max(0, (4 * left - 1) / quota)) : 0;
+  switch (level) {
+    case 3: __builtin_amdgcn_s_setprio(3); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
+}
+
+// Pages [pg0, pg1) of sequence b, KV head h, for one wave: online-softmax state
+// (acc, m_ref, lsum; lsum still per lane) of all query heads of the group.
+__device__ __forceinline__ void wave_share(const DecodeArgs& a, int b, int h, int pg0, int pg1, int lane,
+                                           uint8_t* ring, int32_t* ids, f32x4 (&acc)[8], float& m_ref,
+                                           float& lsum, int& left, int quota) {
   const int n = lane & 15;
   const int G = lane >> 4;
+  b = uniform(b);
+  h = uniform(h);
+  pg0 = uniform(pg0);
+  pg1 = uniform(pg1);
+  m_ref = -__builtin_inff();
+  lsum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (pg0 >= pg1) return;
+
+  const int L = load_uniform(a.seq_lens, b);
+  const bool head_ok = n < a.group;
+  const uint8_t* pool_h = a.pool + (int64_t)h * (2 * kSlab);
+  const int64_t page_bytes = (int64_t)a.num_kv_heads * (2 * kSlab);
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+  const uint32_t ids_lds = (uint32_t)(uintptr_t)ids;
+  const DmaOffsets off = dma_offsets(lane);
+  const int n_pages = pg1 - pg0;
+  const int n_pairs = (n_pages + 1) / 2;
+  const int lim = min(L, pg1 * kPage);  // tokens of this share end here
+  const int32_t* pt_split = a.page_table + (int64_t)b * a.pt_stride + pg0;
+
+  // Start-up: the first two id chunks and the group's queries are copied at
+  // once, the first pages go out as soon as the ids have landed, and the queries
+  // are converted while those pages are in flight. The queries are staged in the
+  // ring's last two slots, which the loop's first refill overwrites only after
+  // they have been read.
+  const uint32_t q_lds = ring_lds + (kRing - 2) * kSlotBytes;
+  const uint8_t* qsrc =
+      reinterpret_cast<const uint8_t*>(a.q + ((size_t)b * a.num_q_heads + (size_t)h * a.group) * kHeadDim);
+  const uint32_t qbytes = (uint32_t)a.group * (kHeadDim * 2);  // 256 .. 4096
+  issue_ids(pt_split, 0, n_pages, ids_lds, lane);
+  issue_ids(pt_split, 1, n_pages, ids_lds, lane);
+#pragma unroll
+  for (int k = 0; k < kQDmas; ++k)
+    dma16(qsrc, min((uint32_t)(k * 1024 + 16 * lane), qbytes - 16u), q_lds + k * 1024);
+  wait_dma<kQDmas>();  // the ids have landed
+  int ids_v = ids[lane];  // chunk 0
+  // The ring holds kPairsAhead + 1 pairs: one being computed, the others in
+  // flight. Pages past the share's end re-read its last page (masked by `lim`),
+  // so every iteration issues the same number of copies and the wait count is a
+  // constant.
+#pragma unroll
+  for (int j = 0; j < 2 * kPairsAhead; ++j)
+    issue_page(slab_of(pool_h, ids_v, min(j, n_pages - 1), page_bytes), off, ring_lds + j * kSlotBytes, lane);
+  wait_dma<2 * kPairsAhead * kDmaPerPage>();  // the queries have landed
+
+  // ---- Q: head n of the group, channels 32G..32G+31, as f16 after rescale ----
+  float qv[32];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(ring + (kRing - 2) * kSlotBytes + n * (kHeadDim * 2) + 64 * G);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 u = head_ok ? qp[i] : make_uint4(0, 0, 0, 0);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qv[8 * i + 2 * e] = __uint_as_float(w[e] << 16);
+        qv[8 * i + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      }
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // staging slots read: free for the refill
+  float qmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) qmax = __builtin_fmaxf(qmax, __builtin_fabsf(qv[i]));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, o));
+  int qexp = 0;
+  if (qmax > 0.0f) {
+    int e2;
+    (void)__builtin_frexpf(qmax, &e2);  // qmax = m * 2^e2, m in [0.5, 1)
+    qexp = e2 - 15;                      // qmax * 2^-qexp in [2^14, 2^15)
+  }
+  // A negative softmax scale is carried by the query's sign (exact), so that the
+  // logit multiplier c below is positive.
+  const float qmul = a.qk_scale_log2 < 0.0f ? -__builtin_ldexpf(1.0f, -qexp) : __builtin_ldexpf(1.0f, -qexp);
+  f16x8 qf[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[st][e] = (_Float16)(qv[8 * st + e] * qmul);
+  // z (base-2 logit) = S_acc * c: undoes the Q rescale and the 1/256 of the K scales
+  const float c = __builtin_ldexpf(__builtin_fabsf(a.qk_scale_log2), qexp + 8);
+
+  int cur = 0;  // ring slot of the current pair's first page
+  for (int i = 0; i < n_pairs; ++i) {
+    // Issue priority follows the work this wave has left: the hardware favours
+    // the oldest wave, which would otherwise finish far ahead of waves started
+    // with it while the CU idles at the end.
+    set_priority(left, quota);
+    left -= 2;
+    const int ahead = 2 * (i + kPairsAhead);  // first page of the pair to fetch now
+    if (ahead % kIdChunk == 0 && ahead < n_pages) {
+      // Entering id chunk k = ahead / 64: its buffer has landed long ago; take
+      // its ids into the register and refill the other buffer with chunk k + 1.
+      ids_v = ids[((ahead / kIdChunk) & 1) * kIdChunk + lane];
+      issue_ids(pt_split, ahead / kIdChunk + 1, n_pages, ids_lds, lane);
+    }
+    const int nxt = cur == 0 ? kRing - 2 : cur - 2;  // the slot pair freed last iteration
+    issue_page(slab_of(pool_h, ids_v, min(ahead, n_pages - 1), page_bytes), off, ring_lds + nxt * kSlotBytes, lane);
+    issue_page(slab_of(pool_h, ids_v, min(ahead + 1, n_pages - 1), page_bytes), off,
+               ring_lds + (nxt + 1) * kSlotBytes, lane);
+    wait_dma<2 * kPairsAhead * kDmaPerPage>();  // the current pair's copies have landed
+    const PageRegs ra = read_page(ring + cur * kSlotBytes, lane);
+    const PageRegs rb = read_page(ring + (cur + 1) * kSlotBytes, lane);
+    pair_step(ra, rb, (pg0 + 2 * i) * kPage, lim, G, qf, c, m_ref, lsum, acc);
+    cur = cur + 2 == kRing ? 0 : cur + 2;
+  }
+  wait_dma<0>();  // no copy may outlive the wave's use of its LDS
+}
+
+
+// Inclusive prefix sum over the wave (lane order).
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t t = __shfl_up(v, o);
+    v += lane >= o ? t : 0;
+  }
+  return v;
+}
+
+// Work decomposition. The launch's work is the units (b, h, s): split s < S of
+// sequence b and KV head h covers pages [s P_b, min((s+1) P_b, n_b)), P_b =
+// ceil(n_b / S). In the flattened page space, where (b, h) occupies
+// [Hkv cum_b + h n_b, + n_b) (cum_b = pages of the sequences before b), a unit
+// starts at its segment's start + min(s P_b, n_b). Workgroup g owns the units
+// that start in [g T / W, (g + 1) T / W), T = total pages, W = workgroups (the
+// last one owns everything after its start). Its units form at most a few runs
+// of consecutive splits of one (b, h); a run is processed as one range of pages,
+// its four waves taking a quarter each, and writes one state (in its first
+// split's slot; the run's other splits get empty states).
+struct Cursor {
+  int b;        // current sequence (a.batch = done)
+  int64_t seg;  // flattened start of segment (b, 0)
+  int np;       // pages of sequence b
+};
+
+// Four waves per SIMD (at most 128 VGPRs): the persistent grid assumes four
+// resident workgroups per CU.
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_split(DecodeArgs a) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform by construction
+  const int lane = threadIdx.x & 63;
   const int S = a.num_splits;
+  const int Hkv = a.num_kv_heads;
+  const int g = blockIdx.x;
+  const int W = gridDim.x;
 
   __shared__ int waves_done;
+  __shared__ __attribute__((aligned(16))) uint8_t ring_all[kWaves][kRing * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) int32_t ids_all[kWaves][2 * kIdChunk];
   if (threadIdx.x == 0) waves_done = 0;
   __syncthreads();
 
-  const int L = a.seq_lens[b];
-  const int npages = (L + kPage - 1) / kPage;
-  const int pps = (npages + S - 1) / S;
-  const int split_pg0 = min(split * pps, npages);
-  const int split_pg1 = min(split_pg0 + pps, npages);
-  // this wave's share: an even number of pages, so that only the last pair of the
-  // share can hold masked rows
-  const int share = (((split_pg1 - split_pg0 + kWaves - 1) / kWaves) + 1) & ~1;
-  const int pg0 = min(split_pg0 + wave * share, split_pg1);
-  const int pg1 = min(pg0 + share, split_pg1);
-
-  float m_ref = -__builtin_inff();
-  float lsum = 0.0f;
-  f32x4 acc[8];
+  // ---- total pages and this workgroup's window (every wave computes the same) ----
+  int64_t total = 0;
+  for (int c0 = 0; c0 < a.batch; c0 += 64) {
+    const int bb = c0 + lane;
+    int64_t v = bb < a.batch ? (int64_t)Hkv * seq_pages_lane(a, bb) : 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    total += v;
+  }
+  total = uniform(total);
+  const int64_t lo = total * g / W;
+  const int64_t hi = g == W - 1 ? INT64_MAX : total * (g + 1) / W;
 
-  const bool head_ok = n < a.group;
-  const int qh = h * a.group + n;
-  const int32_t* pt_row = a.page_table + (int64_t)b * a.pt_stride;
-  const uint8_t* pool_h = a.pool + (int64_t)h * (2 * kSlab);
-  const int64_t page_bytes = (int64_t)a.num_kv_heads * (2 * kSlab);
-  __shared__ __attribute__((aligned(16))) uint8_t ring_all[kWaves][kRing * kSlotBytes];
-  uint8_t* const ring = ring_all[wave];
-  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
-  const DmaOffsets off = dma_offsets(lane);
-
-  __shared__ __attribute__((aligned(16))) int32_t ids_all[kWaves][2 * kIdChunk];
-  int32_t* const ids = ids_all[wave];
-  const uint32_t ids_lds = (uint32_t)(uintptr_t)ids;
-  if (pg0 < pg1) {
-    const int n_pages = pg1 - pg0;
-    const int n_pairs = (n_pages + 1) / 2;
-    const int lim = min(L, pg1 * kPage);  // tokens of this split end here
-    const int32_t* pt_split = pt_row + pg0;
-    // Start-up: the first two id chunks and the group's queries are copied at
-    // once, the first pages go out as soon as the ids have landed, and the
-    // queries are converted while those pages are in flight. The queries are
-    // staged in the ring's last two slots, which the loop's first refill
-    // overwrites only after they have been read.
-    issue_ids(pt_split, 0, n_pages, ids_lds, lane);
-    issue_ids(pt_split, 1, n_pages, ids_lds, lane);
-    const uint32_t q_lds = ring_lds + (kRing - 2) * kSlotBytes;
-    {
-      const uint8_t* qsrc =
-          reinterpret_cast<const uint8_t*>(a.q + ((size_t)b * a.num_q_heads + (size_t)h * a.group) * kHeadDim);
-      const uint32_t qbytes = (uint32_t)a.group * (kHeadDim * 2);  // 256 .. 4096
-#pragma unroll
-      for (int k = 0; k < kQDmas; ++k)
-        dma16(qsrc, min((uint32_t)(k * 1024 + 16 * lane), qbytes - 16u), q_lds + k * 1024);
+  // ---- first segment that can hold a unit starting at or after lo: the first b
+  // whose segments end at or after lo ----
+  Cursor cu{a.batch, 0, 0};
+  {
+    int64_t base = 0;
+    for (int c0 = 0; c0 < a.batch; c0 += 64) {
+      const int bb = c0 + lane;
+      const int np = bb < a.batch ? seq_pages_lane(a, bb) : 0;
+      const int64_t incl = wave_incl_scan((int64_t)Hkv * np, lane);  // segments of b <= bb end at base + incl
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(bb < a.batch && base + incl >= lo);
+      if (hit) {
+        const int k = __builtin_ctzll(hit);
+        const int64_t incl_k = uniform((int64_t)__shfl(incl, k));
+        const int np_k = uniform(__shfl(np, k));
+        cu = Cursor{uniform(c0 + k), base + incl_k - (int64_t)Hkv * np_k, np_k};
+        break;
+      }
+      base += uniform((int64_t)__shfl(incl, 63));
     }
-    wait_dma<kQDmas>();  // the ids have landed
-    int ids_v = ids[lane];  // chunk 0
-    // The ring holds kPairsAhead + 1 pairs: one being computed, the others in
-    // flight. Pages past the split's end re-read its last page (masked by `lim`),
-    // so every iteration issues the same number of copies and the wait count is
-    // a constant.
-#pragma unroll
-    for (int j = 0; j < 2 * kPairsAhead; ++j)
-      issue_page(slab_of(pool_h, ids_v, min(j, n_pages - 1), page_bytes), off, ring_lds + j * kSlotBytes, lane);
-    wait_dma<2 * kPairsAhead * kDmaPerPage>();  // the queries have landed
+  }
+  int h = 0;
+  int s = 0;
+  if (cu.b < a.batch && lo > cu.seg) {
+    // First (h, s) of sequence cu.b whose unit starts at or after lo. Here
+    // cu.seg < lo <= cu.seg + Hkv np, so np > 0. With rel = lo - cu.seg in
+    // [1, Hkv np], segment h = (rel - 1) / np holds offset r = rel - h np in
+    // [1, np], and its unit s = ceil(r / P) is the first to start at or after lo
+    // (s = S: none does, the loop moves on; r = np: the segment's empty trailing
+    // splits start exactly at lo).
+    const int P = (cu.np + S - 1) / S;
+    const int64_t rel = lo - cu.seg;
+    h = (int)((rel - 1) / cu.np);
+    const int64_t r = rel - (int64_t)h * cu.np;
+    s = (int)((r + P - 1) / P);
+  }
 
-    // ---- Q: head n of the group, channels 32G..32G+31, as f16 after rescale ----
-    float qv[32];
+  // ---- runs ----
+  // pages this wave is expected to process (a quarter of the window), and left
+  const int quota = (int)min<int64_t>((g == W - 1 ? total - lo : hi - lo) / kWaves + 1, 1 << 30);
+  int left = quota;
+  uint8_t* const ring = ring_all[wave];
+  int32_t* const ids = ids_all[wave];
+  while (cu.b < a.batch) {
+    if (s >= S) {  // (b, h) exhausted: next head, or next sequence
+      s = 0;
+      if (++h >= Hkv) {
+        h = 0;
+        cu.seg += (int64_t)Hkv * cu.np;
+        if (++cu.b >= a.batch) break;
+        cu.np = seq_pages(a, cu.b);
+      }
+      continue;
+    }
+    const int np = cu.np;
+    const int P = (np + S - 1) / S;
+    const int64_t seg = cu.seg + (int64_t)h * np;
+    auto unit_start = [&](int k) -> int64_t { return seg + min((int64_t)k * P, (int64_t)np); };
+    if (unit_start(s) >= hi) break;  // the window ends before this unit
+    // the run: splits s .. s1 of (b, h), all starting before hi
+    int s1 = S - 1;
+    if (unit_start(S - 1) >= hi) {
+      // last split starting before hi (P > 0 here, since the unit at s starts before hi)
+      const int64_t last = (hi - 1 - seg) / P;  // split index of page hi - 1 relative to seg
+      s1 = (int)min<int64_t>(last, S - 1);
+    }
+    const int rp0 = min(s * P, np);
+    const int rp1 = min((s1 + 1) * P, np);
+    // this wave's share: an even number of pages, so that only the last pair of
+    // the share can hold masked rows
+    const int share = (((rp1 - rp0 + kWaves - 1) / kWaves) + 1) & ~1;
+    const int pg0 = min(rp0 + wave * share, rp1);
+    const int pg1 = min(pg0 + share, rp1);
+
+    // The lane index is re-read each run so that the many values derived from it
+    // (copy offsets, LDS addresses) are rebuilt here rather than hoisted and kept
+    // live across the page loop, where registers are scarce.
+    int ln;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+    const int n = ln & 15;
+    const int G = ln >> 4;
+    f32x4 acc[8];
+    float m_ref, lsum;
+    wave_share(a, cu.b, h, pg0, pg1, ln, ring, ids, acc, m_ref, lsum, left, quota);
+
+    // ---- merge the waves' states; the last wave to finish writes the run's ----
+    lsum = xor16_sum(lsum);
+    lsum = xor32_sum(lsum);  // per head n, on every lane of head n
     {
-      const uint4* qp =
-          reinterpret_cast<const uint4*>(ring + (kRing - 2) * kSlotBytes + n * (kHeadDim * 2) + 64 * G);
+      // own state into own ring region (its copies have all landed): acc as
+      // [q][lane] float4s, then (m, l) per head
+      float4* acc_lds = reinterpret_cast<float4*>(ring);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 u = head_ok ? qp[i] : make_uint4(0, 0, 0, 0);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      for (int q = 0; q < 8; ++q) acc_lds[q * 64 + ln] = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+      if (G == 0) reinterpret_cast<float2*>(ring + 8 * 64 * 16)[n] = make_float2(m_ref, lsum);
+    }
+    int prior = 0;
+    if (ln == 0) prior = __hip_atomic_fetch_add(&waves_done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    prior = __builtin_amdgcn_readfirstlane(prior);
+    if (prior == kWaves - 1) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      float mw[kWaves], lw[kWaves];
+      float m_all = -__builtin_inff();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qv[8 * i + 2 * e] = __uint_as_float(w[e] << 16);
-          qv[8 * i + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      for (int w = 0; w < kWaves; ++w) {
+        const float2 ml = reinterpret_cast<const float2*>(&ring_all[w][0] + 8 * 64 * 16)[n];
+        mw[w] = ml.x;
+        lw[w] = ml.y;
+        m_all = __builtin_fmaxf(m_all, ml.x);
+      }
+      float l_all = 0.0f;
+      f32x4 o_all[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o_all[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        // an empty share has m = -inf and weight 0; so does everything when all are
+        const float f = (mw[w] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - m_all);
+        l_all += f * lw[w];
+        const float4* src = reinterpret_cast<const float4*>(&ring_all[w][0]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float4 v = src[q * 64 + ln];
+          o_all[q][0] += f * v.x;
+          o_all[q][1] += f * v.y;
+          o_all[q][2] += f * v.z;
+          o_all[q][3] += f * v.w;
         }
       }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // staging slots read: free for the refill
-    float qmax = 0.0f;
+      if (n < a.group) {
+        const int qh = h * a.group + n;
+        const size_t unit = ((size_t)cu.b * a.num_q_heads + qh) * S + s;
+        float* po = a.part_o + unit * kHeadDim;
+        // o_all[q][r] is O^T[channel 8 (4G + r) + q][head n], in units of 1/256 of
+        // the value scale (the V scales were carried as E4M3/256)
+        const float vs = a.v_scale * 256.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) qmax = __builtin_fmaxf(qmax, __builtin_fabsf(qv[i]));
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, o));
-    int qexp = 0;
-    if (qmax > 0.0f) {
-      int e2;
-      (void)__builtin_frexpf(qmax, &e2);  // qmax = m * 2^e2, m in [0.5, 1)
-      qexp = e2 - 15;                      // qmax * 2^-qexp in [2^14, 2^15)
-    }
-    // A negative softmax scale is carried by the query's sign (exact), so that the
-    // logit multiplier c below is positive.
-    const float qmul = a.qk_scale_log2 < 0.0f ? -__builtin_ldexpf(1.0f, -qexp) : __builtin_ldexpf(1.0f, -qexp);
-    f16x8 qf[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[st][e] = (_Float16)(qv[8 * st + e] * qmul);
-    // z (base-2 logit) = S_acc * c: undoes the Q rescale and the 1/256 of the K scales
-    const float c = __builtin_ldexpf(__builtin_fabsf(a.qk_scale_log2), qexp + 8);
-
-    int cur = 0;  // ring slot of the current pair's first page
-    for (int i = 0; i < n_pairs; ++i) {
-      const int ahead = 2 * (i + kPairsAhead);  // first page of the pair to fetch now
-      if (ahead % kIdChunk == 0 && ahead < n_pages) {
-        // Entering id chunk k = ahead / 64: its buffer has landed long ago; take
-        // its ids into the register and refill the other buffer with chunk k + 1.
-        ids_v = ids[((ahead / kIdChunk) & 1) * kIdChunk + lane];
-        issue_ids(pt_split, ahead / kIdChunk + 1, n_pages, ids_lds, lane);
+        for (int r = 0; r < 4; ++r) {
+          const float4 v0 = make_float4(o_all[0][r] * vs, o_all[1][r] * vs, o_all[2][r] * vs, o_all[3][r] * vs);
+          const float4 v1 = make_float4(o_all[4][r] * vs, o_all[5][r] * vs, o_all[6][r] * vs, o_all[7][r] * vs);
+          *reinterpret_cast<float4*>(po + 32 * G + 8 * r) = v0;
+          *reinterpret_cast<float4*>(po + 32 * G + 8 * r + 4) = v1;
+        }
+        // the run's state, then empty states for its other splits
+        float2* pml = reinterpret_cast<float2*>(a.part_ml) + unit;
+        for (int k = G; k <= s1 - s; k += 4) pml[k] = k == 0 ? make_float2(m_all, l_all) : make_float2(-__builtin_inff(), 0.0f);
       }
-      const int nxt = cur == 0 ? kRing - 2 : cur - 2;  // the slot pair freed last iteration
-      issue_page(slab_of(pool_h, ids_v, min(ahead, n_pages - 1), page_bytes), off, ring_lds + nxt * kSlotBytes,
-                 lane);
-      issue_page(slab_of(pool_h, ids_v, min(ahead + 1, n_pages - 1), page_bytes), off,
-                 ring_lds + (nxt + 1) * kSlotBytes, lane);
-      wait_dma<2 * kPairsAhead * kDmaPerPage>();  // the current pair's copies have landed
-      const PageRegs ra = read_page(ring + cur * kSlotBytes, lane);
-      const PageRegs rb = read_page(ring + (cur + 1) * kSlotBytes, lane);
-      pair_step(ra, rb, (pg0 + 2 * i) * kPage, lim, G, qf, c, m_ref, lsum, acc);
-      cur = cur + 2 == kRing ? 0 : cur + 2;
+      waves_done = 0;  // for the next run; the barrier below orders it
     }
-    wait_dma<0>();  // no copy may outlive the wave's LDS
-  }
-
-  // ---- merge the waves' states; the last wave to finish writes the split's ----
-  lsum = xor16_sum(lsum);
-  lsum = xor32_sum(lsum);  // per head n, on every lane of head n
-  {
-    // own state into own ring region (its copies have all landed): acc as
-    // [q][lane] float4s, then (m, l) per head
-    float4* acc_lds = reinterpret_cast<float4*>(ring);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc_lds[q * 64 + lane] = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
-    if (G == 0) reinterpret_cast<float2*>(ring + 8 * 64 * 16)[n] = make_float2(m_ref, lsum);
-  }
-  int prior = 0;
-  if (lane == 0) prior = __hip_atomic_fetch_add(&waves_done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-  prior = __builtin_amdgcn_readfirstlane(prior);
-  if (prior != kWaves - 1) return;  // not the last wave of the split
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-
-  float mw[kWaves], lw[kWaves];
-  float m_all = -__builtin_inff();
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float2 ml = reinterpret_cast<const float2*>(&ring_all[w][0] + 8 * 64 * 16)[n];
-    mw[w] = ml.x;
-    lw[w] = ml.y;
-    m_all = __builtin_fmaxf(m_all, ml.x);
-  }
-  float l_all = 0.0f;
-  f32x4 o_all[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) o_all[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    // an empty share has m = -inf and weight 0; so does everything when all are
-    const float f = (mw[w] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - m_all);
-    l_all += f * lw[w];
-    const float4* src = reinterpret_cast<const float4*>(&ring_all[w][0]);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float4 v = src[q * 64 + lane];
-      o_all[q][0] += f * v.x;
-      o_all[q][1] += f * v.y;
-      o_all[q][2] += f * v.z;
-      o_all[q][3] += f * v.w;
-    }
-  }
-
-  if (head_ok) {
-    const size_t unit = ((size_t)b * a.num_q_heads + qh) * S + split;
-    float* po = a.part_o + unit * kHeadDim;
-    // o_all[q][r] is O^T[channel 8 (4G + r) + q][head n], in units of 1/256 of the
-    // value scale (the V scales were carried as E4M3/256)
-    const float vs = a.v_scale * 256.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float4 v0 = make_float4(o_all[0][r] * vs, o_all[1][r] * vs, o_all[2][r] * vs, o_all[3][r] * vs);
-      const float4 v1 = make_float4(o_all[4][r] * vs, o_all[5][r] * vs, o_all[6][r] * vs, o_all[7][r] * vs);
-      *reinterpret_cast<float4*>(po + 32 * G + 8 * r) = v0;
-      *reinterpret_cast<float4*>(po + 32 * G + 8 * r + 4) = v1;
-    }
-    if (G == 0) *reinterpret_cast<float2*>(a.part_ml + unit * 2) = make_float2(m_all, l_all);
+    __syncthreads();  // every wave's state has been merged: rings may be reused
+    s = s1 + 1;
   }
 }
 
@@ -509,11 +672,20 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_split(DecodeArgs a) {
 
 int decode_waves_per_split() { return kWaves; }
 
+// Four workgroups of four waves per CU: LDS (under 40 KB per workgroup of the
+// CU's 160 KB) and registers (at most 128 VGPRs, i.e. four waves per SIMD) both
+// allow exactly that. More workgroups than fit would only queue behind the
+// resident ones; the kernel's result does not depend on the count.
+constexpr int kWorkgroupsPerCu = 4;
+constexpr int kLdsPerWorkgroup = kWaves * (kRing * kSlotBytes + 2 * kIdChunk * 4) + 16;
+static_assert(kWorkgroupsPerCu * kLdsPerWorkgroup <= 160 * 1024, "four workgroups must fit a CU's LDS");
+
+int decode_resident_workgroups(int num_cus) { return kWorkgroupsPerCu * (num_cus > 0 ? num_cus : 1); }
+
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_decode_split, dim3(a.num_splits, a.num_kv_heads, a.batch), dim3(64 * kWaves), 0, stream, a);
+  hipLaunchKernelGGL(k_decode_split, dim3(a.num_workgroups), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
-
 
 }  // namespace nvfp4kv

@@ -46,6 +46,7 @@ struct DecodeArgs {
   float qk_scale_log2;     // sm_scale * log2(e) * g
   float v_scale;           // g (the partial states carry V in true units)
   int32_t num_splits;
+  int32_t num_workgroups;  // persistent workgroups of the decode kernel
   float* part_o;           // [B][Hq][S][128]
   float* part_ml;          // [B][Hq][S][2]: running max (log2 units), sum
   void* out;
@@ -71,6 +72,8 @@ struct DequantArgs {
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
 // Waves that share one split of the decode kernel (one workgroup per split).
 int decode_waves_per_split();
+// Workgroups of the decode kernel that fit on the device at once.
+int decode_resident_workgroups(int num_cus);
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);

@@ -132,10 +132,11 @@ int32_t nvfp4_kv_quantize(const void* k_src, const void* v_src, int32_t src_dtyp
                           const nvfp4kv_pool* pool, void* stream);
 
 /*
- * Split count the decode call uses when passed num_splits = 0. Each (sequence,
- * KV head, split) is one workgroup of 4 waves that share the split's pages; the
- * default gives about 44 waves per compute unit (2.75 rounds of the waves a CU
- * keeps resident), at least 4 pages per wave, at most NVFP4KV_MAX_SPLITS.
+ * Split count the decode call uses when passed num_splits = 0. The decode
+ * kernel keeps 4 workgroups of 4 waves resident per compute unit for the whole
+ * launch and gives each a window of about equal page count, cut at split
+ * boundaries; the default makes about 16 splits per window (windows within about
+ * 6% of each other), at least 4 pages per split, at most NVFP4KV_MAX_SPLITS.
  * num_cus <= 0 asks the current
  * HIP device for its compute-unit count (the only HIP call of this function).
  * Returns >= 1.
@@ -188,17 +189,22 @@ int32_t nvfp4_paged_decode_attn(const void* q, const int32_t* page_table, int64_
  * sequence b covers logical pages [s*P, min((s+1)*P, n_b)), P = ceil(n_b / S),
  * n_b = ceil(seq_lens[b] / 16). For every (b, qh, s) it writes an online-softmax
  * state into the workspace:
- *   M[b][qh][s]      reference exponent (base 2) of the split's logits, -inf
- *                    for an empty split; not necessarily their maximum,
- *   Z[b][qh][s]      sum over the split's tokens of 2^(x_t log2(e) - M),
- *   O[b][qh][s][128] sum over the split's tokens of 2^(x_t log2(e) - M) v^_t,
- * with x_t = sm_scale q . k^_t (natural-log logits). Workspace layout: O as f32
- * [B][Hq][S][128] at byte 0, then (M, Z) as f32 pairs [B][Hq][S][2] at byte
- * B*Hq*S*128*4.
+ *   M[b][qh][s]      reference exponent (base 2) of the logits of the tokens the
+ *                    state covers, -inf for an empty state; not necessarily
+ *                    their maximum,
+ *   Z[b][qh][s]      sum over those tokens of 2^(x_t log2(e) - M),
+ *   O[b][qh][s][128] sum over those tokens of 2^(x_t log2(e) - M) v^_t,
+ * with x_t = sm_scale q . k^_t (natural-log logits). State s covers the tokens
+ * of splits s..s' for some s' >= s (consecutive splits one workgroup processed
+ * together); the states of splits s+1..s' are then empty (M = -inf, Z = 0) and
+ * their O is not written. Together the S states cover every token once.
+ * Workspace layout: O as f32 [B][Hq][S][128] at byte 0, then (M, Z) as f32
+ * pairs [B][Hq][S][2] at byte B*Hq*S*128*4.
  *
  * Phase 2, nvfp4_decode_combine: for every (b, qh) merges the S states:
  *   M* = max_s M, Z* = sum_s 2^(M_s - M*) Z_s, out = sum_s 2^(M_s - M*) O_s / Z*,
- *   lse = (M* + log2 Z*) ln 2; all states empty: out = 0, lse = -inf.
+ *   lse = (M* + log2 Z*) ln 2; all states empty: out = 0, lse = -inf. The O of
+ *   an empty state (M = -inf) is never read.
  * Errors: as nvfp4_paged_decode_attn (ERR_SHAPE for num_splits outside
  * 1..4096, ERR_WORKSPACE when the workspace is smaller than the layout above).
  */

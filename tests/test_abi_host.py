@@ -51,9 +51,9 @@ def test_constants_and_strings(L):
 
 
 def test_default_splits_and_workspace_size(L):
-    # 44 x 8 (sequence, KV head) pairs on 256 CUs: 32 waves each, i.e. 8 splits of
-    # 4 waves (one workgroup per split)
-    assert L.nvfp4_paged_decode_attn_default_splits(44, 8, 32768, 256) == 8
+    # 256 CUs hold 1024 persistent workgroups; about 16 splits per workgroup window
+    # over 44 x 8 (sequence, KV head) segments: ceil(16 * 1024 / 352) = 47
+    assert L.nvfp4_paged_decode_attn_default_splits(44, 8, 32768, 256) == 47
     assert L.nvfp4_paged_decode_attn_default_splits(1, 1, 16, 256) == 1
     assert L.nvfp4_paged_decode_attn_default_splits(2, 8, 1048576, 256) <= 4096
     s = L.nvfp4_paged_decode_attn_default_splits(15, 8, 163840, 256)

@@ -243,3 +243,93 @@ def test_extreme_magnitudes(kscale, qscale):
     ref, ref_lse = _oracle_attn(w, opool, q)
     assert_close(out.cpu().numpy(), ref, atol=2e-3 * kscale, what=f"k x{kscale} q x{qscale}")
     assert_close(lse.cpu().numpy(), ref_lse, atol=1e-3, rtol=1e-4, what="lse")
+
+
+def test_partial_states_cover_every_token_once_and_match_oracle():
+    """Phase 1 on its own: each non-empty state s covers the tokens of splits
+    s .. t-1 (t = the next non-empty state, or S), as the C header documents, and
+    matches the oracle over exactly those tokens; empty states are (-inf, 0); the
+    states together give the full call's output. 4 x 8 (sequence, KV head) x 64
+    splits are more units than resident workgroups, so runs of several splits
+    (merged into one state) occur."""
+    lens = [2048, 1500, 2048, 700]
+    S = 64
+    w = W.small_workload(321, len(lens), 64, 8, lens, name="partial_states")
+    kv = _kv(w)
+    gpool = gpu_pool_from_kv(w, kv)
+    opool = oracle_pool_from_kv(w, kv)
+    q = W.query(w)
+    pt = torch.as_tensor(w.page_table, device="cuda").contiguous()
+    sl = torch.as_tensor(w.seq_lens, device="cuda")
+    Bn, Hq = w.batch, w.num_q_heads
+    ws = torch.empty(B.nvfp4_paged_decode_attn_workspace_bytes(Bn, Hq, S), dtype=torch.uint8, device="cuda")
+    B.nvfp4_paged_decode_attn_partial(q.cuda(), pt, sl, gpool, w.sm_scale, w.max_seq_len, S, ws)
+    torch.cuda.synchronize()
+    wsf = ws.view(torch.float32).cpu().numpy()
+    n_o = Bn * Hq * S * 128
+    O = wsf[:n_o].reshape(Bn, Hq, S, 128).astype(np.float64)
+    ML = wsf[n_o:n_o + Bn * Hq * S * 2].reshape(Bn, Hq, S, 2).astype(np.float64)
+    M, Z = ML[..., 0], ML[..., 1]
+    empty = np.isneginf(M)
+    assert np.all(Z[empty] == 0) and np.all(Z[~empty] > 0) and np.all(np.isfinite(M[~empty]))
+    # every query head of a KV group shares the decomposition
+    grp = Hq // w.num_kv_heads
+    for h in range(w.num_kv_heads):
+        assert np.array_equal(empty[:, h * grp:(h + 1) * grp], np.repeat(empty[:, h * grp:h * grp + 1], grp, axis=1))
+    merged = 0
+    rows, seq_lens, owners = [], [], []
+    for b, L in enumerate(lens):
+        n_b = -(-L // 16)
+        P = -(-n_b // S)
+        for h in range(w.num_kv_heads):
+            live = [s for s in range(S) if not empty[b, h * grp, s]]
+            for i, s in enumerate(live):
+                t = live[i + 1] if i + 1 < len(live) else S
+                merged += t - s > 1 and min(t * P, n_b) > min((s + 1) * P, n_b)
+                p0, p1 = min(s * P, n_b), min(t * P, n_b)
+                assert p1 > p0, (b, h, s, t)
+                row = np.full(w.page_table.shape[1], -1, dtype=np.int32)
+                row[:p1 - p0] = w.page_table[b, p0:p1]
+                rows.append(row)
+                seq_lens.append(min(L, p1 * 16) - p0 * 16)
+                owners.append((b, h, s))
+            # the live states' ranges tile the sequence: pages before the first
+            # live state belong to no state only if they do not exist
+            assert not live or min(live[0] * P, n_b) == 0
+    assert merged > 0, "no state covered several splits"
+    # oracle over each state's tokens: one virtual sequence per (b, h, state)
+    vpt = np.stack(rows)
+    vlen = np.asarray(seq_lens, dtype=np.int32)
+    qv = torch.stack([q[b, h * grp:(h + 1) * grp] for b, h, _ in owners])  # [V, grp, 128]
+    ref, ref_lse = _oracle_per_head(w, opool, qv, vpt, vlen, owners)
+    for i, (b, h, s) in enumerate(owners):
+        heads = slice(h * grp, (h + 1) * grp)
+        got = O[b, heads, s] / Z[b, heads, s][:, None]
+        assert_close(got, ref[i], what=f"state b={b} h={h} s={s}")
+        lse_state = (M[b, heads, s] + np.log2(Z[b, heads, s])) * math.log(2.0)
+        assert_close(lse_state, ref_lse[i], atol=1e-3, rtol=1e-4, what=f"state lse b={b} h={h} s={s}")
+    # the combine of these states is the full call's output
+    out = torch.empty((Bn, Hq, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((Bn, Hq), dtype=torch.float32, device="cuda")
+    B.nvfp4_decode_combine(ws, Bn, Hq, S, out, lse=lse)
+    full_out, full_lse = run_decode(w, gpool, q, num_splits=S)
+    torch.cuda.synchronize()
+    assert torch.equal(out, full_out) and torch.equal(lse, full_lse)
+
+
+def _oracle_per_head(w, opool, qv, vpt, vlen, owners):
+    """Oracle attention of each virtual sequence for the query heads of its own KV
+    head: run with the workload's KV-head count, the group's queries placed at
+    their head and zeros elsewhere, then keep the owner head's rows."""
+    grp = w.num_q_heads // w.num_kv_heads
+    V = len(owners)
+    qfull = torch.zeros((V, w.num_q_heads, 128), dtype=torch.bfloat16)
+    units = []
+    for i, (_, h, _) in enumerate(owners):
+        qfull[i, h * grp:(h + 1) * grp] = qv[i]
+        units += [i * w.num_q_heads + h * grp + g for g in range(grp)]
+    out, lse = oracle.decode_attn(bf16_bits(qfull), vpt, vlen, opool, w.num_kv_heads, w.sm_scale, units=units,
+                                  n_threads=8)
+    ref = np.stack([out[i, h * grp:(h + 1) * grp] for i, (_, h, _) in enumerate(owners)])
+    ref_lse = np.stack([lse[i, h * grp:(h + 1) * grp] for i, (_, h, _) in enumerate(owners)])
+    return ref, ref_lse

@@ -49,15 +49,34 @@ def test_copies_use_sgpr_base(decode_asm):
         assert re.search(r",\s*s\[\d+:\d+\]", operands), operands
 
 
+def _loops(body):
+    """(header label, loop text) of every loop, the text running from the header
+    to the branch back to it."""
+    out = []
+    # the "Loop Header" note sits on the label's line or on the comment line after it
+    for head in re.findall(r"(\.LBB\d+_\d+):[^\n]*(?:\n\s*;[^\n]*)?Loop Header", body):
+        text = body[body.index(head + ":"):]
+        back = re.search(rf"s_c?branch\w*\s+{re.escape(head)}\b", text)
+        out.append((head, text[:back.end()] if back else text))
+    return out
+
+
 def test_page_loop_never_drains_copies(decode_asm):
     body = _function(decode_asm, "k_decode_split")
-    loops = re.findall(r"(\.LBB\d+_\d+):[^\n]*Loop Header", body)
-    assert loops, "page loop not found"
-    head = loops[0]
-    loop = body[body.index(head + ":"):]
-    loop = loop[:loop.index(f"s_branch {head}") if f"s_branch {head}" in loop else len(loop)]
+    # the page loop: the innermost loop that issues copies and runs the MFMAs
+    page_loops = [t for _, t in _loops(body) if "v_mfma" in t and "global_load_lds" in t]
+    assert page_loops, "page loop not found"
+    loop = min(page_loops, key=len)
     waits = re.findall(r"s_waitcnt vmcnt\((\d+)\)", loop)
     assert waits and all(int(w) > 0 for w in waits), waits
+
+
+def test_four_waves_per_simd(decode_asm):
+    # the persistent grid launches four workgroups of four waves per CU
+    body_start = re.search(r"^_Z\S*k_decode_split\S*:", decode_asm, flags=re.M).start()
+    meta = decode_asm[body_start:]
+    vgprs = int(re.search(r"; NumVgprs:\s*(\d+)", meta).group(1))
+    assert vgprs <= 128, vgprs
 
 
 def test_no_packed_fp32_and_no_scratch(decode_asm):
