@@ -49,26 +49,48 @@ def test_copies_use_sgpr_base(decode_asm):
         assert re.search(r",\s*s\[\d+:\d+\]", operands), operands
 
 
-def _loops(body):
-    """(header label, loop text) of every loop, the text running from the header
-    to the branch back to it."""
+def _blocks(body):
+    """Basic blocks as (label, annotation, text); the annotation is the comment
+    lines the compiler puts on and after the label (loop membership)."""
     out = []
-    # the "Loop Header" note sits on the label's line or on the comment line after it
-    for head in re.findall(r"(\.LBB\d+_\d+):[^\n]*(?:\n\s*;[^\n]*)?Loop Header", body):
-        text = body[body.index(head + ":"):]
-        back = re.search(rf"s_c?branch\w*\s+{re.escape(head)}\b", text)
-        out.append((head, text[:back.end()] if back else text))
+    parts = re.split(r"^(\.LBB\d+_\d+):", body, flags=re.M)
+    for label, rest in zip(parts[1::2], parts[2::2]):
+        lines = rest.split("\n")
+        note = [lines[0]]
+        k = 1
+        while k < len(lines) and lines[k].strip().startswith(";"):
+            note.append(lines[k])
+            k += 1
+        out.append((label, "\n".join(note), "\n".join(lines[k:])))
     return out
+
+
+def _innermost_loops(body):
+    """{header: text of the loop's blocks} for loops no other loop nests in; a
+    block belongs to loop X when its annotation says "in Loop: Header=X" or it is
+    X's header."""
+    blocks = _blocks(body)
+    headers = {lab for lab, note, _ in blocks if "Loop Header" in note}
+    parents = set(re.findall(r"Parent Loop (BB\d+_\d+)", "\n".join(n for _, n, _ in blocks)))
+    # labels read ".LBB0_7"; annotations name the same block "BB0_7"
+    inner = {h for h in headers if h[2:] not in parents}
+    loops = {}
+    for lab, note, text in blocks:
+        m = re.search(r"in Loop: Header=(BB\d+_\d+)", note)
+        owner = lab if lab in inner else (".L" + m.group(1) if m else None)
+        if owner in inner:
+            loops[owner] = loops.get(owner, "") + text
+    return loops
 
 
 def test_page_loop_never_drains_copies(decode_asm):
     body = _function(decode_asm, "k_decode_split")
-    # the page loop: the innermost loop that issues copies and runs the MFMAs
-    page_loops = [t for _, t in _loops(body) if "v_mfma" in t and "global_load_lds" in t]
+    # the page loops: innermost loops that issue copies and run the MFMAs
+    page_loops = [t for t in _innermost_loops(body).values() if "v_mfma" in t and "global_load_lds" in t]
     assert page_loops, "page loop not found"
-    loop = min(page_loops, key=len)
-    waits = re.findall(r"s_waitcnt vmcnt\((\d+)\)", loop)
-    assert waits and all(int(w) > 0 for w in waits), waits
+    for loop in page_loops:
+        waits = re.findall(r"s_waitcnt vmcnt\((\d+)\)", loop)
+        assert waits and all(int(w) > 0 for w in waits), waits
 
 
 def test_four_waves_per_simd(decode_asm):
