@@ -54,18 +54,9 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, float D, bool zero_scale)
   return sign | c;
 }
 
-__global__ __launch_bounds__(256) void k_quantize(QuantizeArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_token = (int64_t)a.num_kv_heads * 16;
-  if (idx >= a.num_tokens * per_token) return;
-  const int64_t t = idx / per_token;
-  const int rem = (int)(idx - t * per_token);
-  const int h = rem >> 4;
-  const int kind = (rem >> 3) & 1;
-  const int j = rem & 7;
-  const int32_t slot = a.slots[t];
-  if (slot < 0) return;
-
+// Codes and scale byte of block j (16 values) of token t, head h, kind (0 K, 1 V).
+__device__ __forceinline__ void encode_block(const QuantizeArgs& a, int64_t t, int h, int kind, int j,
+                                             uint32_t (&code)[16], int& s) {
   const int64_t off = t * a.token_stride + (int64_t)h * a.head_stride + j * 16;
   float x[16];
   if (a.bf16) {
@@ -91,17 +82,68 @@ __global__ __launch_bounds__(256) void k_quantize(QuantizeArgs a) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
-
-  const int s = scale_byte(amax, 6.0f * a.g);
+  s = scale_byte(amax, 6.0f * a.g);
   const float D = e4m3_value(s) * a.g;
   const bool zs = (s == 0);
-  uint32_t code[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) code[i] = e2m1_code(x[i], D, zs);
+}
 
+__global__ __launch_bounds__(256) void k_quantize(QuantizeArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_token = (int64_t)a.num_kv_heads * 16;
+  if (idx >= a.num_tokens * per_token) return;
+  const int64_t t = idx / per_token;
+  const int rem = (int)(idx - t * per_token);
+  const int h = rem >> 4;
+  const int kind = (rem >> 3) & 1;
+  const int j = rem & 7;
+  const int32_t slot = a.slots[t];
+  if (slot < 0) return;
   const int64_t page = slot >> 4;
   const int row = slot & 15;
   uint8_t* slab = a.pool + ((page * a.num_kv_heads + h) * 2 + kind) * (int64_t)kSlab;
+
+  if (kind == 1) {
+    // V: a code byte holds rows r and r ^ 2 and a 32-bit word rows 4g .. 4g+3 of
+    // one page. When this call writes those four rows as four consecutive tokens,
+    // the thread of the first one encodes all four and writes whole words.
+    const int r4 = row & 3;
+    const int64_t tl = t - r4;
+    bool full = tl >= 0 && tl + 3 < a.num_tokens;
+    const int32_t s0 = full ? a.slots[tl] : -1;
+    full = full && s0 >= 0 && (s0 & 3) == 0;
+#pragma unroll
+    for (int i = 1; i < 4; ++i) full = full && a.slots[tl + i] == s0 + i;
+    if (full) {
+      if (r4 != 0) return;  // written by the group's first token
+      uint32_t c4[4][16];
+      int s4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) encode_block(a, t + i, h, 1, j, c4[i], s4[i]);
+      // chunk (row/4)*16 + 2j + c holds channels 16j + 8c .. +7; its word wi holds
+      // channel q = 8c + 2wi (bytes 0, 1) and q + 1 (bytes 2, 3), rows 0|2 in the
+      // even byte and rows 1|3 in the odd one
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        uint32_t w[4];
+#pragma unroll
+        for (int wi = 0; wi < 4; ++wi) {
+          const int q = 8 * c + 2 * wi;
+          w[wi] = (c4[0][q] | (c4[2][q] << 4)) | ((c4[1][q] | (c4[3][q] << 4)) << 8) |
+                  ((c4[0][q + 1] | (c4[2][q + 1] << 4)) << 16) | ((c4[1][q + 1] | (c4[3][q + 1] << 4)) << 24);
+        }
+        *reinterpret_cast<uint4*>(slab + ((row >> 2) * 16 + 2 * j + c) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      *reinterpret_cast<uint32_t*>(slab + kCodeBytes + j * 16 + row) =
+          (uint32_t)s4[0] | ((uint32_t)s4[1] << 8) | ((uint32_t)s4[2] << 16) | ((uint32_t)s4[3] << 24);
+      return;
+    }
+  }
+
+  uint32_t code[16];
+  int s;
+  encode_block(a, t, h, kind, j, code, s);
   if (kind == 0) {
     // K: the token's 8 code bytes of block j are contiguous, channel 2i in the low
     // nibble of byte i
@@ -115,11 +157,12 @@ __global__ __launch_bounds__(256) void k_quantize(QuantizeArgs a) {
     *reinterpret_cast<uint2*>(slab + row * 64 + j * 8) = make_uint2(w[0], w[1]);
     slab[kCodeBytes + row * 8 + j] = (uint8_t)s;
   } else {
-    // V: channel 16j + e sits in 16-byte chunk (row/4)*16 + 2j + e/8, byte
-    // 2*(e%8) + row%2, high nibble for rows with row%4 >= 2; the other nibble of
-    // each byte is row r ^ 2 of the same page, which another thread (or another
-    // call) may be writing, so the block's nibbles are cleared and set with 32-bit
-    // atomics that leave every other bit alone.
+    // V, a token alone in its four-row group: channel 16j + e sits in 16-byte
+    // chunk (row/4)*16 + 2j + e/8, byte 2*(e%8) + row%2, high nibble for rows with
+    // row%4 >= 2; the other nibble of each byte is row r ^ 2 of the same page,
+    // which another thread (or another call) may be writing, so the block's
+    // nibbles are cleared and set with 32-bit atomics that leave every other bit
+    // alone.
     const int sh = 8 * (row & 1) + 4 * ((row >> 1) & 1);
     const uint32_t mask = (0xFu << sh) | (0xFu << (sh + 16));
 #pragma unroll

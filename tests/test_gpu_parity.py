@@ -333,3 +333,53 @@ def _oracle_per_head(w, opool, qv, vpt, vlen, owners):
     ref = np.stack([out[i, h * grp:(h + 1) * grp] for i, (_, h, _) in enumerate(owners)])
     ref_lse = np.stack([lse[i, h * grp:(h + 1) * grp] for i, (_, h, _) in enumerate(owners)])
     return ref, ref_lse
+
+
+def test_quantize_write_orders_give_the_oracle_bytes():
+    """A V code byte holds two rows of a page: whole four-row groups written by one
+    call take the grouped path, single tokens and broken groups the per-nibble
+    atomic path. Any mix of them, in any order, over stale bytes, must leave the
+    oracle's bytes (the oracle writes everything in one call)."""
+    lens = [70, 45, 16]
+    w = W.small_workload(500, len(lens), 8, 2, lens, name="write_orders")
+    kv = _kv(w)
+    opool = oracle_pool_from_kv(w, kv)
+    rng = np.random.default_rng(7)
+    gpool = B.Pool(w.num_pages, w.num_kv_heads, device="cuda",
+                   data=torch.full((opool.size,), 0xA5, dtype=torch.uint8, device="cuda"))
+    for b, (k, v) in enumerate(kv):
+        L = k.shape[0]
+        slots = W.slots(w, b, 0, L)
+        t = 0
+        calls = []
+        while t < L:  # cut the sequence into runs of 1..9 tokens
+            n = int(rng.integers(1, 10))
+            calls.append(np.arange(t, min(L, t + n)))
+            t += n
+        rng.shuffle(calls)
+        for idx in calls:
+            if rng.random() < 0.3:
+                idx = idx[::-1].copy()  # reversed: groups are not consecutive in the call
+            ti = torch.as_tensor(idx)
+            kk = k[ti].cuda().contiguous()
+            vv = v[ti].cuda().contiguous()
+            B.nvfp4_kv_quantize(kk, vv, torch.as_tensor(slots[idx], device="cuda"), gpool)
+    # one call with a skipped token (slot -1) in the middle of a group
+    k0, v0 = kv[2]
+    sl = W.slots(w, 2, 0, 16).copy()
+    sl[5] = -1
+    B.nvfp4_kv_quantize(k0.cuda().contiguous(), v0.cuda().contiguous(), torch.as_tensor(sl, device="cuda"), gpool)
+    B.nvfp4_kv_quantize(k0[5:6].cuda().contiguous(), v0[5:6].cuda().contiguous(),
+                        torch.as_tensor(W.slots(w, 2, 5, 6), device="cuda"), gpool)
+    torch.cuda.synchronize()
+    g = gpool.data.cpu().numpy()
+    # compare the bytes every written token owns: whole slabs of fully written
+    # pages, and for partly written pages the dequantized tokens
+    ko, vo = oracle.dequant_workspace(g, w.num_kv_heads, w.page_table, w.seq_lens)
+    kr, vr = oracle.dequant_workspace(opool, w.num_kv_heads, w.page_table, w.seq_lens)
+    assert np.array_equal(ko, kr) and np.array_equal(vo, vr)
+    full_pages = [int(p) for b, L in enumerate(lens) for p in w.page_table[b, :L // 16]]
+    for p in full_pages:
+        o = oracle.slab_offset(p, 0, 0, w.num_kv_heads)
+        span = w.num_kv_heads * 2 * 1152
+        assert np.array_equal(g[o:o + span], opool[o:o + span]), f"page {p}"
