@@ -16,19 +16,20 @@
 namespace nvfp4kv {
 namespace {
 
-__device__ __forceinline__ void store2(void* base, size_t idx, float x, float y, bool bf16) {
+// Eight consecutive values of one output row, as one 16-byte store (bf16) or two
+// (f32).
+__device__ __forceinline__ void store8(void* base, size_t idx, const float (&v)[8], bool bf16) {
   if (bf16) {
-    const uint32_t p = (uint32_t)f32_to_bf16_bits(x) | ((uint32_t)f32_to_bf16_bits(y) << 16);
-    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(base) + idx) = p;
+    uint32_t p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      p[i] = (uint32_t)f32_to_bf16_bits(v[2 * i]) | ((uint32_t)f32_to_bf16_bits(v[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx) = make_uint4(p[0], p[1], p[2], p[3]);
   } else {
-    *reinterpret_cast<float2*>(static_cast<float*>(base) + idx) = make_float2(x, y);
+    float4* o = reinterpret_cast<float4*>(static_cast<float*>(base) + idx);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
   }
-}
-
-template <int SEL>
-__device__ __forceinline__ f32x2 dq2(uint32_t w, float scale) {
-  f32x2 v = fp4x2_to_f32x2<SEL>(w);
-  return v * scale;
 }
 
 __global__ __launch_bounds__(64) void k_dequant(DequantArgs a) {
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(64) void k_dequant(DequantArgs a) {
   const int H = a.num_kv_heads;
   const bool bf16 = a.out_bf16 != 0;
 
-  // ---- K: token n, channels 32G..32G+31 ----
+  // ---- K: token n, channels 32G..32G+31 (four runs of 8) ----
   if (pg * kPage + n < L) {
     const uint4 kc = *reinterpret_cast<const uint4*>(kslab + n * 64 + G * 16);
     const uint32_t ks = *reinterpret_cast<const uint16_t*>(kslab + kCodeBytes + n * 8 + G * 2);
@@ -58,11 +59,10 @@ __global__ __launch_bounds__(64) void k_dequant(DequantArgs a) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float sc = w < 2 ? sc0 : sc1;
-      const f32x2 v0 = dq2<0>(kw[w], sc), v1 = dq2<1>(kw[w], sc), v2 = dq2<2>(kw[w], sc), v3 = dq2<3>(kw[w], sc);
-      store2(a.k_out, base + 8 * w + 0, v0[0], v0[1], bf16);
-      store2(a.k_out, base + 8 * w + 2, v1[0], v1[1], bf16);
-      store2(a.k_out, base + 8 * w + 4, v2[0], v2[1], bf16);
-      store2(a.k_out, base + 8 * w + 6, v3[0], v3[1], bf16);
+      const f32x2 v0 = fp4x2_to_f32x2<0>(kw[w]), v1 = fp4x2_to_f32x2<1>(kw[w]);
+      const f32x2 v2 = fp4x2_to_f32x2<2>(kw[w]), v3 = fp4x2_to_f32x2<3>(kw[w]);
+      const float v[8] = {v0[0] * sc, v0[1] * sc, v1[0] * sc, v1[1] * sc, v2[0] * sc, v2[1] * sc, v3[0] * sc, v3[1] * sc};
+      store8(a.k_out, base + 8 * w, v, bf16);
     }
   }
 
@@ -92,9 +92,10 @@ __global__ __launch_bounds__(64) void k_dequant(DequantArgs a) {
       const int tok = 4 * G + i;
       if (pg * kPage + tok >= L) continue;
       const float sc = e4m3_to_f32((vs >> (8 * i)) & 0xFFu) * a.g;
-      const size_t base = ((size_t)(row0 + tok) * H + h) * kHeadDim + 8 * n;
+      float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) store2(a.v_out, base + e, val[i][e] * sc, val[i][e + 1] * sc, bf16);
+      for (int e = 0; e < 8; ++e) v[e] = val[i][e] * sc;
+      store8(a.v_out, ((size_t)(row0 + tok) * H + h) * kHeadDim + 8 * n, v, bf16);
     }
   }
 }
