@@ -679,6 +679,7 @@ int decode_waves_per_split() { return kWaves; }
 constexpr int kWorkgroupsPerCu = 4;
 constexpr int kLdsPerWorkgroup = kWaves * (kRing * kSlotBytes + 2 * kIdChunk * 4) + 16;
 static_assert(kWorkgroupsPerCu * kLdsPerWorkgroup <= 160 * 1024, "four workgroups must fit a CU's LDS");
+static_assert(kLdsPerWorkgroup <= 64 * 1024, "a workgroup addresses at most 64 KB of LDS");
 
 int decode_resident_workgroups(int num_cus) { return kWorkgroupsPerCu * (num_cus > 0 ? num_cus : 1); }
 
