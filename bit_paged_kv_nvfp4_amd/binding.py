@@ -20,6 +20,7 @@ PAGE_SIZE = 16
 SLAB_BYTES = 1152
 F32 = 0
 BF16 = 1
+FP8_E4M3 = 2  # extend workspace only
 
 EXPORTED = [
     "nvfp4kv_pool_bytes",
@@ -209,14 +210,14 @@ def nvfp4_kv_dequant_workspace(pool: Pool, page_table: torch.Tensor, seq_lens: t
                                row_offsets: torch.Tensor, max_seq_len: int, k_out: torch.Tensor,
                                v_out: torch.Tensor, stream=None):
     """Writes K^, V^ rows [row_offsets[s] + t] of k_out / v_out ([rows, Hkv, 128],
-    bf16 or float32) for t < seq_lens[s]."""
+    float32, bfloat16 or float8_e4m3fn) for t < seq_lens[s]."""
     if row_offsets.dtype != torch.int64:
         raise ValueError("row_offsets must be int64")
     if k_out.dtype != v_out.dtype or not k_out.is_contiguous() or not v_out.is_contiguous():
         raise ValueError("k_out and v_out must be contiguous and share a dtype")
-    odt = {torch.float32: F32, torch.bfloat16: BF16}.get(k_out.dtype)
+    odt = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}.get(k_out.dtype)
     if odt is None:
-        raise ValueError("workspace dtype must be float32 or bfloat16")
+        raise ValueError("workspace dtype must be float32, bfloat16 or float8_e4m3fn")
     d = pool.desc()
     _check("nvfp4_kv_dequant_workspace",
            lib().nvfp4_kv_dequant_workspace(ctypes.byref(d), _ptr(page_table), page_table.shape[1], _ptr(seq_lens),

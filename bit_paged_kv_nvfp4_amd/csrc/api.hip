@@ -262,7 +262,8 @@ int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page
                                    const int32_t* seq_lens, const int64_t* row_offsets, int32_t n_seqs,
                                    int32_t max_seq_len, void* k_out, void* v_out, int32_t out_dtype, void* stream) {
   if (int32_t e = check_pool(pool)) return e;
-  if (out_dtype != NVFP4KV_F32 && out_dtype != NVFP4KV_BF16) return NVFP4KV_ERR_DTYPE;
+  if (out_dtype != NVFP4KV_F32 && out_dtype != NVFP4KV_BF16 && out_dtype != NVFP4KV_FP8_E4M3)
+    return NVFP4KV_ERR_DTYPE;
   if (n_seqs < 0 || max_seq_len < 0 || page_table_stride < 1) return NVFP4KV_ERR_SHAPE;
   if ((int64_t)max_seq_len > page_table_stride * NVFP4KV_PAGE_SIZE) return NVFP4KV_ERR_SHAPE;
   if (n_seqs > 65535 || pool->num_kv_heads > 65535) return NVFP4KV_ERR_SHAPE;
@@ -283,7 +284,7 @@ int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page
   a.max_seq_len = max_seq_len;
   a.k_out = k_out;
   a.v_out = v_out;
-  a.out_bf16 = out_dtype == NVFP4KV_BF16;
+  a.out_dtype = out_dtype;
   return hip_status(nvfp4kv::launch_dequant(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -9,17 +9,51 @@
 // 32G..32G+31 of token t (16 code bytes) and their two scale bytes; V: lane
 // (n, G) reads its 16-byte chunk (channels 8n..8n+7 of tokens 4G..4G+3) and the
 // four scale bytes of block n/2 for those tokens. Values E2M1(c) * E4M3(s) * g
-// are exact in fp32 and in bf16 (at most 6 significant bits), so the workspace
-// is bit-exact.
+// are exact in fp32 and in bf16 (at most 6 significant bits); an FP8 E4M3
+// workspace (the pages' choice) rounds each of them once, from its exact value.
+#include "nvfp4kv.h"
 #include "nvfp4kv_device.h"
 
 namespace nvfp4kv {
 namespace {
 
-// Eight consecutive values of one output row, as one 16-byte store (bf16) or two
-// (f32).
-__device__ __forceinline__ void store8(void* base, size_t idx, const float (&v)[8], bool bf16) {
-  if (bf16) {
+// E4M3 ("fn") code of x: nearest value, ties to the even code, magnitudes above
+// 448 saturate to 448, sign kept (also of zero). x must be finite. Written out
+// from the format: normal codes 8..126 hold (1 + m/8) 2^(e-7), codes 0..7 hold
+// m 2^-9; rounding the binary32 significand to 3 bits with a carry into the
+// exponent covers every normal case, and below 2^-6 the value is rounded to a
+// multiple of 2^-9 (which reaches code 8 = 2^-6 exactly when it rounds up).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __builtin_fabsf(x);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7Eu;
+  } else if (a < 0x1p-6f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);  // exact product, nearest-even integer 0..8
+  } else {
+    const uint32_t bits = u & 0x7FFFFFFFu;
+    const uint32_t e = (bits >> 23) - 127u + 7u;  // 1..15 here
+    const uint32_t m = bits & 0x7FFFFFu;
+    const uint32_t r = m >> 20, rem = m & 0xFFFFFu;
+    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ? 1u : 0u;
+    code = (e << 3) + r + up;  // a carry out of the mantissa moves to the next exponent
+  }
+  return sign | code;
+}
+
+// Eight consecutive values of one output row, as one 16-byte store (bf16), two
+// (f32) or one 8-byte store (FP8 E4M3).
+__device__ __forceinline__ void store8(void* base, size_t idx, const float (&v)[8], int dtype) {
+  if (dtype == NVFP4KV_FP8_E4M3) {
+    uint32_t p[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      p[i] = f32_to_e4m3(v[4 * i]) | (f32_to_e4m3(v[4 * i + 1]) << 8) | (f32_to_e4m3(v[4 * i + 2]) << 16) |
+             (f32_to_e4m3(v[4 * i + 3]) << 24);
+    *reinterpret_cast<uint2*>(static_cast<uint8_t*>(base) + idx) = make_uint2(p[0], p[1]);
+  } else if (dtype == NVFP4KV_BF16) {
     uint32_t p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -46,7 +80,7 @@ __global__ __launch_bounds__(64) void k_dequant(DequantArgs a) {
   const uint8_t* vslab = kslab + kSlab;
   const int64_t row0 = a.row_offsets[s] + (int64_t)pg * kPage;
   const int H = a.num_kv_heads;
-  const bool bf16 = a.out_bf16 != 0;
+  const int dt = a.out_dtype;
 
   // ---- K: token n, channels 32G..32G+31 (four runs of 8) ----
   if (pg * kPage + n < L) {
@@ -62,7 +96,7 @@ __global__ __launch_bounds__(64) void k_dequant(DequantArgs a) {
       const f32x2 v0 = fp4x2_to_f32x2<0>(kw[w]), v1 = fp4x2_to_f32x2<1>(kw[w]);
       const f32x2 v2 = fp4x2_to_f32x2<2>(kw[w]), v3 = fp4x2_to_f32x2<3>(kw[w]);
       const float v[8] = {v0[0] * sc, v0[1] * sc, v1[0] * sc, v1[1] * sc, v2[0] * sc, v2[1] * sc, v3[0] * sc, v3[1] * sc};
-      store8(a.k_out, base + 8 * w, v, bf16);
+      store8(a.k_out, base + 8 * w, v, dt);
     }
   }
 
@@ -95,7 +129,7 @@ __global__ __launch_bounds__(64) void k_dequant(DequantArgs a) {
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = val[i][e] * sc;
-      store8(a.v_out, ((size_t)(row0 + tok) * H + h) * kHeadDim + 8 * n, v, bf16);
+      store8(a.v_out, ((size_t)(row0 + tok) * H + h) * kHeadDim + 8 * n, v, dt);
     }
   }
 }

@@ -66,7 +66,7 @@ struct DequantArgs {
   int32_t max_seq_len;
   void* k_out;
   void* v_out;
-  int32_t out_bf16;
+  int32_t out_dtype;  // NVFP4KV_F32, NVFP4KV_BF16 or NVFP4KV_FP8_E4M3
 };
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);

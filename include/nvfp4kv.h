@@ -90,7 +90,10 @@ enum nvfp4kv_status {
   NVFP4KV_ERR_HIP = 7        /* a HIP runtime call failed */
 };
 
-enum nvfp4kv_dtype { NVFP4KV_F32 = 0, NVFP4KV_BF16 = 1 };
+/* Element types. NVFP4KV_FP8_E4M3 (OCP E4M3 "fn": 1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, largest finite 448, no infinities) is an output type
+ * of the extend dequantization only. */
+enum nvfp4kv_dtype { NVFP4KV_F32 = 0, NVFP4KV_BF16 = 1, NVFP4KV_FP8_E4M3 = 2 };
 
 /* NVFP4 KV pool of one layer. */
 typedef struct nvfp4kv_pool {
@@ -222,13 +225,16 @@ int32_t nvfp4_decode_combine(const void* workspace, size_t workspace_bytes, int3
  * current chunk). For each listed sequence s and t < seq_lens[s], writes the
  * dequantized K and V rows of every KV head to row row_offsets[s] + t of the
  * dense workspaces k_out / v_out, shaped [rows][num_kv_heads][128]. The values
- * are exact in both output dtypes (at most 6 significant bits).
+ * (at most 6 significant bits) are exact in f32 and bf16. With
+ * NVFP4KV_FP8_E4M3 (the pages' FP8 workspace) each value is rounded to the
+ * nearest E4M3 value, ties to the even code, and values of magnitude above 448
+ * become +-448 (saturation); the sign of zero is kept.
  *   page_table      device int32 [n_seqs][page_table_stride]
  *   seq_lens        device int32 [n_seqs], prefix tokens to dequantize, each in
  *                   [0, max_seq_len]
  *   row_offsets     device int64 [n_seqs], first workspace row of each sequence
  *   max_seq_len     host upper bound of seq_lens (<= page_table_stride*16)
- *   k_out, v_out    device, bf16 or f32 per out_dtype
+ *   k_out, v_out    device, f32, bf16 or FP8 E4M3 (one byte) per out_dtype
  * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_VALUE (global scale),
  * ERR_HIP.
  */

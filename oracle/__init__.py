@@ -64,6 +64,8 @@ def _load(path: str) -> ctypes.CDLL:
     L.orc_quantize_block16.restype = None
     L.orc_slab_offset.argtypes = [c.c_int64, c.c_int, c.c_int, c.c_int]
     L.orc_slab_offset.restype = c.c_int64
+    L.orc_e4m3_code_of.argtypes = [c.c_double]
+    L.orc_e4m3_code_of.restype = c.c_int
     L.orc_code_nibble.argtypes = [c.c_int, c.c_int, c.c_int]
     L.orc_code_nibble.restype = c.c_int
     L.orc_scale_byte_offset.argtypes = [c.c_int, c.c_int, c.c_int]
@@ -124,6 +126,18 @@ def build_variant(source_text: str, out_path: str) -> str:
 def source_text() -> str:
     with open(_SRC) as f:
         return f.read()
+
+
+def e4m3_code_of(x: float) -> int:
+    """FP8 E4M3 code of a finite value: nearest, ties to even, saturating at 448."""
+    return int(lib().orc_e4m3_code_of(float(x)))
+
+
+def e4m3_codes_of(values: np.ndarray) -> np.ndarray:
+    """Elementwise e4m3_code_of over an array (uint8 codes, same shape)."""
+    flat = np.asarray(values, dtype=np.float64).ravel()
+    f = lib().orc_e4m3_code_of
+    return np.fromiter((f(float(v)) for v in flat), dtype=np.uint8, count=flat.size).reshape(np.shape(values))
 
 
 def code_nibble(kind: int, row: int, channel: int) -> int:

@@ -116,6 +116,14 @@ int orc_e4m3_nearest_of_quotient(double amax, double den) {
   return k;
 }
 
+/* FP8 E4M3 code of a finite value x (the extend path's FP8 workspace): the
+ * nearest E4M3 magnitude, ties to the even code, saturating at 448 (the same
+ * rounding as a block scale, applied to |x|), with the sign bit of x. */
+int orc_e4m3_code_of(double x) {
+  int mag = orc_e4m3_nearest_of_quotient(fabs(x), 1.0);
+  return (signbit(x) ? 0x80 : 0) | mag;
+}
+
 int orc_scale_byte(float amax, float g) {
   return orc_e4m3_nearest_of_quotient((double)amax, 6.0 * (double)g);
 }

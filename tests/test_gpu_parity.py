@@ -160,6 +160,24 @@ def test_dequant_workspace_bitexact():
             assert torch.equal(want.double(), torch.from_numpy(ref))
             assert torch.equal(got.cpu().view(torch.int16 if dt == torch.bfloat16 else torch.int32),
                                want.view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+    # FP8 E4M3 workspace: each value's code is the oracle's rounding of its exact
+    # value (nearest, ties to even, saturating at 448); scales of 2^-2 .. 2^7
+    # times large codes exceed 448 in places, so saturation is exercised too
+    big = [(k * 64.0, v * 64.0) for k, v in kv]
+    gbig = gpu_pool_from_kv(w, big)
+    obig = oracle_pool_from_kv(w, big)
+    assert np.array_equal(gbig.data.cpu().numpy(), obig)
+    for pool_g, pool_o in ((gpool, opool), (gbig, obig)):
+        kr, vr = oracle.dequant_workspace(pool_o, 2, w.page_table, w.seq_lens)
+        k8 = torch.full((rows, 2, 128), 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+        v8 = torch.full_like(k8.view(torch.uint8), 0x7F).view(torch.float8_e4m3fn)
+        B.nvfp4_kv_dequant_workspace(pool_g, pt, sl, ro, max(lens), k8, v8)
+        torch.cuda.synchronize()
+        for got, ref in ((k8, kr), (v8, vr)):
+            want = oracle.e4m3_codes_of(ref)
+            gotb = got.view(torch.uint8).cpu().numpy()
+            assert np.array_equal(gotb, want), f"{int((gotb != want).sum())} FP8 codes differ"
+    assert np.abs(kr).max() > 448  # saturation was exercised
 
 
 def test_split_count_and_page_permutation_invariance_and_reproducibility():

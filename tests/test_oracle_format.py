@@ -268,3 +268,25 @@ def test_byte_accounting_against_page_figures(oracle_lib):
     assert int(free / (vpt * s8["tokens"] * pool_ratio / gib)) == s8["sessions_nvfp4"]
     # per token and layer of the 8-KV-head, head-dim-128 geometry: 1152 bytes
     assert oracle_lib.pool_bytes(1, 8) // 16 == 1152
+
+
+def test_fp8_workspace_rounding_vs_library(oracle_lib):
+    # the FP8 E4M3 workspace code of a value: below 448 it is the library's
+    # round-to-nearest-even float8_e4m3fn cast; above, saturation to +-448
+    rng = np.random.default_rng(31)
+    # float32 inputs (ties and their float32 neighbours are exact there), so the
+    # library rounds once, from the same value the oracle sees
+    finite = np.array([oracle_lib.e4m3_value(b) for b in range(127)], dtype=np.float32)
+    mids = (0.5 * (finite[:-1].astype(np.float64) + finite[1:])).astype(np.float32)  # exact ties
+    xs = np.concatenate([finite, mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(np.inf)),
+                         rng.uniform(0, 448, 2000).astype(np.float32),
+                         rng.uniform(0, 2.0 ** -6, 500).astype(np.float32), np.zeros(1, np.float32)])
+    xs = xs[xs < 448]
+    for sgn in (np.float32(1.0), np.float32(-1.0)):
+        v = sgn * xs
+        lib_codes = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        ours = oracle_lib.e4m3_codes_of(v)
+        assert np.array_equal(ours, lib_codes), (v[ours != lib_codes][:5], ours[ours != lib_codes][:5])
+    for x, want in [(448.0, 0x7E), (464.0, 0x7E), (2688.0, 0x7E), (-1e30, 0xFE), (-0.0, 0x80), (0.0, 0x00),
+                    (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02), (2.0 ** -9 * 7.5, 0x08)]:
+        assert oracle_lib.e4m3_code_of(x) == want, (x, want)

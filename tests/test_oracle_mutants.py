@@ -46,6 +46,7 @@ MUTANTS = [
      "orc_dequant_row(J->pool, page, (int)(15 - t % ORC_PAGE), h, 0,"),
     ("workspace_row_offset", "int64_t o = ((cu_rows[s] + t) * num_kv_heads + h) * ORC_D;",
      "int64_t o = ((cu_rows[s] + t) * num_kv_heads) * ORC_D;"),
+    ("fp8_workspace_sign_dropped", "return (signbit(x) ? 0x80 : 0) | mag;", "return mag;"),
     ("slab_kind_ignored", "return ((page * num_kv_heads + head) * 2 + kind) * (int64_t)ORC_SLAB;",
      "return ((page * num_kv_heads + head) * 2) * (int64_t)ORC_SLAB;"),
 ]
@@ -60,6 +61,7 @@ def _pins(o):
     yield lambda: TF.test_e2m1_code_threshold_edges(o)
     yield lambda: TF.test_round_trip_of_representable_blocks(o)
     yield lambda: TF.test_zero_scale_reading(o)
+    yield lambda: TF.test_fp8_workspace_rounding_vs_library(o)
     yield lambda: TA.test_attention_vs_library_sdpa_on_representable_kv(o, 8, 2, [16, 50, 1])
     yield lambda: TA.test_dequant_workspace_returns_representable_values_exactly(o)
     yield lambda: TA.test_seq_len_one_returns_first_value_row(o)
