@@ -328,10 +328,11 @@ __device__ __forceinline__ int seq_pages(const DecodeArgs& a, int b) {
 // The same for a per-lane b.
 __device__ __forceinline__ int seq_pages_lane(const DecodeArgs& a, int b) { return (a.seq_lens[b] + kPage - 1) / kPage; }
 
-// s_setprio level 3 while more than 3/4 of `quota` pages are left, down to 0
-// for the last quarter.
+// s_setprio level from the share of `quota` pages still left: 3 above 1/3, 2
+// above 1/6, 1 above 1/12, 0 for the rest. Each step down lets the waves that
+// trail catch up; the steps sit late, where the spread of finish times forms.
 __device__ __forceinline__ void set_priority(int left, int quota) {
-  const int level = quota > 0 ? min(3, max(0, (4 * left - 1) / quota)) : 0;
+  const int level = (int)(left * 3 > quota) + (int)(left * 6 > quota) + (int)(left * 12 > quota);
   switch (level) {
     case 3: __builtin_amdgcn_s_setprio(3); break;
     case 2: __builtin_amdgcn_s_setprio(2); break;
