@@ -170,6 +170,13 @@ def query(w: Workload, device: str | torch.device = "cpu") -> torch.Tensor:
     return q.to(torch.bfloat16)
 
 
+def extend_query(w: Workload, device: str | torch.device = "cpu") -> torch.Tensor:
+    """Queries of the extend request's chunk: bfloat16 [chunk, Hq, 128]."""
+    g = torch.Generator(device=device).manual_seed(_mix(w.seed, 0xE9))
+    q = torch.randn((w.extend_chunk, w.num_q_heads, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+    return q.to(torch.bfloat16)
+
+
 def _kv_chunk(w: Workload, seq: int, chunk: int, device) -> tuple[torch.Tensor, torch.Tensor]:
     g = torch.Generator(device=device).manual_seed(_mix(w.seed, 0xC4, seq, chunk))
     shape = (CHUNK_TOKENS, w.num_kv_heads, HEAD_DIM)

@@ -16,6 +16,9 @@ Parity status of each function (what pins it is listed in the tests):
                                    through a permuted page table)
   decode_attn                      pinned (fp64 library SDPA on representable
                                    K/V; closed-form special cases)
+  extend_attn                      pinned (fp64 library SDPA with an explicit
+                                   prefix + causal mask, all three workspace
+                                   dtypes; single-row and equal-key closed forms)
   quantized-vs-unquantized error   parity unpinned (the pages give no number)
 """
 from __future__ import annotations
@@ -82,6 +85,9 @@ def _load(path: str) -> ctypes.CDLL:
     L.orc_decode_attn.argtypes = [P, P, c.c_int64, P, c.c_int, c.c_int, c.c_int, P, c.c_float, c.c_double, P,
                                   P, P, c.c_int, c.c_int]
     L.orc_decode_attn.restype = None
+    L.orc_extend_attn.argtypes = [P, P, P, c.c_int, c.c_int64, P, P, c.c_int64, c.c_int, c.c_int, c.c_double, P, P,
+                                  P, c.c_int64, c.c_int]
+    L.orc_extend_attn.restype = None
     return L
 
 
@@ -253,4 +259,37 @@ def decode_attn(q_bf16_bits: np.ndarray, page_table: np.ndarray, seq_lens: np.nd
         n_u, u_ptr = len(u_arr), _ptr(u_arr)
     lib().orc_decode_attn(_ptr(q), _ptr(pt), pt.shape[1], _ptr(sl), B, hq, num_kv_heads, _ptr(pool), float(g),
                           float(sm_scale), _ptr(out), _ptr(lse), u_ptr, n_u, int(n_threads))
+    return out, lse
+
+
+_WS_DTYPES = {np.dtype(np.float32): 0, np.dtype(np.uint16): 1, np.dtype(np.uint8): 2}
+
+
+def extend_attn(q_bf16_bits: np.ndarray, k_prefix: np.ndarray, v_prefix: np.ndarray, k_chunk_bits: np.ndarray,
+                v_chunk_bits: np.ndarray, sm_scale: float, units=None, n_threads: int = 1):
+    """Extend attention of a C-token chunk after a P-token prefix workspace.
+    q: [C, Hq, 128] bf16 bits; k/v_prefix: [P, Hkv, 128] as float32 values,
+    uint16 bf16 bits or uint8 FP8 E4M3 bytes; k/v_chunk: [C, Hkv, 128] bf16 bits.
+    Returns (out fp64 [C, Hq, 128], lse fp64 [C, Hq]); ``units``: optional
+    iterable of i*Hq + qh to compute (others stay NaN)."""
+    q = np.ascontiguousarray(q_bf16_bits.astype(np.uint16, copy=False))
+    C, hq, d = q.shape
+    kp = np.ascontiguousarray(k_prefix)
+    vp = np.ascontiguousarray(v_prefix)
+    assert kp.dtype == vp.dtype and kp.dtype in _WS_DTYPES and kp.shape == vp.shape
+    P, hkv, d2 = kp.shape
+    assert d == d2 == HEAD_DIM and hq % hkv == 0
+    kc = np.ascontiguousarray(k_chunk_bits.astype(np.uint16, copy=False))
+    vc = np.ascontiguousarray(v_chunk_bits.astype(np.uint16, copy=False))
+    assert kc.shape == vc.shape == (C, hkv, HEAD_DIM)
+    out = np.full((C, hq, HEAD_DIM), np.nan, dtype=np.float64)
+    lse = np.full((C, hq), np.nan, dtype=np.float64)
+    if units is None:
+        u_ptr, n_u = None, C * hq
+    else:
+        u_arr = np.ascontiguousarray(np.asarray(list(units), dtype=np.int64))
+        u_ptr, n_u = _ptr(u_arr), len(u_arr)
+    lib().orc_extend_attn(_ptr(q), _ptr(kp) if P else None, _ptr(vp) if P else None, _WS_DTYPES[kp.dtype], P,
+                          _ptr(kc), _ptr(vc), C, hq, hkv, float(sm_scale), _ptr(out), _ptr(lse), u_ptr, n_u,
+                          int(n_threads))
     return out, lse

@@ -40,6 +40,14 @@
  *      q / (Hq / Hkv) (grouped-query attention, [EUROK] "Unterstuetzung in den
  *      Engines"). Evaluated in fp64 as the plain definition: all logits, their
  *      maximum, exponentials, sums, one division.
+ *   8. Extend (chunked-prefill) attention ([LMSYS] "Interpretation": the
+ *      extend path dequantizes the cached prefix into a workspace, then runs
+ *      attention over it). Query i of a C-token chunk that follows a P-token
+ *      prefix attends over all P workspace rows and chunk rows 0..i, with the
+ *      same softmax and head grouping as step 7. Readings (the page names no
+ *      mask and no precision for the chunk's own keys and values): the mask is
+ *      causal over the chunk, and the chunk's keys and values enter as the
+ *      bf16 values they arrive in, not via the NVFP4 cache.
  *
  * Pool layout (the written definition both sides implement independently):
  *   A pool holds num_pages pages; each page holds, for each KV head h, a K slab
@@ -421,6 +429,125 @@ void orc_decode_attn(const uint16_t* q_bf16, const int32_t* page_table, int64_t 
     orc_attn_worker(&J);
   } else {
     for (i = 0; i < n_threads; ++i) pthread_create(&th[i], NULL, orc_attn_worker, &J);
+    for (i = 0; i < n_threads; ++i) pthread_join(th[i], NULL);
+  }
+  pthread_mutex_destroy(&J.lock);
+}
+
+
+/* ---- 8. extend attention: prefix workspace + causal chunk ---------------- */
+/* Value of element idx of a workspace stored as dtype 0 = f32, 1 = bf16 bits,
+ * 2 = FP8 E4M3 bytes (the three dtypes the extend dequant writes). */
+static double orc_ws_value(const void* base, int dtype, int64_t idx) {
+  if (dtype == 0) return (double)((const float*)base)[idx];
+  if (dtype == 1) return (double)orc_bf16_to_float(((const uint16_t*)base)[idx]);
+  return orc_e4m3_value(((const uint8_t*)base)[idx]);
+}
+
+typedef struct {
+  const uint16_t* q;                 /* bf16 bits [C][Hq][128] */
+  const void *k_pre, *v_pre;         /* [P][Hkv][128] of pre_dtype */
+  int pre_dtype;
+  int64_t prefix_len;
+  const uint16_t *k_chunk, *v_chunk; /* bf16 bits [C][Hkv][128] */
+  int64_t chunk_len;
+  int num_q_heads, num_kv_heads;
+  double sm_scale;
+  double* out; /* [C][Hq][128] */
+  double* lse; /* [C][Hq] */
+  const int64_t* units; /* optional list of (i*Hq + qh); NULL = all */
+  int64_t n_units;
+  int64_t next;
+  pthread_mutex_t lock;
+} orc_ext_job;
+
+/* Key (kind 0) or value (kind 1) channel d of visible row t of KV head h:
+ * rows [0, P) are the prefix workspace, rows P + j chunk row j. */
+static double orc_ext_kv(const orc_ext_job* J, int kind, int64_t t, int h, int d) {
+  if (t < J->prefix_len)
+    return orc_ws_value(kind ? J->v_pre : J->k_pre, J->pre_dtype, (t * J->num_kv_heads + h) * ORC_D + d);
+  {
+    const uint16_t* c = kind ? J->v_chunk : J->k_chunk;
+    return (double)orc_bf16_to_float(c[((t - J->prefix_len) * J->num_kv_heads + h) * ORC_D + d]);
+  }
+}
+
+static void orc_ext_one(orc_ext_job* J, int64_t i, int qh) {
+  int group = J->num_q_heads / J->num_kv_heads;
+  int h = qh / group;
+  int64_t n_vis = J->prefix_len + i + 1; /* causal: chunk rows 0..i */
+  double q[ORC_D], acc[ORC_D];
+  double m = -INFINITY, sum = 0.0;
+  double* z = (double*)malloc(sizeof(double) * (size_t)n_vis);
+  double* out = J->out + (i * J->num_q_heads + qh) * ORC_D;
+  int64_t t;
+  int d;
+  for (d = 0; d < ORC_D; ++d) q[d] = (double)orc_bf16_to_float(J->q[(i * J->num_q_heads + qh) * ORC_D + d]);
+  for (d = 0; d < ORC_D; ++d) acc[d] = 0.0;
+  for (t = 0; t < n_vis; ++t) { /* logits */
+    double dot = 0.0;
+    for (d = 0; d < ORC_D; ++d) dot += q[d] * orc_ext_kv(J, 0, t, h, d);
+    z[t] = J->sm_scale * dot;
+    if (z[t] > m) m = z[t];
+  }
+  for (t = 0; t < n_vis; ++t) { /* weights and weighted sum of values */
+    double w = exp(z[t] - m);
+    sum += w;
+    for (d = 0; d < ORC_D; ++d) acc[d] += w * orc_ext_kv(J, 1, t, h, d);
+  }
+  for (d = 0; d < ORC_D; ++d) out[d] = acc[d] / sum;
+  if (J->lse) J->lse[i * J->num_q_heads + qh] = m + log(sum);
+  free(z);
+}
+
+static void* orc_ext_worker(void* arg) {
+  orc_ext_job* J = (orc_ext_job*)arg;
+  for (;;) {
+    int64_t u;
+    pthread_mutex_lock(&J->lock);
+    u = J->next++;
+    pthread_mutex_unlock(&J->lock);
+    if (u >= J->n_units) break;
+    {
+      int64_t unit = J->units ? J->units[u] : u;
+      orc_ext_one(J, unit / J->num_q_heads, (int)(unit % J->num_q_heads));
+    }
+  }
+  return NULL;
+}
+
+/* Computes out/lse for the listed (i*Hq + qh) units (all when units == NULL)
+ * over n_threads threads; a unit's arithmetic does not depend on the thread. */
+void orc_extend_attn(const uint16_t* q_bf16, const void* k_pre, const void* v_pre, int pre_dtype,
+                     int64_t prefix_len, const uint16_t* k_chunk, const uint16_t* v_chunk, int64_t chunk_len,
+                     int num_q_heads, int num_kv_heads, double sm_scale, double* out, double* lse,
+                     const int64_t* units, int64_t n_units, int n_threads) {
+  orc_ext_job J;
+  pthread_t th[256];
+  int i;
+  J.q = q_bf16;
+  J.k_pre = k_pre;
+  J.v_pre = v_pre;
+  J.pre_dtype = pre_dtype;
+  J.prefix_len = prefix_len;
+  J.k_chunk = k_chunk;
+  J.v_chunk = v_chunk;
+  J.chunk_len = chunk_len;
+  J.num_q_heads = num_q_heads;
+  J.num_kv_heads = num_kv_heads;
+  J.sm_scale = sm_scale;
+  J.out = out;
+  J.lse = lse;
+  J.units = units;
+  J.n_units = units ? n_units : chunk_len * num_q_heads;
+  J.next = 0;
+  pthread_mutex_init(&J.lock, NULL);
+  if (n_threads < 1) n_threads = 1;
+  if (n_threads > 256) n_threads = 256;
+  if (n_threads == 1) {
+    orc_ext_worker(&J);
+  } else {
+    for (i = 0; i < n_threads; ++i) pthread_create(&th[i], NULL, orc_ext_worker, &J);
     for (i = 0; i < n_threads; ++i) pthread_join(th[i], NULL);
   }
   pthread_mutex_destroy(&J.lock);

@@ -5,6 +5,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_attention as TA
+from tests import test_oracle_extend as TE
 from tests import test_oracle_format as TF
 
 # (name, original text, replacement) — each is a single plausible slip that keeps every
@@ -47,6 +48,17 @@ MUTANTS = [
     ("workspace_row_offset", "int64_t o = ((cu_rows[s] + t) * num_kv_heads + h) * ORC_D;",
      "int64_t o = ((cu_rows[s] + t) * num_kv_heads) * ORC_D;"),
     ("fp8_workspace_sign_dropped", "return (signbit(x) ? 0x80 : 0) | mag;", "return mag;"),
+    ("extend_not_causal", "int64_t n_vis = J->prefix_len + i + 1;", "int64_t n_vis = J->prefix_len + J->chunk_len;"),
+    ("extend_misses_own_row", "int64_t n_vis = J->prefix_len + i + 1;", "int64_t n_vis = J->prefix_len + i;"),
+    ("extend_gqa_head_modulo", "int h = qh / group;\n  int64_t n_vis", "int h = qh % J->num_kv_heads;\n  int64_t n_vis"),
+    ("extend_no_sm_scale", "orc_ext_kv(J, 0, t, h, d);\n    z[t] = J->sm_scale * dot;",
+     "orc_ext_kv(J, 0, t, h, d);\n    z[t] = dot;"),
+    ("extend_value_from_key", "acc[d] += w * orc_ext_kv(J, 1, t, h, d);", "acc[d] += w * orc_ext_kv(J, 0, t, h, d);"),
+    ("extend_lse_without_max", "J->lse[i * J->num_q_heads + qh] = m + log(sum);",
+     "J->lse[i * J->num_q_heads + qh] = log(sum);"),
+    ("extend_bf16_workspace_read_as_fp8", "if (dtype == 1) return", "if (dtype == 3) return"),
+    ("extend_chunk_head_ignored", "((t - J->prefix_len) * J->num_kv_heads + h) * ORC_D + d]",
+     "((t - J->prefix_len) * J->num_kv_heads) * ORC_D + d]"),
     ("slab_kind_ignored", "return ((page * num_kv_heads + head) * 2 + kind) * (int64_t)ORC_SLAB;",
      "return ((page * num_kv_heads + head) * 2) * (int64_t)ORC_SLAB;"),
 ]
@@ -65,6 +77,10 @@ def _pins(o):
     yield lambda: TA.test_attention_vs_library_sdpa_on_representable_kv(o, 8, 2, [16, 50, 1])
     yield lambda: TA.test_dequant_workspace_returns_representable_values_exactly(o)
     yield lambda: TA.test_seq_len_one_returns_first_value_row(o)
+    yield lambda: TE.test_first_chunk_query_without_prefix_sees_only_itself(o)
+    yield lambda: TE.test_constant_keys_give_running_mean_of_values(o)
+    for kind in TE.PRE_DTYPES:
+        yield lambda kind=kind: TE.test_extend_vs_library_sdpa(o, kind, 37, 19, 8, 2)
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
