@@ -33,6 +33,7 @@ EXPORTED = [
     "nvfp4_paged_decode_attn_partial",
     "nvfp4_decode_combine",
     "nvfp4_kv_dequant_workspace",
+    "nvfp4_extend_attn",
 ]
 
 
@@ -77,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_kv_dequant_workspace.argtypes = [c.POINTER(PoolDesc), P, c.c_int64, P, P, c.c_int32, c.c_int32,
                                                  P, P, c.c_int32, P]
         L.nvfp4_kv_dequant_workspace.restype = c.c_int32
+        L.nvfp4_extend_attn.argtypes = [P, P, P, c.c_int32, c.c_int64, P, P, c.c_int64, c.c_int32, c.c_int32,
+                                        c.c_float, P, P, P]
+        L.nvfp4_extend_attn.restype = c.c_int32
         _lib = L
     return _lib
 
@@ -223,3 +227,31 @@ def nvfp4_kv_dequant_workspace(pool: Pool, page_table: torch.Tensor, seq_lens: t
            lib().nvfp4_kv_dequant_workspace(ctypes.byref(d), _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
                                             _ptr(row_offsets), seq_lens.numel(), int(max_seq_len), _ptr(k_out),
                                             _ptr(v_out), odt, _stream(stream)))
+
+
+def nvfp4_extend_attn(q: torch.Tensor, k_prefix: torch.Tensor, v_prefix: torch.Tensor, k_chunk: torch.Tensor,
+                      v_chunk: torch.Tensor, sm_scale: float, out: torch.Tensor | None = None,
+                      lse: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Chunk queries q [C, Hq, 128] (bf16) over the prefix workspace k/v_prefix
+    [P, Hkv, 128] (bfloat16 or float8_e4m3fn) and the chunk's own k/v_chunk
+    [C, Hkv, 128] (bf16), causal over the chunk. Returns out [C, Hq, 128] bf16;
+    fills lse [C, Hq] (float32, natural log) when given."""
+    for name, t in (("q", q), ("k_chunk", k_chunk), ("v_chunk", v_chunk)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous bfloat16")
+    if k_prefix.dtype != v_prefix.dtype or not k_prefix.is_contiguous() or not v_prefix.is_contiguous():
+        raise ValueError("k_prefix and v_prefix must be contiguous and share a dtype")
+    pdt = {torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}.get(k_prefix.dtype)
+    if pdt is None:
+        raise ValueError("prefix workspace dtype must be bfloat16 or float8_e4m3fn")
+    C, hq, _ = q.shape
+    P, hkv, _ = k_prefix.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32")
+    _check("nvfp4_extend_attn",
+           lib().nvfp4_extend_attn(_ptr(q), _ptr(k_prefix) if P else None, _ptr(v_prefix) if P else None, pdt, P,
+                                   _ptr(k_chunk), _ptr(v_chunk), C, hq, hkv, float(sm_scale), _ptr(out), _ptr(lse),
+                                   _stream(stream)))
+    return out

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libnvfp4kv.so")
-SOURCES = ["api.hip", "quantize.hip", "decode.hip", "combine.hip", "dequant.hip"]
+SOURCES = ["api.hip", "quantize.hip", "decode.hip", "combine.hip", "dequant.hip", "extend.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -288,4 +288,44 @@ int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page
   return hip_status(nvfp4kv::launch_dequant(a, static_cast<hipStream_t>(stream)));
 }
 
+int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_prefix, int32_t prefix_dtype,
+                          int64_t prefix_len, const void* k_chunk, const void* v_chunk, int64_t chunk_len,
+                          int32_t num_q_heads, int32_t num_kv_heads, float sm_scale, void* out, float* lse,
+                          void* stream) {
+  if (prefix_dtype != NVFP4KV_BF16 && prefix_dtype != NVFP4KV_FP8_E4M3) return NVFP4KV_ERR_DTYPE;
+  if (prefix_len < 0 || chunk_len < 0 || num_q_heads < 1 || num_kv_heads < 1) return NVFP4KV_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > NVFP4KV_MAX_GROUP) return NVFP4KV_ERR_SHAPE;
+  // element offsets of every operand stay far inside int64
+  if (prefix_len > ((int64_t)1 << 40) / ((int64_t)num_kv_heads * 128) ||
+      chunk_len > ((int64_t)1 << 31) / ((int64_t)num_q_heads * 128))
+    return NVFP4KV_ERR_SHAPE;
+  if (!isfinite(sm_scale)) return NVFP4KV_ERR_VALUE;
+  if (chunk_len == 0) return NVFP4KV_OK;
+  if (!q || !k_chunk || !v_chunk || !out || (prefix_len > 0 && (!k_prefix || !v_prefix))) return NVFP4KV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(out) ||
+      (prefix_len > 0 && (!aligned16(k_prefix) || !aligned16(v_prefix))) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return NVFP4KV_ERR_ALIGN;
+  nvfp4kv::ExtendArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pre = k_prefix;
+  a.v_pre = v_prefix;
+  a.pre_fp8 = prefix_dtype == NVFP4KV_FP8_E4M3;
+  a.prefix_len = prefix_len;
+  a.k_chunk = static_cast<const uint16_t*>(k_chunk);
+  a.v_chunk = static_cast<const uint16_t*>(v_chunk);
+  a.chunk_len = chunk_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.qk_scale_log2 = fabsf(sm_scale) * 1.4426950408889634f;
+  a.q_sign = sm_scale < 0.0f ? 0x80008000u : 0u;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.tokens_per_block = nvfp4kv::extend_tokens_per_block(a.group);
+  const int64_t blocks = (chunk_len + a.tokens_per_block - 1) / a.tokens_per_block;
+  if (blocks * num_kv_heads > ((int64_t)1 << 31) - 1) return NVFP4KV_ERR_SHAPE;
+  a.num_token_blocks = (int32_t)blocks;
+  return hip_status(nvfp4kv::launch_extend(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -41,27 +41,6 @@ namespace {
 constexpr float kLazyRescaleLog2 = 8.0f;
 
 
-__device__ __forceinline__ float xor16_max(float v) {
-  const uint32_t u = __float_as_uint(v);
-  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_max(float v) {
-  const uint32_t u = __float_as_uint(v);
-  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor16_sum(float v) {
-  const uint32_t u = __float_as_uint(v);
-  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xor32_sum(float v) {
-  const uint32_t u = __float_as_uint(v);
-  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 __device__ __forceinline__ f16x2 pk_mul(uint32_t a, uint32_t b) { return as_f16x2(a) * as_f16x2(b); }
 
 struct PageRegs {

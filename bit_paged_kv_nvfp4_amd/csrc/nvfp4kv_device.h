@@ -19,6 +19,29 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// Reductions over the four 16-lane rows of a wave64: lane l combines its value
+// with lane l ^ 16 (permlane16 swap) or l ^ 32 (permlane32 swap).
+__device__ __forceinline__ float xor16_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 struct QuantizeArgs {
   const void* k;
   const void* v;
@@ -69,6 +92,26 @@ struct DequantArgs {
   int32_t out_dtype;  // NVFP4KV_F32, NVFP4KV_BF16 or NVFP4KV_FP8_E4M3
 };
 
+struct ExtendArgs {
+  const uint16_t* q;       // bf16 bits [C][Hq][128]
+  const void* k_pre;       // prefix workspace [P][Hkv][128], bf16 or FP8 E4M3
+  const void* v_pre;
+  int32_t pre_fp8;         // 1: the prefix workspace holds FP8 E4M3 bytes
+  int64_t prefix_len;      // P
+  const uint16_t* k_chunk; // bf16 bits [C][Hkv][128]
+  const uint16_t* v_chunk;
+  int64_t chunk_len;       // C
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;           // Hq / Hkv
+  float qk_scale_log2;     // |sm_scale| * log2(e)
+  uint32_t q_sign;         // 0x80008000 when sm_scale < 0 (flips the sign of Q), else 0
+  uint16_t* out;           // bf16 bits [C][Hq][128]
+  float* lse;              // [C][Hq] natural log, or null
+  int32_t tokens_per_block;
+  int32_t num_token_blocks;
+};
+
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
 // Waves that share one split of the decode kernel (one workgroup per split).
 int decode_waves_per_split();
@@ -77,6 +120,9 @@ int decode_resident_workgroups(int num_cus);
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
+// Chunk tokens per workgroup of the extend kernel for a GQA group size.
+int extend_tokens_per_block(int group);
+hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream);
 
 // ---- device helpers --------------------------------------------------------
 

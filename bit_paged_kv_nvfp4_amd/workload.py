@@ -177,6 +177,21 @@ def extend_query(w: Workload, device: str | torch.device = "cpu") -> torch.Tenso
     return q.to(torch.bfloat16)
 
 
+def extend_inputs(seed: int, prefix_len: int, chunk_len: int, num_q_heads: int, num_kv_heads: int,
+                  prefix_dtype=torch.bfloat16, device: str | torch.device = "cpu"):
+    """Seeded inputs of one extend-attention call: q [C, Hq, 128] bf16; a prefix
+    workspace K, V [P, Hkv, 128] in prefix_dtype (bfloat16 or float8_e4m3fn, cast
+    from the same draws as a sequence's K/V, outlier channels included); chunk K, V
+    [C, Hkv, 128] bf16 (the tokens that follow the prefix)."""
+    w = small_workload(seed, 1, num_q_heads, num_kv_heads, [prefix_len + chunk_len])
+    g = torch.Generator(device=device).manual_seed(_mix(seed, 0xE9))
+    q = torch.randn((chunk_len, num_q_heads, HEAD_DIM), generator=g, device=device,
+                    dtype=torch.float32).to(torch.bfloat16)
+    k, v = kv(w, 0, 0, prefix_len + chunk_len, device)
+    return (q, k[:prefix_len].to(prefix_dtype), v[:prefix_len].to(prefix_dtype), k[prefix_len:].to(torch.bfloat16),
+            v[prefix_len:].to(torch.bfloat16))
+
+
 def _kv_chunk(w: Workload, seq: int, chunk: int, device) -> tuple[torch.Tensor, torch.Tensor]:
     g = torch.Generator(device=device).manual_seed(_mix(w.seed, 0xC4, seq, chunk))
     shape = (CHUNK_TOKENS, w.num_kv_heads, HEAD_DIM)

@@ -20,6 +20,8 @@
  *     queries and NVFP4 keys and values).
  *   - nvfp4_kv_dequant_workspace: the extend path's dequantization of a cached
  *     prefix into a dense workspace ([LMSYS] "Interpretation").
+ *   - nvfp4_extend_attn: the extend path's attention of a chunk of queries over
+ *     that workspace and the chunk itself ([LMSYS] "Interpretation").
  *
  * NVFP4 ([EUROK] "Bytes pro Token"; [LMSYS] "Interpretation", "Perspective"):
  * each value is E2M1 (1 sign, 2 exponent, 1 mantissa bit; magnitudes 0, 0.5, 1,
@@ -241,6 +243,39 @@ int32_t nvfp4_decode_combine(const void* workspace, size_t workspace_bytes, int3
 int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page_table, int64_t page_table_stride,
                                    const int32_t* seq_lens, const int64_t* row_offsets, int32_t n_seqs,
                                    int32_t max_seq_len, void* k_out, void* v_out, int32_t out_dtype, void* stream);
+
+/*
+ * Extend-path attention ([LMSYS] "Interpretation": after the cached prefix is
+ * dequantized into a workspace, the chunk's queries attend over it and over the
+ * chunk). One request: a chunk of C tokens that follows a P-token prefix. Query
+ * token i (0 <= i < C), query head qh, attends over all P workspace rows and
+ * over chunk rows 0..i (causal), reading KV head qh / (num_q_heads /
+ * num_kv_heads):
+ *   out[i][qh] = sum_t softmax_t(sm_scale * q[i][qh] . k_t) v_t,
+ *   lse[i][qh] = ln sum_t exp(sm_scale * q[i][qh] . k_t)   (natural log)
+ * Readings (the page names no mask and no precision for the chunk's own rows):
+ * the mask is causal over the chunk, and the chunk's keys and values enter as
+ * the bf16 values given here, not via the NVFP4 cache.
+ *   q               device bf16 [C][num_q_heads][128], contiguous
+ *   k_prefix, v_prefix  device [P][num_kv_heads][128] workspace as written by
+ *                   nvfp4_kv_dequant_workspace: NVFP4KV_BF16 or
+ *                   NVFP4KV_FP8_E4M3 per prefix_dtype (finite values); may be
+ *                   NULL when P = 0
+ *   k_chunk, v_chunk    device bf16 [C][num_kv_heads][128], contiguous
+ *   out             device bf16 [C][num_q_heads][128]
+ *   lse             device f32 [C][num_q_heads] or NULL
+ * num_q_heads must be a multiple of num_kv_heads with a quotient of at most 16.
+ * Arithmetic: bf16 products with fp32 accumulation on the matrix cores; the
+ * softmax weights enter the second product rounded to bf16 (the row sums use
+ * the same rounded weights). All device pointers 16-byte aligned; nothing is
+ * allocated; the call is asynchronous on `stream`.
+ * Errors: ERR_NULL, ERR_SHAPE (counts out of range, group > 16), ERR_ALIGN,
+ * ERR_DTYPE (prefix_dtype), ERR_VALUE (sm_scale not finite), ERR_HIP.
+ */
+int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_prefix, int32_t prefix_dtype,
+                          int64_t prefix_len, const void* k_chunk, const void* v_chunk, int64_t chunk_len,
+                          int32_t num_q_heads, int32_t num_kv_heads, float sm_scale, void* out, float* lse,
+                          void* stream);
 
 #ifdef __cplusplus
 }

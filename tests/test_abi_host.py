@@ -135,6 +135,30 @@ def test_dequant_validation(L):
     assert x_call(L, pool(), ro=FAKE + 4) == ERR_ALIGN
 
 
+def e_call(L, q=FAKE, kp=FAKE, vp=FAKE, pdt=1, P=100, kc=FAKE, vc=FAKE, C=10, hq=8, hkv=1, sm=0.088, out=FAKE,
+           lse=None):
+    return L.nvfp4_extend_attn(q, kp, vp, pdt, P, kc, vc, C, hq, hkv, sm, out, lse, None)
+
+
+def test_extend_validation(L):
+    assert e_call(L, pdt=0) == ERR_DTYPE  # f32 prefix is not an attention input
+    assert e_call(L, pdt=7) == ERR_DTYPE
+    assert e_call(L, P=-1) == ERR_SHAPE
+    assert e_call(L, C=-1) == ERR_SHAPE
+    assert e_call(L, hq=0) == ERR_SHAPE
+    assert e_call(L, hq=8, hkv=3) == ERR_SHAPE
+    assert e_call(L, hq=17, hkv=1) == ERR_SHAPE  # group > 16
+    assert e_call(L, sm=float("nan")) == ERR_VALUE
+    assert e_call(L, C=0) == OK  # no-op, no HIP call
+    assert e_call(L, q=None) == ERR_NULL
+    assert e_call(L, kc=None) == ERR_NULL
+    assert e_call(L, out=None) == ERR_NULL
+    assert e_call(L, kp=None) == ERR_NULL
+    assert e_call(L, q=FAKE + 2) == ERR_ALIGN
+    assert e_call(L, vp=FAKE + 8) == ERR_ALIGN
+    assert e_call(L, lse=FAKE + 2) == ERR_ALIGN
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(B, "_lib", None)

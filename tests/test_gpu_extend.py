@@ -1,0 +1,114 @@
+"""GPU parity of the extend attention (nvfp4_extend_attn, through the C ABI)
+against the oracle's fp64 extend attention on the same seeded inputs.
+
+Bar: |gpu - ref| <= 2e-3 + 1e-2 |ref| for the bf16 output; lse within 1e-3 +
+1e-4 |ref|. Inputs: a bf16 or FP8 E4M3 prefix workspace and a bf16 chunk, drawn
+by the workload module; the pipeline case feeds each side its own quantize and
+dequant of the same K/V."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_paged_kv_nvfp4_amd import binding as B
+from bit_paged_kv_nvfp4_amd import workload as W
+from tests.gpu_common import assert_close, bf16_bits, gpu_pool_from_kv, oracle_pool_from_kv
+
+pytestmark = pytest.mark.gpu
+
+
+def _ws_np(t):
+    """A workspace tensor as the oracle's input: bf16 bits or FP8 bytes."""
+    t = t.cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return bf16_bits(t)
+    return t.view(torch.uint8).numpy()
+
+
+def _run(q, kp, vp, kc, vc, sm):
+    C, hq, _ = q.shape
+    lse = torch.empty((C, hq), dtype=torch.float32, device="cuda")
+    out = B.nvfp4_extend_attn(q.cuda(), kp.cuda(), vp.cuda(), kc.cuda(), vc.cuda(), sm, lse=lse)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _oracle(q, kp, vp, kc, vc, sm, units=None):
+    return oracle.extend_attn(bf16_bits(q), _ws_np(kp), _ws_np(vp), bf16_bits(kc), bf16_bits(vc), sm, units=units,
+                              n_threads=8)
+
+
+CASES = [
+    # name, P, C, Hq, Hkv, prefix dtype, sm_scale
+    ("ragged_tiles_gqa8", 100, 37, 8, 1, torch.bfloat16, None),
+    ("no_prefix", 0, 70, 16, 2, torch.bfloat16, None),
+    ("llama_shape_fp8", 200, 130, 64, 8, torch.float8_e4m3fn, None),
+    ("group1", 64, 64, 4, 4, torch.bfloat16, None),
+    ("group3_dummy_rows", 33, 5, 48, 16, torch.float8_e4m3fn, None),
+    ("group16", 17, 40, 32, 2, torch.bfloat16, None),
+    ("negative_scale", 90, 21, 8, 2, torch.bfloat16, -0.05),
+    ("single_token_chunk", 300, 1, 8, 1, torch.float8_e4m3fn, None),
+]
+
+
+@pytest.mark.parametrize("name,P,C,hq,hkv,dt,sm", CASES, ids=[c[0] for c in CASES])
+def test_extend_attention_matches_oracle(name, P, C, hq, hkv, dt, sm):
+    print(f"case {name}: P={P} C={C} Hq={hq} Hkv={hkv} {dt}", flush=True)
+    q, kp, vp, kc, vc = W.extend_inputs(300 + P + C, P, C, hq, hkv, prefix_dtype=dt)
+    sm = 128 ** -0.5 if sm is None else sm
+    out, lse = _run(q, kp, vp, kc, vc, sm)
+    ref, ref_lse = _oracle(q, kp, vp, kc, vc, sm)
+    err = assert_close(out, ref, what=name)
+    assert_close(lse, ref_lse, atol=1e-3, rtol=1e-4, what=name + " lse")
+    print(f"  max abs err {err:.3e}")
+
+
+def test_extend_pipeline_quantize_dequant_attend():
+    """quantize-on-write -> dequant of the prefix into a bf16 and an FP8 workspace
+    -> attention, each side on its own: the GPU through the library, the oracle
+    through its own pool and workspace."""
+    P, C, hq, hkv = 150, 45, 16, 2
+    w = W.small_workload(410, 1, hq, hkv, [P])
+    k, v = W.kv(w, 0, 0, P)
+    gpool = gpu_pool_from_kv(w, [(k, v)])
+    opool = oracle_pool_from_kv(w, [(k, v)])
+    pt = torch.as_tensor(w.page_table, device="cuda").contiguous()
+    sl = torch.as_tensor(w.seq_lens, device="cuda")
+    ro = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ko, vo = oracle.dequant_workspace(opool, hkv, w.page_table, w.seq_lens)  # exact NVFP4 values, fp64
+    q, _, _, kc, vc = W.extend_inputs(411, 0, C, hq, hkv)
+    sm = 128 ** -0.5
+    for dt in (torch.bfloat16, torch.float8_e4m3fn):
+        k_ws = torch.empty((P, hkv, 128), dtype=dt, device="cuda")
+        v_ws = torch.empty_like(k_ws)
+        B.nvfp4_kv_dequant_workspace(gpool, pt, sl, ro, P, k_ws, v_ws)
+        out, lse = _run(q, k_ws, v_ws, kc, vc, sm)
+        if dt == torch.bfloat16:  # the values have at most 6 significant bits: exact in bf16
+            ok = (ko.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+            ov = (vo.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        else:
+            ok, ov = oracle.e4m3_codes_of(ko), oracle.e4m3_codes_of(vo)
+        ref, ref_lse = oracle.extend_attn(bf16_bits(q), ok, ov, bf16_bits(kc), bf16_bits(vc), sm, n_threads=8)
+        assert_close(out, ref, what=f"pipeline {dt}")
+        assert_close(lse, ref_lse, atol=1e-3, rtol=1e-4, what=f"pipeline {dt} lse")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float8_e4m3fn])
+def test_extend_full_size_sampled_rows(dt):
+    """The extend request's full shape (163840-token prefix, 8192-token chunk, 64
+    query / 8 KV heads) in the launch configuration bench.py times; the oracle
+    checks sampled (token, head) rows: first and last tokens, token-block edges."""
+    w = W.config(5)
+    P, C, hq, hkv = w.extend_prefix, w.extend_chunk, w.num_q_heads, w.num_kv_heads
+    print(f"full size P={P} C={C} {dt}", flush=True)
+    q, kp, vp, kc, vc = W.extend_inputs(w.seed, P, C, hq, hkv, prefix_dtype=dt, device="cuda")
+    out, lse = _run(q, kp, vp, kc, vc, w.sm_scale)
+    tokens = [0, 1, 15, 16, 17, 4095, 4096, 8190, 8191]
+    heads = [0, 7, 8, 37, 63]
+    units = [t * hq + h for t in tokens for h in heads]
+    ref, ref_lse = _oracle(q.cpu(), kp.cpu(), vp.cpu(), kc.cpu(), vc.cpu(), w.sm_scale, units=units)
+    ti = np.array([u // hq for u in units])
+    hi = np.array([u % hq for u in units])
+    err = assert_close(out[ti, hi], ref[ti, hi], what="sampled rows (unit order as listed)")
+    assert_close(lse[ti, hi], ref_lse[ti, hi], atol=1e-3, rtol=1e-4, what="sampled lse")
+    print(f"  max abs err {err:.3e} over {len(units)} rows")
