@@ -7,26 +7,30 @@
 // a P-token prefix attends over all P workspace rows and over chunk rows 0..i
 // (causal), with query head q reading KV head q / (Hq / Hkv).
 //
-// Work item: one workgroup of four waves per (KV head, block of chunk tokens).
-// Consecutive workgroups take consecutive KV heads, so with Hkv = 8 every block
-// of one head runs on one XCD and the head's K/V stream is shared through that
-// XCD's L2. A wave owns 32 rows, row = token_in_block * group + head, and per
-// 64-key tile computes
-//   S^T[64 keys x 32 rows] = K[64 x 128] Q^T      32 x v_mfma_f32_16x16x32_bf16
-//   O^T[128 x 32 rows]    += V^T[128 x 64] P^T    32 x v_mfma_f32_16x16x32_f16
+// Work item: one workgroup of four waves per (KV head, block of chunk tokens);
+// two workgroups share a CU. Consecutive workgroups take consecutive KV heads,
+// so with Hkv = 8 every block of one head runs on one XCD and the head's K/V
+// stream is shared through that XCD's L2. A wave owns 32 rows, row =
+// token_in_block * group + head, and per 32-key tile computes
+//   S^T[32 keys x 32 rows] = K[32 x 128] Q^T      16 x v_mfma_f32_16x16x32_bf16
+//   O^T[128 x 32 rows]    += V^T[128 x 32] P^T    16 x v_mfma_f32_16x16x32_f16
 // A 16x16x32 MFMA lane (n = lane % 16, G = lane / 16) holds row n of A and
 // column n of B with k slots 8G..8G+7, and column n, rows 4G..4G+3 of C. So the
 // S^T fragment of a lane (row n; keys 4G..4G+3 of each 16-key block) is already
-// a P^T operand: its k slots are keys 4G..4G+3 of block 2ks, then of block
-// 2ks+1, and the V^T operand is read with the same key order.
-// K and V^T of a tile are staged in LDS (the next tile waits in registers while
-// the current one is computed). 16-byte K pieces and 8-byte V^T pieces are
-// XOR-swizzled by row, so the 16 rows that a quarter-wave reads hit distinct
-// banks. The V^T transpose happens in registers with byte permutes.
-// K enters the first product as bf16 (FP8 workspace bytes widen exactly), V the
-// second as f16, converted on the way into LDS: exact for every value of
-// magnitude below 65504, which covers every NVFP4- or FP8-derived workspace value
-// (at g = 1) and every chunk value a model produces.
+// a P^T operand: its k slots are keys 4G..4G+3 of block 0, then of block 1, and
+// the V^T operand is read with the same key order.
+//
+// Tiles: the prefix in 32-key tiles (the last one may be partial), then the
+// chunk in 32-key tiles, so that every tile has one source dtype. Each tile's
+// K and V rows are copied global -> LDS asynchronously (global_load_lds) into a
+// three-stage ring, two tiles ahead of the one being computed. A bf16 K tile
+// lands directly in the layout the first product reads; raw V (and FP8 K) are
+// then converted by the whole workgroup: V into a transposed f16 tile, FP8 K
+// into bf16 (both exact). 16-byte and 8-byte pieces are XOR-swizzled by row so
+// that the rows a quarter-wave reads fall in distinct banks.
+// K enters the first product as bf16, V the second as f16: exact for every
+// value of magnitude below 65504, which covers every NVFP4- or FP8-derived
+// workspace value (at g = 1) and every chunk value a model produces.
 // Online softmax in fp32, base 2, with a lazy rescale (the running max moves
 // only when a tile's max exceeds it by more than 2^8, so P <= 256); P enters
 // the second product as f16 (11 significant bits, where bf16 would keep 8 and
@@ -39,130 +43,157 @@ namespace nvfp4kv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-constexpr int kXWaves = 4;
-constexpr int kXRows = 32;  // rows per wave
-constexpr int kTile = 64;   // keys per tile
-constexpr float kXLazyLog2 = 8.0f;
-
-struct TileRegs {
-  uint4 k[4];  // K pieces t + 256 j: key p / 16, channels 8 (p % 16) .. +7
-  uint4 v[4];  // V of keys 4 (t / 16) + j, channels 8 (t % 16) .. +7
-};
-
-// Raw 8 elements (channels 8c .. 8c+7) of key row kp: prefix rows come from the
-// workspace (FP8 bytes land in .x, .y), chunk rows from the chunk, rows past the
-// chunk are zero.
-__device__ __forceinline__ uint4 load8(const ExtendArgs& a, const void* pre, const uint16_t* chunk, int h,
-                                       int64_t kp, int c) {
-  uint4 r = make_uint4(0u, 0u, 0u, 0u);
-  if (kp < a.prefix_len) {
-    const int64_t e = (kp * a.num_kv_heads + h) * kHeadDim + 8 * c;
-    if (a.pre_fp8) {
-      const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(pre) + e);
-      r.x = w.x;
-      r.y = w.y;
-    } else {
-      r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(pre) + e);
-    }
-  } else if (kp - a.prefix_len < a.chunk_len) {
-    r = *reinterpret_cast<const uint4*>(chunk + ((kp - a.prefix_len) * a.num_kv_heads + h) * kHeadDim + 8 * c);
-  }
-  return r;
-}
-
-// Two E4M3 values (as f32) -> two bf16 in one word; exact, since three mantissa
-// bits fit in bf16's seven.
-__device__ __forceinline__ uint32_t pack_bf16_exact(f32x2 f) {
-  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
-}
-
-// The raw elements of key row kp as 8 bf16.
-__device__ __forceinline__ uint4 widen8(const ExtendArgs& a, int64_t kp, uint4 r) {
-  if (a.pre_fp8 && kp < a.prefix_len) {
-    return make_uint4(pack_bf16_exact(__builtin_amdgcn_cvt_pk_f32_fp8(r.x, false)),
-                      pack_bf16_exact(__builtin_amdgcn_cvt_pk_f32_fp8(r.x, true)),
-                      pack_bf16_exact(__builtin_amdgcn_cvt_pk_f32_fp8(r.y, false)),
-                      pack_bf16_exact(__builtin_amdgcn_cvt_pk_f32_fp8(r.y, true)));
-  }
-  return r;
-}
-
-// Two floats -> two f16 (nearest, ties to even) in one word.
-__device__ __forceinline__ uint32_t f16x2_rne(float x0, float x1) {
-  const f16x2 h = {(_Float16)x0, (_Float16)x1};
-  return __builtin_bit_cast(uint32_t, h);
-}
-
-// The raw elements of key row kp as 8 f16 (the value operand of the second
-// product). Exact for every value of magnitude below 65504: the workspace holds
-// E4M3 or NVFP4 products, and a bf16 value in f16's normal range needs at most
-// 8 of its 11 significant bits.
-__device__ __forceinline__ uint4 widen8_f16(const ExtendArgs& a, int64_t kp, uint4 r) {
-  uint4 o;
-  if (a.pre_fp8 && kp < a.prefix_len) {
-    const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8(r.x, false), f1 = __builtin_amdgcn_cvt_pk_f32_fp8(r.x, true);
-    const f32x2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8(r.y, false), f3 = __builtin_amdgcn_cvt_pk_f32_fp8(r.y, true);
-    o = make_uint4(f16x2_rne(f0[0], f0[1]), f16x2_rne(f1[0], f1[1]), f16x2_rne(f2[0], f2[1]), f16x2_rne(f3[0], f3[1]));
-  } else {
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-    uint32_t h[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = f16x2_rne(__uint_as_float(w[i] << 16), __uint_as_float(w[i] & 0xFFFF0000u));
-    o = make_uint4(h[0], h[1], h[2], h[3]);
-  }
-  return o;
-}
-
-__device__ __forceinline__ void load_tile(const ExtendArgs& a, int h, int64_t base, int t, TileRegs& x) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int p = t + 256 * j;
-    x.k[j] = load8(a, a.k_pre, a.k_chunk, h, base + (p >> 4), p & 15);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) x.v[j] = load8(a, a.v_pre, a.v_chunk, h, base + 4 * (t >> 4) + j, t & 15);
-}
-
-// k_lds: [key][16 pieces of 16 B], piece c of key r at index r * 16 + (c ^ (r & 15)).
-// vt_lds: [channel][16 pieces of 8 B = 4 keys], piece q of channel d at
-// d * 16 + (q ^ (d & 15)).
-__device__ __forceinline__ void store_tile(const ExtendArgs& a, int64_t base, int t, const TileRegs& x,
-                                           uint4* k_lds, uint2* vt_lds) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int p = t + 256 * j;
-    const int r = p >> 4, c = p & 15;
-    k_lds[r * 16 + (c ^ (r & 15))] = widen8(a, base + r, x.k[j]);
-  }
-  const int q = t >> 4, c = t & 15;
-  uint4 v[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = widen8_f16(a, base + 4 * q + j, x.v[j]);
-  const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-  const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
-  const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
-  const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    // word w of a key holds channels 8c + 2w (low half) and 8c + 2w + 1 (high)
-    const int d0 = 8 * c + 2 * w, d1 = d0 + 1;
-    vt_lds[d0 * 16 + (q ^ (d0 & 15))] = make_uint2(__builtin_amdgcn_perm(w1[w], w0[w], 0x05040100u),
-                                                   __builtin_amdgcn_perm(w3[w], w2[w], 0x05040100u));
-    vt_lds[d1 * 16 + (q ^ (d1 & 15))] = make_uint2(__builtin_amdgcn_perm(w1[w], w0[w], 0x07060302u),
-                                                   __builtin_amdgcn_perm(w3[w], w2[w], 0x07060302u));
-  }
-}
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Two finite floats -> two bf16 (nearest, ties to even) in one word.
+constexpr int kXWaves = 4;
+constexpr int kXRows = 32;                  // rows per wave
+constexpr int kTile = 32;                   // keys per tile
+constexpr int kStages = 3;                  // copies run two tiles ahead
+constexpr int kStageBytes = kTile * 256;    // a tile of bf16 rows of one head
+constexpr float kXLazyLog2 = 8.0f;
+
+// Barrier for LDS data only: the workgroup's LDS writes are complete and
+// visible; outstanding global -> LDS copies are left running.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Two floats -> two bf16 / f16 (nearest, ties to even) in one word.
 __device__ __forceinline__ uint32_t bf16x2_rne(float x0, float x1) {
   const f32x2 f = {x0, x1};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
+__device__ __forceinline__ uint32_t f16x2_rne(float x0, float x1) {
+  const f16x2 h = {(_Float16)x0, (_Float16)x1};
+  return __builtin_bit_cast(uint32_t, h);
+}
+// E4M3 bytes 0,1 (hi = false) or 2,3 of w as two f32 (exact).
+__device__ __forceinline__ f32x2 fp8x2(uint32_t w, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+}
+// Two exact E4M3 values as two bf16 (three mantissa bits fit in seven).
+__device__ __forceinline__ uint32_t bf16x2_exact(f32x2 f) {
+  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+}
 
-__global__ __launch_bounds__(64 * kXWaves) __attribute__((amdgpu_waves_per_eu(1))) void k_extend_attn(ExtendArgs a) {
+// One tile: its keys' source rows and dtype.
+struct Tile {
+  const uint8_t* k;  // K row of the tile's first key, this head
+  const uint8_t* v;
+  int n_valid;       // keys of the tile that exist (the rest is masked)
+  bool fp8;          // rows are E4M3 bytes (else bf16)
+  bool chunk;        // chunk tile (causal mask) or prefix tile
+  int64_t first;     // index of the first key in the chunk (chunk tile) or prefix
+};
+
+template <bool kPreFp8>
+__device__ __forceinline__ Tile tile_of(const ExtendArgs& a, int h, int n_pre, int i) {
+  Tile x;
+  const int64_t Hkv = a.num_kv_heads;
+  if (i < n_pre) {
+    x.first = (int64_t)i * kTile;
+    x.n_valid = (int)min<int64_t>(kTile, a.prefix_len - x.first);
+    x.fp8 = kPreFp8;
+    x.chunk = false;
+    const int64_t row = (x.first * Hkv + h) * kHeadDim * (kPreFp8 ? 1 : 2);
+    x.k = static_cast<const uint8_t*>(a.k_pre) + row;
+    x.v = static_cast<const uint8_t*>(a.v_pre) + row;
+  } else {
+    x.first = (int64_t)(i - n_pre) * kTile;
+    x.n_valid = (int)min<int64_t>(kTile, a.chunk_len - x.first);
+    x.fp8 = false;
+    x.chunk = true;
+    const int64_t row = (x.first * Hkv + h) * kHeadDim * 2;
+    x.k = reinterpret_cast<const uint8_t*>(a.k_chunk) + row;
+    x.v = reinterpret_cast<const uint8_t*>(a.v_chunk) + row;
+  }
+  return x;
+}
+
+// Copies of a tile into one ring stage by wave w: 4 per wave for bf16 rows, 2
+// for FP8 rows. LDS layouts of a stage:
+//   K bf16: piece (16 B) c of key r at 16-byte slot r * 16 + (c ^ (r & 15))
+//   V bf16: piece c of key r at slot r * 16 + (c ^ ((r >> 1) & 15))
+//   K FP8:  piece (16 B = 16 channels) j of key r at slot r * 8 + j
+//   V FP8:  piece j of key r at slot r * 8 + (j ^ ((r >> 1) & 7))
+// Keys past n_valid copy the tile's last valid row (in bounds; masked later).
+__device__ __forceinline__ void issue_tile(const Tile& x, int hkv, uint32_t k_lds, uint32_t v_lds, int w,
+                                           int lane) {
+  if (!x.fp8) {
+    const uint32_t rs = (uint32_t)hkv * 256;  // bytes between consecutive keys of one head
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int p = (2 * w + j) * 64 + lane;
+      const int r = p >> 4, cs = p & 15;
+      const uint32_t rr = (uint32_t)min(r, x.n_valid - 1);
+      dma16(x.k, rr * rs + 16 * (cs ^ (r & 15)), k_lds + (2 * w + j) * 1024);
+      dma16(x.v, rr * rs + 16 * (cs ^ ((r >> 1) & 15)), v_lds + (2 * w + j) * 1024);
+    }
+  } else {
+    const uint32_t rs = (uint32_t)hkv * 128;
+    const int p = w * 64 + lane;
+    const int r = p >> 3, cs = p & 7;
+    const uint32_t rr = (uint32_t)min(r, x.n_valid - 1);
+    dma16(x.k, rr * rs + 16 * cs, k_lds + w * 1024);
+    dma16(x.v, rr * rs + 16 * (cs ^ ((r >> 1) & 7)), v_lds + w * 1024);
+  }
+}
+
+// V^T tile (f16): channel d, keys 4q .. 4q+3 (one 8-byte piece) at byte
+// d * 64 + 8 (q ^ ((d >> 2) & 3)).
+__device__ __forceinline__ uint32_t vt_piece(int d, int q) { return d * 64 + 8 * (q ^ ((d >> 2) & 3)); }
+
+// Workgroup pass over a landed stage: raw V -> V^T (f16); FP8 K -> bf16 K in the
+// K-operand layout. Thread t: channels 8c .. 8c+7 (c = t / 16) of keys 2m, 2m+1
+// (m = t % 16).
+__device__ __forceinline__ void convert_tile(bool fp8, int t, const uint8_t* k_st, const uint8_t* v_st,
+                                             uint8_t* vt, uint8_t* kconv) {
+  const int c = t >> 4, m = t & 15;
+  uint32_t lo[4], hi[4];  // channels (8c + 2e, 8c + 2e + 1) of key 2m and of key 2m + 1, as f16 pairs
+  if (!fp8) {
+    const uint4 a0 = *reinterpret_cast<const uint4*>(v_st + 16 * ((2 * m) * 16 + (c ^ m)));
+    const uint4 a1 = *reinterpret_cast<const uint4*>(v_st + 16 * ((2 * m + 1) * 16 + (c ^ m)));
+    const uint32_t w0[4] = {a0.x, a0.y, a0.z, a0.w}, w1[4] = {a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = f16x2_rne(__uint_as_float(w0[e] << 16), __uint_as_float(w0[e] & 0xFFFF0000u));
+      hi[e] = f16x2_rne(__uint_as_float(w1[e] << 16), __uint_as_float(w1[e] & 0xFFFF0000u));
+    }
+  } else {
+    const int off = 16 * ((c >> 1) ^ (m & 7)) + 8 * (c & 1);
+    const uint2 b0 = *reinterpret_cast<const uint2*>(v_st + (2 * m) * 128 + off);
+    const uint2 b1 = *reinterpret_cast<const uint2*>(v_st + (2 * m + 1) * 128 + off);
+    const uint32_t w0[2] = {b0.x, b0.y}, w1[2] = {b1.x, b1.y};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f32x2 f0 = fp8x2(w0[e >> 1], e & 1), f1 = fp8x2(w1[e >> 1], e & 1);
+      lo[e] = f16x2_rne(f0[0], f0[1]);
+      hi[e] = f16x2_rne(f1[0], f1[1]);
+    }
+    // FP8 K: thread t widens 16 channels (piece t % 8) of key t / 8
+    const int r = t >> 3, j = t & 7;
+    const uint4 kb = *reinterpret_cast<const uint4*>(k_st + r * 128 + 16 * j);
+    const uint32_t kw[4] = {kb.x, kb.y, kb.z, kb.w};
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint4 o = make_uint4(bf16x2_exact(fp8x2(kw[2 * hh], false)), bf16x2_exact(fp8x2(kw[2 * hh], true)),
+                                 bf16x2_exact(fp8x2(kw[2 * hh + 1], false)),
+                                 bf16x2_exact(fp8x2(kw[2 * hh + 1], true)));
+      const int cc = 2 * j + hh;
+      *reinterpret_cast<uint4*>(kconv + 16 * (r * 16 + (cc ^ (r & 15)))) = o;
+    }
+  }
+  // keys 2m, 2m + 1 are half (m & 1) of the 4-key piece m / 2
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int d0 = 8 * c + 2 * e, d1 = d0 + 1;
+    *reinterpret_cast<uint32_t*>(vt + vt_piece(d0, m >> 1) + 4 * (m & 1)) =
+        __builtin_amdgcn_perm(hi[e], lo[e], 0x05040100u);
+    *reinterpret_cast<uint32_t*>(vt + vt_piece(d1, m >> 1) + 4 * (m & 1)) =
+        __builtin_amdgcn_perm(hi[e], lo[e], 0x07060302u);
+  }
+}
+
+template <bool kPreFp8>
+__global__ __launch_bounds__(64 * kXWaves) __attribute__((amdgpu_waves_per_eu(2))) void k_extend_attn(ExtendArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -174,17 +205,18 @@ __global__ __launch_bounds__(64 * kXWaves) __attribute__((amdgpu_waves_per_eu(1)
   const int64_t P = a.prefix_len, C = a.chunk_len;
   const int64_t t_first = (int64_t)tb * a.tokens_per_block;
   const int64_t t_last = min(t_first + a.tokens_per_block, C) - 1;
-  const int64_t n_keys = P + t_last + 1;
-  const int n_tiles = (int)((n_keys + kTile - 1) / kTile);
+  const int n_pre = (int)((P + kTile - 1) / kTile);
+  const int n_tiles = n_pre + (int)((t_last + kTile) / kTile);  // chunk keys 0 .. t_last
 
-  __shared__ uint4 k_lds[kTile * 16];
-  __shared__ uint2 vt_lds[kHeadDim * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t k_ring[kStages][kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t v_ring[kStages][kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t vt[kTile * kHeadDim * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t kconv[kPreFp8 ? kStageBytes : 16];
+  const uint32_t k_ring_lds = (uint32_t)reinterpret_cast<uintptr_t>(&k_ring[0][0]);
+  const uint32_t v_ring_lds = (uint32_t)reinterpret_cast<uintptr_t>(&v_ring[0][0]);
 
-  TileRegs nxt;
-  load_tile(a, h, 0, t, nxt);
-
-  // this lane's rows (one per row block): token, query head; tokens past the
-  // chunk (or rows past the block's tokens) are computed but never stored
+  // this lane's rows (one per row block): token, query head; rows past the
+  // block's tokens or the chunk are computed but never stored
   int64_t tok[2];
   int qh[2];
   bool valid[2];
@@ -198,18 +230,29 @@ __global__ __launch_bounds__(64 * kXWaves) __attribute__((amdgpu_waves_per_eu(1)
     if (!valid[rb]) tok[rb] = INT64_MAX / 4;  // sees every key: no masking
   }
   // Q^T operands: column = row, k slots = channels 32 s + 8 G .. +7
+  uint4 qraw[2][4];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qraw[rb][s] = make_uint4(0u, 0u, 0u, 0u);
+      if (valid[rb])
+        qraw[rb][s] =
+            *reinterpret_cast<const uint4*>(a.q + (tok[rb] * a.num_q_heads + qh[rb]) * kHeadDim + 32 * s + 8 * G);
+    }
   bf16x8 qf[2][4];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      uint4 u = make_uint4(0u, 0u, 0u, 0u);
-      if (valid[rb])
-        u = *reinterpret_cast<const uint4*>(a.q + (tok[rb] * a.num_q_heads + qh[rb]) * kHeadDim + 32 * s + 8 * G);
+      uint4 u = qraw[rb][s];
       u.x ^= a.q_sign;
       u.y ^= a.q_sign;
       u.z ^= a.q_sign;
       u.w ^= a.q_sign;
+      // consume the loads here, so that their wait is not placed inside the
+      // tile loop (where it would also drain the asynchronous copies)
+      asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
       qf[rb][s] = __builtin_bit_cast(bf16x8, u);
     }
   const float c2 = a.qk_scale_log2;  // >= 0: a negative scale is folded into the sign of Q
@@ -222,39 +265,57 @@ __global__ __launch_bounds__(64 * kXWaves) __attribute__((amdgpu_waves_per_eu(1)
   float m_ref[2] = {-__builtin_inff(), -__builtin_inff()};
   float lsum[2] = {0.f, 0.f};
 
-  for (int it = 0; it < n_tiles; ++it) {
-    const int64_t base = (int64_t)it * kTile;
-    __syncthreads();  // every wave is done with the previous tile
-    store_tile(a, base, t, nxt, k_lds, vt_lds);
-    __syncthreads();
-    if (it + 1 < n_tiles) load_tile(a, h, base + kTile, t, nxt);
+  // prologue: tiles 0 and 1 in flight
+  for (int i = 0; i < 2 && i < n_tiles; ++i)
+    issue_tile(tile_of<kPreFp8>(a, h, n_pre, i), Hkv, k_ring_lds + i * kStageBytes, v_ring_lds + i * kStageBytes,
+               wave, lane);
+
+  for (int i = 0; i < n_tiles; ++i) {
+    const int st = i % kStages;
+    const Tile x = tile_of<kPreFp8>(a, h, n_pre, i);
+    // this wave's copies of tile i have landed once only tile i+1's are pending
+    if (i + 1 >= n_tiles)
+      wait_dma<0>();
+    else if (kPreFp8 && i + 1 < n_pre)
+      wait_dma<2>();
+    else
+      wait_dma<4>();
+    lds_barrier();  // every wave: tile i landed, tile i-1 fully consumed
+    if (i + 2 < n_tiles) {
+      const int s2 = (i + 2) % kStages;
+      issue_tile(tile_of<kPreFp8>(a, h, n_pre, i + 2), Hkv, k_ring_lds + s2 * kStageBytes,
+                 v_ring_lds + s2 * kStageBytes, wave, lane);
+    }
+    convert_tile(x.fp8, t, k_ring[st], v_ring[st], vt, kconv);
+    lds_barrier();  // V^T (and widened K) of tile i complete
 
     // ---- S^T = K Q^T ----
-    f32x4 sacc[4][2];
+    const uint4* kt = reinterpret_cast<const uint4*>(x.fp8 ? kconv : k_ring[st]);
+    f32x4 sacc[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) sacc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int r = 16 * kb + n;
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, k_lds[r * 16 + ((4 * s + G) ^ n)]);
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, kt[(16 * kb + n) * 16 + ((4 * s + G) ^ n)]);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][s], sacc[kb][rb], 0, 0, 0);
+        for (int rb = 0; rb < 2; ++rb)
+          sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][s], sacc[kb][rb], 0, 0, 0);
       }
 
-    // ---- mask: key kp is visible to token i iff kp <= P + i ----
-    if (base + kTile - 1 > P + t_first) {
+    // ---- mask: missing keys; chunk key j is visible to token i iff j <= i ----
+    if (x.n_valid < kTile || (x.chunk && x.first + kTile - 1 > t_first)) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int64_t kp = base + 16 * kb + 4 * G + r;
+          const int j = 16 * kb + 4 * G + r;
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
-            if (kp > P + tok[rb]) sacc[kb][rb][r] = -__builtin_inff();
+            if (j >= x.n_valid || (x.chunk && x.first + j > tok[rb])) sacc[kb][rb][r] = -__builtin_inff();
         }
     }
 
@@ -265,7 +326,7 @@ __global__ __launch_bounds__(64 * kXWaves) __attribute__((amdgpu_waves_per_eu(1)
     for (int rb = 0; rb < 2; ++rb) {
       float mx = -__builtin_inff();
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = __builtin_fmaxf(mx, sacc[kb][rb][r]);
       mx = xor32_max(xor16_max(mx));
@@ -282,38 +343,31 @@ __global__ __launch_bounds__(64 * kXWaves) __attribute__((amdgpu_waves_per_eu(1)
         for (int d = 0; d < 8; ++d) oacc[d][rb] *= alpha;
       }
     }
-    // P^T operands: k slots = keys 4G..4G+3 of block 2ks, then of block 2ks + 1
-    uint32_t pw[2][2][4];
+    // P^T operands: k slots = keys 4G..4G+3 of block 0, then of block 1
+    f16x8 pf[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const float mu = m_ref[rb] == -__builtin_inff() ? 0.0f : m_ref[rb];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; r += 2) {
-          const f16x2 ph = {(_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][r], c2, -mu)),
-                            (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][r + 1], c2, -mu))};
-          lsum[rb] += (float)ph[0] + (float)ph[1];
-          pw[rb][kb >> 1][(kb & 1) * 2 + (r >> 1)] = __builtin_bit_cast(uint32_t, ph);
+        for (int r = 0; r < 4; ++r) {
+          const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][r], c2, -mu));
+          pf[rb][4 * kb + r] = p;
+          lsum[rb] += (float)p;
         }
     }
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      f16x8 pf[2];
+    for (int d = 0; d < 8; ++d) {
+      const int dim = 16 * d + n;
+      const uint2 v0 = *reinterpret_cast<const uint2*>(vt + vt_piece(dim, G));
+      const uint2 v1 = *reinterpret_cast<const uint2*>(vt + vt_piece(dim, 4 + G));
+      const f16x8 vf = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
-        pf[rb] = __builtin_bit_cast(f16x8, make_uint4(pw[rb][ks][0], pw[rb][ks][1], pw[rb][ks][2], pw[rb][ks][3]));
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const int dim = 16 * d + n;
-        const uint2 v0 = vt_lds[dim * 16 + ((8 * ks + G) ^ n)];
-        const uint2 v1 = vt_lds[dim * 16 + ((8 * ks + 4 + G) ^ n)];
-        const f16x8 vf = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) oacc[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[rb], oacc[d][rb], 0, 0, 0);
-      }
+        oacc[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[rb], oacc[d][rb], 0, 0, 0);
     }
   }
 
@@ -330,7 +384,8 @@ __global__ __launch_bounds__(64 * kXWaves) __attribute__((amdgpu_waves_per_eu(1)
       // channels 16 d + 4 G .. +3 of this row
       *reinterpret_cast<uint2*>(o + 16 * d + 4 * G) = make_uint2(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]));
     }
-    if (a.lse != nullptr && G == 0) a.lse[tok[rb] * a.num_q_heads + qh[rb]] = (m_ref[rb] + __builtin_log2f(l)) * 0.69314718055994531f;
+    if (a.lse != nullptr && G == 0)
+      a.lse[tok[rb] * a.num_q_heads + qh[rb]] = (m_ref[rb] + __builtin_log2f(l)) * 0.69314718055994531f;
   }
 }
 
@@ -340,8 +395,11 @@ int extend_tokens_per_block(int group) { return kXWaves * kXRows / group; }
 
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream) {
   if (a.chunk_len == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_extend_attn, dim3((unsigned)a.num_token_blocks * (unsigned)a.num_kv_heads),
-                     dim3(64 * kXWaves), 0, stream, a);
+  const dim3 grid((unsigned)a.num_token_blocks * (unsigned)a.num_kv_heads), block(64 * kXWaves);
+  if (a.pre_fp8)
+    hipLaunchKernelGGL(k_extend_attn<true>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_extend_attn<false>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

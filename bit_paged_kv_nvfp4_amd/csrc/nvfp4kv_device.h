@@ -42,6 +42,40 @@ __device__ __forceinline__ float xor32_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// One asynchronous 16-byte-per-lane copy global -> LDS (gfx950 global_load_lds
+// dwordx4): lane i reads base + voff and writes LDS address lds + 16 i. It is
+// issued from inline assembly so that the compiler, which cannot tell which LDS
+// bytes such a copy writes, does not drain all outstanding copies before every
+// LDS read; completion is awaited explicitly with wait_dma().
+// A wave-uniform copy of a pointer, held in SGPRs (readfirstlane is free when the
+// value already is scalar); the copy instructions take their base from SGPRs.
+template <typename T>
+__device__ __forceinline__ const T* sgpr_ptr(const T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sgpr_ptr(base)),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// Same with 4 bytes per lane (lane i writes LDS address lds + 4 i).
+__device__ __forceinline__ void dma4(const int32_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(sgpr_ptr(base)),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_dma() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 struct QuantizeArgs {
   const void* k;
   const void* v;
