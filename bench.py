@@ -28,6 +28,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16/fp16 matrix peak
 METRIC = "NVFP4 paged decode-attn KV-read GB/s (% of HBM peak) + decode steps/s/layer"
 
 
@@ -140,7 +141,8 @@ def cpu_baseline(w, n_seqs, W, torch):
 def extend_step(w, pool, B, W, torch, steps, warmup):
     """Config 5's chunked-prefill step: quantize-write the 8192-token bf16 chunk
     into the extend request's pages, dequantize its 163840-token prefix into a
-    bf16 workspace. Events on the stream bracket each kernel."""
+    bf16 (and, separately, an FP8) workspace, and run the chunk's attention over
+    workspace + chunk. Events on the stream bracket each kernel."""
     row = w.extend_row
     # the prefix must be resident: fill it once (untimed)
     P, C = w.extend_prefix, w.extend_chunk
@@ -149,6 +151,8 @@ def extend_step(w, pool, B, W, torch, steps, warmup):
         k, v = W.kv(w, row, t0, t1, device="cuda")
         B.nvfp4_kv_quantize(k, v, torch.as_tensor(W.slots(w, row, t0, t1), device="cuda"), pool)
     kc, vc = W.extend_chunk_kv(w, device="cuda")
+    qc = W.extend_query(w, device="cuda")
+    att_out = torch.empty_like(qc)
     cslots = torch.as_tensor(W.slots(w, row, P, P + C), device="cuda")
     # Two prefixes of P tokens in turn, the extend request's and the first P tokens
     # of decode sequence 0 (both in the pool), so that one repeat's 189 MB read is
@@ -166,20 +170,31 @@ def extend_step(w, pool, B, W, torch, steps, warmup):
     for i in range(warmup):
         B.nvfp4_kv_quantize(kc, vc, cslots, pool, stream=stream)
         B.nvfp4_kv_dequant_workspace(pool, pts[i % 2], sl, ro, P, k_ws, v_ws, stream=stream)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        B.nvfp4_extend_attn(qc, k_ws, v_ws, kc, vc, w.sm_scale, out=att_out, stream=stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
+        # the bf16 step: quantize the chunk, dequantize the prefix, attend; then
+        # the same dequant and attention with an FP8 workspace
         ev[i][0].record(stream)
         B.nvfp4_kv_quantize(kc, vc, cslots, pool, stream=stream)
         ev[i][1].record(stream)
         B.nvfp4_kv_dequant_workspace(pool, pts[i % 2], sl, ro, P, k_ws, v_ws, stream=stream)
         ev[i][2].record(stream)
-        B.nvfp4_kv_dequant_workspace(pool, pts[(i + 1) % 2], sl, ro, P, k_w8, v_w8, stream=stream)
+        B.nvfp4_extend_attn(qc, k_ws, v_ws, kc, vc, w.sm_scale, out=att_out, stream=stream)
         ev[i][3].record(stream)
+        B.nvfp4_kv_dequant_workspace(pool, pts[(i + 1) % 2], sl, ro, P, k_w8, v_w8, stream=stream)
+        ev[i][4].record(stream)
+        B.nvfp4_extend_attn(qc, k_w8, v_w8, kc, vc, w.sm_scale, out=att_out, stream=stream)
+        ev[i][5].record(stream)
     torch.cuda.synchronize()
     q_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     d_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-    d8_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+    a_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+    d8_ms = sum(e[3].elapsed_time(e[4]) for e in ev) / steps
+    a8_ms = sum(e[4].elapsed_time(e[5]) for e in ev) / steps
+    # attention flops: QK^T and PV, 2 x 128 multiply-adds per (query row, visible key)
+    a_flops = 4 * w.num_q_heads * 128 * (C * P + C * (C + 1) // 2)
     q_bytes = C * w.num_kv_heads * 128 * 2 * 2 + C * w.num_kv_heads * 2 * 8 * 9  # bf16 in + NVFP4 out
     d_bytes = P * w.num_kv_heads * 2 * 8 * 9 + P * w.num_kv_heads * 128 * 2 * 2  # NVFP4 in + bf16 out
     d8_bytes = P * w.num_kv_heads * 2 * 8 * 9 + P * w.num_kv_heads * 128 * 2  # NVFP4 in + FP8 out
@@ -188,6 +203,13 @@ def extend_step(w, pool, B, W, torch, steps, warmup):
             "dequant_prefix_GBps": round(d_bytes / (d_ms * 1e-3) / 1e9, 1), "dequant_prefix_bytes": d_bytes,
             "dequant_prefix_fp8_ms": round(d8_ms, 5), "dequant_prefix_fp8_GBps": round(d8_bytes / (d8_ms * 1e-3) / 1e9, 1),
             "dequant_prefix_fp8_bytes": d8_bytes,
+            "attn_ms": round(a_ms, 4), "attn_TFLOPs": round(a_flops / (a_ms * 1e-3) / 1e12, 1),
+            "attn_fp8_ms": round(a8_ms, 4), "attn_fp8_TFLOPs": round(a_flops / (a8_ms * 1e-3) / 1e12, 1),
+            "attn_flops": a_flops,
+            "attn_roofline": {"bound": "mfma", "achieved": round(a_flops / (a_ms * 1e-3) / 1e12, 1),
+                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(a_flops / (a_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "step_ms": round(q_ms + d_ms + a_ms, 4), "step_fp8_ms": round(q_ms + d8_ms + a8_ms, 4),
             "chunk_tokens": C, "prefix_tokens": P,
             "note": "two different prefixes alternate, so no repeat reads the previous one's bytes from the last-level cache"}
 
