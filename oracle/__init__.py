@@ -16,6 +16,9 @@ Parity status of each function (what pins it is listed in the tests):
                                    through a permuted page table)
   decode_attn                      pinned (fp64 library SDPA on representable
                                    K/V; closed-form special cases)
+  fp8_* (FP8 baseline pool)        pinned (codes vs library float8 cast of x/s;
+                                   layout bijection; attention vs fp64 SDPA on
+                                   E4M3-representable K/V with scales)
   extend_attn                      pinned (fp64 library SDPA with an explicit
                                    prefix + causal mask, all three workspace
                                    dtypes; single-row and equal-key closed forms)
@@ -88,6 +91,22 @@ def _load(path: str) -> ctypes.CDLL:
     L.orc_extend_attn.argtypes = [P, P, P, c.c_int, c.c_int64, P, P, c.c_int64, c.c_int, c.c_int, c.c_double, P, P,
                                   P, c.c_int64, c.c_int]
     L.orc_extend_attn.restype = None
+    L.orc_fp8_slab_offset.argtypes = [c.c_int64, c.c_int, c.c_int, c.c_int]
+    L.orc_fp8_slab_offset.restype = c.c_int64
+    L.orc_fp8_byte_offset.argtypes = [c.c_int, c.c_int, c.c_int]
+    L.orc_fp8_byte_offset.restype = c.c_int
+    L.orc_fp8_pool_bytes.argtypes = [c.c_int64, c.c_int]
+    L.orc_fp8_pool_bytes.restype = c.c_int64
+    L.orc_fp8_code.argtypes = [c.c_float, c.c_float]
+    L.orc_fp8_code.restype = c.c_int
+    L.orc_fp8_quantize_to_pool.argtypes = [P, P, c.c_int, c.c_int64, c.c_int64, P, c.c_int64, c.c_int, c.c_float,
+                                           c.c_float, P]
+    L.orc_fp8_quantize_to_pool.restype = None
+    L.orc_fp8_dequant_row.argtypes = [P, c.c_int64, c.c_int, c.c_int, c.c_int, c.c_int, c.c_float, P]
+    L.orc_fp8_dequant_row.restype = None
+    L.orc_fp8_decode_attn.argtypes = [P, P, c.c_int64, P, c.c_int, c.c_int, c.c_int, P, c.c_float, c.c_float,
+                                      c.c_double, P, P, P, c.c_int, c.c_int]
+    L.orc_fp8_decode_attn.restype = None
     return L
 
 
@@ -292,4 +311,71 @@ def extend_attn(q_bf16_bits: np.ndarray, k_prefix: np.ndarray, v_prefix: np.ndar
     lib().orc_extend_attn(_ptr(q), _ptr(kp) if P else None, _ptr(vp) if P else None, _WS_DTYPES[kp.dtype], P,
                           _ptr(kc), _ptr(vc), C, hq, hkv, float(sm_scale), _ptr(out), _ptr(lse), u_ptr, n_u,
                           int(n_threads))
+    return out, lse
+
+
+# ---- FP8 baseline (E4M3 per value, per-tensor scale) ------------------------
+FP8_SLAB_BYTES = 2048
+
+
+def fp8_pool_bytes(num_pages: int, num_kv_heads: int) -> int:
+    return int(lib().orc_fp8_pool_bytes(num_pages, num_kv_heads))
+
+
+def fp8_byte_offset(kind: int, row: int, channel: int) -> int:
+    return int(lib().orc_fp8_byte_offset(kind, row, channel))
+
+
+def fp8_slab_offset(page: int, head: int, kind: int, num_kv_heads: int) -> int:
+    return int(lib().orc_fp8_slab_offset(page, head, kind, num_kv_heads))
+
+
+def fp8_code(x: float, scale: float = 1.0) -> int:
+    return int(lib().orc_fp8_code(float(x), float(scale)))
+
+
+def fp8_quantize_to_pool(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray, num_pages: int,
+                         k_scale: float = 1.0, v_scale: float = 1.0, pool: np.ndarray | None = None) -> np.ndarray:
+    """k, v: [T, Hkv, 128] float32 or uint16 (bf16 bits). Returns the FP8 pool."""
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    assert k.shape == v.shape and k.dtype == v.dtype and k.shape[2] == HEAD_DIM
+    T, hkv, _ = k.shape
+    dtype = 0 if k.dtype == np.float32 else 1
+    assert dtype == 0 or k.dtype == np.uint16
+    if pool is None:
+        pool = np.zeros(fp8_pool_bytes(num_pages, hkv), dtype=np.uint8)
+    sm = np.ascontiguousarray(slot_mapping.astype(np.int32, copy=False))
+    lib().orc_fp8_quantize_to_pool(_ptr(k), _ptr(v), dtype, hkv * HEAD_DIM, HEAD_DIM, _ptr(sm), T, hkv,
+                                   float(k_scale), float(v_scale), _ptr(pool))
+    return pool
+
+
+def fp8_dequant_row(pool: np.ndarray, page: int, row: int, head: int, kind: int, num_kv_heads: int,
+                    scale: float = 1.0) -> np.ndarray:
+    out = np.zeros(HEAD_DIM, dtype=np.float64)
+    lib().orc_fp8_dequant_row(_ptr(pool), int(page), int(row), int(head), int(kind), int(num_kv_heads),
+                              float(scale), _ptr(out))
+    return out
+
+
+def fp8_decode_attn(q_bf16_bits: np.ndarray, page_table: np.ndarray, seq_lens: np.ndarray, pool: np.ndarray,
+                    num_kv_heads: int, sm_scale: float, k_scale: float = 1.0, v_scale: float = 1.0, units=None,
+                    n_threads: int = 1):
+    """Decode attention over the FP8 baseline pool; same conventions as decode_attn."""
+    q = np.ascontiguousarray(q_bf16_bits.astype(np.uint16, copy=False))
+    B, hq, d = q.shape
+    assert d == HEAD_DIM and hq % num_kv_heads == 0
+    pt = np.ascontiguousarray(page_table.astype(np.int32, copy=False))
+    sl = np.ascontiguousarray(seq_lens.astype(np.int32, copy=False))
+    out = np.full((B, hq, HEAD_DIM), np.nan, dtype=np.float64)
+    lse = np.full((B, hq), np.nan, dtype=np.float64)
+    if units is None:
+        u_ptr, n_u = None, B * hq
+    else:
+        u_arr = np.ascontiguousarray(np.asarray(list(units), dtype=np.int32))
+        u_ptr, n_u = _ptr(u_arr), len(u_arr)
+    lib().orc_fp8_decode_attn(_ptr(q), _ptr(pt), pt.shape[1], _ptr(sl), B, hq, num_kv_heads, _ptr(pool),
+                              float(k_scale), float(v_scale), float(sm_scale), _ptr(out), _ptr(lse), u_ptr, n_u,
+                              int(n_threads))
     return out, lse

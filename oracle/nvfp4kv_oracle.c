@@ -48,6 +48,13 @@
  *      mask and no precision for the chunk's own keys and values): the mask is
  *      causal over the chunk, and the chunk's keys and values enter as the
  *      bf16 values they arrive in, not via the NVFP4 cache.
+ *   9. FP8 baseline ([LMSYS] "Perspective" and "Synopsis" compare NVFP4 KV
+ *      against an FP8 KV cache; [EUROK] "Bytes pro Token" gives FP8 one byte
+ *      per value). Each value is stored as the E4M3 code of x / s, s the
+ *      per-tensor scale of K or V: the nearest E4M3 value, ties to the even
+ *      code, saturating at 448, sign of x kept (the rounding of step 3 applied
+ *      to |x|, with den = s). It decodes to E4M3(code) * s. Decode attention
+ *      over such a cache is step 7 with these rows.
  *
  * Pool layout (the written definition both sides implement independently):
  *   A pool holds num_pages pages; each page holds, for each KV head h, a K slab
@@ -63,6 +70,13 @@
  *     V scale (row r, block j): byte 1024 + j*16 + r
  *   (a V code byte holds rows r and r+2 of one channel).
  *   Token t of a sequence lives at page page_table[t/16], row t%16.
+ *
+ * FP8 pool layout (the baseline's written definition): each page holds, for
+ * each KV head h, a K slab then a V slab of 2048 bytes each, slab(p, h, kind) at
+ * byte ((p * Hkv + h) * 2 + kind) * 2048, one code byte per value:
+ *     K (row r, channel d): byte r*128 + d
+ *     V (row r, channel d): byte ((r/4)*16 + d/8)*32 + (d%8)*4 + r%4
+ *   (a 32-byte V chunk holds channels 8n..8n+7 of rows 4g..4g+3, channel-major).
  */
 #include <math.h>
 #include <pthread.h>
@@ -334,6 +348,8 @@ typedef struct {
   int batch, num_q_heads, num_kv_heads;
   const uint8_t* pool;
   float g;
+  int fp8;                /* 1: the pool is the FP8 baseline (step 9) */
+  float k_scale, v_scale; /* its per-tensor scales */
   double sm_scale;
   double* out; /* [B][Hq][128] */
   double* lse; /* [B][Hq] */
@@ -342,6 +358,18 @@ typedef struct {
   int next; /* work counter */
   pthread_mutex_t lock;
 } orc_attn_job;
+
+void orc_fp8_dequant_row(const uint8_t* pool, int64_t page, int row, int head, int kind, int num_kv_heads,
+                         float scale, double* out128);
+
+/* Decoded K (kind 0) or V (kind 1) row of one head for the attention: from the
+ * NVFP4 pool (step 6) or the FP8 baseline pool (step 9). */
+static void orc_attn_row(const orc_attn_job* J, int64_t page, int row, int h, int kind, double* out) {
+  if (J->fp8)
+    orc_fp8_dequant_row(J->pool, page, row, h, kind, J->num_kv_heads, kind ? J->v_scale : J->k_scale, out);
+  else
+    orc_dequant_row(J->pool, page, row, h, kind, J->num_kv_heads, J->g, out);
+}
 
 static void orc_attn_one(orc_attn_job* J, int b, int qh) {
   int group = J->num_q_heads / J->num_kv_heads;
@@ -364,7 +392,7 @@ static void orc_attn_one(orc_attn_job* J, int b, int qh) {
   for (t = 0; t < L; ++t) { /* logits */
     int64_t page = J->page_table[b * J->page_table_stride + t / ORC_PAGE];
     double dot = 0.0;
-    orc_dequant_row(J->pool, page, (int)(t % ORC_PAGE), h, 0, J->num_kv_heads, J->g, kd);
+    orc_attn_row(J, page, (int)(t % ORC_PAGE), h, 0, kd);
     for (d = 0; d < ORC_D; ++d) dot += q[d] * kd[d];
     z[t] = J->sm_scale * dot;
     if (z[t] > m) m = z[t];
@@ -372,7 +400,7 @@ static void orc_attn_one(orc_attn_job* J, int b, int qh) {
   for (t = 0; t < L; ++t) { /* weights and weighted sum of values */
     int64_t page = J->page_table[b * J->page_table_stride + t / ORC_PAGE];
     double w = exp(z[t] - m);
-    orc_dequant_row(J->pool, page, (int)(t % ORC_PAGE), h, 1, J->num_kv_heads, J->g, vd);
+    orc_attn_row(J, page, (int)(t % ORC_PAGE), h, 1, vd);
     sum += w;
     for (d = 0; d < ORC_D; ++d) acc[d] += w * vd[d];
   }
@@ -400,10 +428,10 @@ static void* orc_attn_worker(void* arg) {
 /* Computes out/lse for the listed (b*Hq + qh) units (all when units == NULL),
  * spreading whole units over n_threads threads; the arithmetic of a unit does
  * not depend on the thread count. */
-void orc_decode_attn(const uint16_t* q_bf16, const int32_t* page_table, int64_t page_table_stride,
-                     const int32_t* seq_lens, int batch, int num_q_heads, int num_kv_heads,
-                     const uint8_t* pool, float g, double sm_scale, double* out, double* lse,
-                     const int32_t* units, int n_units, int n_threads) {
+static void orc_attn_run(const uint16_t* q_bf16, const int32_t* page_table, int64_t page_table_stride,
+                         const int32_t* seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                         const uint8_t* pool, float g, int fp8, float k_scale, float v_scale, double sm_scale,
+                         double* out, double* lse, const int32_t* units, int n_units, int n_threads) {
   orc_attn_job J;
   pthread_t th[256];
   int i;
@@ -416,6 +444,9 @@ void orc_decode_attn(const uint16_t* q_bf16, const int32_t* page_table, int64_t 
   J.num_kv_heads = num_kv_heads;
   J.pool = pool;
   J.g = g;
+  J.fp8 = fp8;
+  J.k_scale = k_scale;
+  J.v_scale = v_scale;
   J.sm_scale = sm_scale;
   J.out = out;
   J.lse = lse;
@@ -432,6 +463,23 @@ void orc_decode_attn(const uint16_t* q_bf16, const int32_t* page_table, int64_t 
     for (i = 0; i < n_threads; ++i) pthread_join(th[i], NULL);
   }
   pthread_mutex_destroy(&J.lock);
+}
+
+void orc_decode_attn(const uint16_t* q_bf16, const int32_t* page_table, int64_t page_table_stride,
+                     const int32_t* seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                     const uint8_t* pool, float g, double sm_scale, double* out, double* lse,
+                     const int32_t* units, int n_units, int n_threads) {
+  orc_attn_run(q_bf16, page_table, page_table_stride, seq_lens, batch, num_q_heads, num_kv_heads, pool, g, 0, 1.0f,
+               1.0f, sm_scale, out, lse, units, n_units, n_threads);
+}
+
+/* Decode attention over the FP8 baseline pool (steps 7 and 9). */
+void orc_fp8_decode_attn(const uint16_t* q_bf16, const int32_t* page_table, int64_t page_table_stride,
+                         const int32_t* seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                         const uint8_t* pool, float k_scale, float v_scale, double sm_scale, double* out,
+                         double* lse, const int32_t* units, int n_units, int n_threads) {
+  orc_attn_run(q_bf16, page_table, page_table_stride, seq_lens, batch, num_q_heads, num_kv_heads, pool, 1.0f, 1,
+               k_scale, v_scale, sm_scale, out, lse, units, n_units, n_threads);
 }
 
 
@@ -551,4 +599,62 @@ void orc_extend_attn(const uint16_t* q_bf16, const void* k_pre, const void* v_pr
     for (i = 0; i < n_threads; ++i) pthread_join(th[i], NULL);
   }
   pthread_mutex_destroy(&J.lock);
+}
+
+
+/* ---- 9. FP8 baseline: pool layout, quantize-on-write, row decode ---------- */
+#define ORC_FP8_SLAB 2048
+
+int64_t orc_fp8_slab_offset(int64_t page, int head, int kind, int num_kv_heads) {
+  return ((page * num_kv_heads + head) * 2 + kind) * (int64_t)ORC_FP8_SLAB;
+}
+
+int orc_fp8_byte_offset(int kind, int row, int d) {
+  if (kind == 0) return row * 128 + d;
+  return ((row / 4) * 16 + d / 8) * 32 + (d % 8) * 4 + row % 4;
+}
+
+int64_t orc_fp8_pool_bytes(int64_t num_pages, int num_kv_heads) {
+  return num_pages * num_kv_heads * 2 * (int64_t)ORC_FP8_SLAB;
+}
+
+/* E4M3 code of x / s: nearest E4M3 magnitude of |x| / s (exact comparisons of
+ * |x| against s times each midpoint), ties to the even code, saturating at 448,
+ * sign of x. */
+int orc_fp8_code(float x, float s) {
+  int mag = orc_e4m3_nearest_of_quotient(fabs((double)x), (double)s);
+  return (signbit(x) ? 0x80 : 0) | mag;
+}
+
+/* Quantize-on-write of T tokens of K and V ([T][Hkv][128], element strides
+ * given) into the FP8 pool at slot_mapping[t] = page*16 + row (negative = skip).
+ * src_dtype 0 = float32, 1 = bfloat16 bits. Every byte belongs to one (token,
+ * head, channel), so write order does not matter. */
+void orc_fp8_quantize_to_pool(const void* k_src, const void* v_src, int src_dtype, int64_t token_stride,
+                              int64_t head_stride, const int32_t* slot_mapping, int64_t num_tokens,
+                              int num_kv_heads, float k_scale, float v_scale, uint8_t* pool) {
+  int64_t t;
+  int h, kind, d;
+  for (t = 0; t < num_tokens; ++t) {
+    int32_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    for (h = 0; h < num_kv_heads; ++h)
+      for (kind = 0; kind < 2; ++kind) {
+        const void* src = kind == 0 ? k_src : v_src;
+        uint8_t* slab = pool + orc_fp8_slab_offset(slot / ORC_PAGE, h, kind, num_kv_heads);
+        for (d = 0; d < ORC_D; ++d) {
+          int64_t idx = t * token_stride + h * head_stride + d;
+          float x = src_dtype == 0 ? ((const float*)src)[idx] : orc_bf16_to_float(((const uint16_t*)src)[idx]);
+          slab[orc_fp8_byte_offset(kind, slot % ORC_PAGE, d)] = (uint8_t)orc_fp8_code(x, kind ? v_scale : k_scale);
+        }
+      }
+  }
+}
+
+/* Decoded K (kind 0) or V (kind 1) row of one head: E4M3(code) * scale. */
+void orc_fp8_dequant_row(const uint8_t* pool, int64_t page, int row, int head, int kind, int num_kv_heads,
+                         float scale, double* out128) {
+  const uint8_t* slab = pool + orc_fp8_slab_offset(page, head, kind, num_kv_heads);
+  int d;
+  for (d = 0; d < ORC_D; ++d) out128[d] = orc_e4m3_value(slab[orc_fp8_byte_offset(kind, row, d)]) * (double)scale;
 }

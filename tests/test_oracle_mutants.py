@@ -6,6 +6,7 @@ import pytest
 import oracle
 from tests import test_oracle_attention as TA
 from tests import test_oracle_extend as TE
+from tests import test_oracle_fp8 as T8
 from tests import test_oracle_format as TF
 
 # (name, original text, replacement) — each is a single plausible slip that keeps every
@@ -36,15 +37,15 @@ MUTANTS = [
      "int s = slab[orc_scale_byte_offset(kind, row, d / 32)];"),
     ("gqa_head_modulo", "int h = qh / group;", "int h = qh % J->num_kv_heads;"),
     ("no_sm_scale", "z[t] = J->sm_scale * dot;", "z[t] = dot;"),
-    ("value_row_shifted", "orc_dequant_row(J->pool, page, (int)(t % ORC_PAGE), h, 1,",
-     "orc_dequant_row(J->pool, page, (int)((t + 1) % ORC_PAGE), h, 1,"),
-    ("value_uses_key_slab", "orc_dequant_row(J->pool, page, (int)(t % ORC_PAGE), h, 1,",
-     "orc_dequant_row(J->pool, page, (int)(t % ORC_PAGE), h, 0,"),
+    ("value_row_shifted", "orc_attn_row(J, page, (int)(t % ORC_PAGE), h, 1,",
+     "orc_attn_row(J, page, (int)((t + 1) % ORC_PAGE), h, 1,"),
+    ("value_uses_key_slab", "orc_attn_row(J, page, (int)(t % ORC_PAGE), h, 1,",
+     "orc_attn_row(J, page, (int)(t % ORC_PAGE), h, 0,"),
     ("last_token_dropped", "for (t = 0; t < L; ++t) { /* weights", "for (t = 0; t < L - 1; ++t) { /* weights"),
     ("lse_without_max", "J->lse[(int64_t)b * J->num_q_heads + qh] = m + log(sum);",
      "J->lse[(int64_t)b * J->num_q_heads + qh] = log(sum);"),
-    ("key_row_reversed", "orc_dequant_row(J->pool, page, (int)(t % ORC_PAGE), h, 0,",
-     "orc_dequant_row(J->pool, page, (int)(15 - t % ORC_PAGE), h, 0,"),
+    ("key_row_reversed", "orc_attn_row(J, page, (int)(t % ORC_PAGE), h, 0,",
+     "orc_attn_row(J, page, (int)(15 - t % ORC_PAGE), h, 0,"),
     ("workspace_row_offset", "int64_t o = ((cu_rows[s] + t) * num_kv_heads + h) * ORC_D;",
      "int64_t o = ((cu_rows[s] + t) * num_kv_heads) * ORC_D;"),
     ("fp8_workspace_sign_dropped", "return (signbit(x) ? 0x80 : 0) | mag;", "return mag;"),
@@ -59,6 +60,14 @@ MUTANTS = [
     ("extend_bf16_workspace_read_as_fp8", "if (dtype == 1) return", "if (dtype == 3) return"),
     ("extend_chunk_head_ignored", "((t - J->prefix_len) * J->num_kv_heads + h) * ORC_D + d]",
      "((t - J->prefix_len) * J->num_kv_heads) * ORC_D + d]"),
+    ("fp8_v_rows_collapsed", "(d % 8) * 4 + row % 4;", "(d % 8) * 4;"),
+    ("fp8_code_sign_dropped", "(double)s);\n  return (signbit(x) ? 0x80 : 0) | mag;", "(double)s);\n  return mag;"),
+    ("fp8_scale_ignored_on_decode", "orc_fp8_byte_offset(kind, row, d)]) * (double)scale;",
+     "orc_fp8_byte_offset(kind, row, d)]);"),
+    ("fp8_k_scale_used_for_v", "orc_fp8_code(x, kind ? v_scale : k_scale)", "orc_fp8_code(x, k_scale)"),
+    ("fp8_attn_v_scale_for_k", "kind ? J->v_scale : J->k_scale", "J->v_scale"),
+    ("fp8_slab_kind_ignored", "((page * num_kv_heads + head) * 2 + kind) * (int64_t)ORC_FP8_SLAB",
+     "((page * num_kv_heads + head) * 2) * (int64_t)ORC_FP8_SLAB"),
     ("slab_kind_ignored", "return ((page * num_kv_heads + head) * 2 + kind) * (int64_t)ORC_SLAB;",
      "return ((page * num_kv_heads + head) * 2) * (int64_t)ORC_SLAB;"),
 ]
@@ -79,6 +88,10 @@ def _pins(o):
     yield lambda: TA.test_seq_len_one_returns_first_value_row(o)
     yield lambda: TE.test_first_chunk_query_without_prefix_sees_only_itself(o)
     yield lambda: TE.test_constant_keys_give_running_mean_of_values(o)
+    yield lambda: T8.test_fp8_layout_is_a_bijection(o)
+    yield lambda: T8.test_fp8_codes_vs_library_cast(o, 0.5)
+    yield lambda: T8.test_fp8_codes_saturate_and_keep_sign(o)
+    yield lambda: T8.test_fp8_round_trip_and_attention_vs_library_sdpa(o, 0.5, 2.0)
     for kind in TE.PRE_DTYPES:
         yield lambda kind=kind: TE.test_extend_vs_library_sdpa(o, kind, 37, 19, 8, 2)
 
