@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = batch 44 x 32K, the metric's workload)")
     ap.add_argument("--splits", type=int, default=-1, help="-1 = the workload's setting, else the library default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8-baseline", action="store_true",
+                    help="skip the FP8 E4M3 cache timed on the same workload and step")
     ap.add_argument("--cpu-sample-seqs", type=int, default=24)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="calibration only: time a plain device copy of this many bytes instead of the decode step "
@@ -101,6 +103,57 @@ def fill_pool(w, pool, B, W, torch, seqs=None, step=65536):
             slots = torch.as_tensor(W.slots(w, b, t0, t1), device="cuda")
             B.nvfp4_kv_quantize(k, v, slots, pool)
     torch.cuda.synchronize()
+
+
+def fp8_baseline(w, q, pt, sl, new_k, new_v, new_slots, splits, B, W, torch, steps, warmup, nvfp4_ms, nvfp4_k_ms):
+    """The same decode step over an FP8 E4M3 cache of the same K/V (the format the
+    pages compare NVFP4 against): quantize the new tokens, the split kernel, the
+    combine. Timed like the NVFP4 step: K steps with events only around the loop,
+    then K more with events around each split launch."""
+    pool8 = B.Fp8Pool(w.num_pages, w.num_kv_heads, device="cuda")
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        for t0 in range(0, L, 65536):
+            t1 = min(L, t0 + 65536)
+            k, v = W.kv(w, b, t0, t1, device="cuda")
+            B.fp8_kv_quantize(k, v, torch.as_tensor(W.slots(w, b, t0, t1), device="cuda"), pool8)
+    ws = torch.empty(B.nvfp4_paged_decode_attn_workspace_bytes(w.batch, w.num_q_heads, splits), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        B.fp8_kv_quantize(new_k, new_v, new_slots, pool8, stream=stream)
+        if evs:
+            evs[0].record(stream)
+        B.fp8_paged_decode_attn_partial(q, pt, sl, pool8, w.sm_scale, w.max_seq_len, splits, ws, stream=stream)
+        if evs:
+            evs[1].record(stream)
+        B.nvfp4_decode_combine(ws, w.batch, w.num_q_heads, splits, out, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        step(kev[i])
+    torch.cuda.synchronize()
+    k_ms = sum(a.elapsed_time(b) for a, b in kev) / steps
+    kv8 = int(w.seq_lens.astype("int64").sum()) * w.num_kv_heads * 2 * 128  # one byte per value
+    del pool8
+    return {"kv_bytes_per_step": kv8, "ms_per_step": round(ms, 5), "GBps": round(kv8 / (ms * 1e-3) / 1e9, 2),
+            "kernel": "k_decode_split_fp8", "kernel_ms": round(k_ms, 5),
+            "kernel_GBps": round(kv8 / (k_ms * 1e-3) / 1e9, 2),
+            "kernel_frac": round(kv8 / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "num_splits": splits,
+            "nvfp4_bytes_over_fp8": round(w.kv_bytes_per_step() / kv8, 4),
+            "nvfp4_step_speedup": round(ms / nvfp4_ms, 3), "nvfp4_kernel_speedup": round(k_ms / nvfp4_k_ms, 3)}
 
 
 def cpu_baseline(w, n_seqs, W, torch):
@@ -319,6 +372,9 @@ def main():
         "wall_s_timed": round(wall, 3),
         "pool_fill_s": round(t_fill, 2),
     }
+    if not args.no_fp8_baseline:
+        res["fp8_baseline"] = fp8_baseline(w, q, pt, sl, new_k, new_v, new_slots, splits, B, W, torch, args.steps,
+                                           args.warmup, ms, k_ms)
     if w.extend_prefix:
         res["extend"] = extend_step(w, pool, B, W, torch, max(3, args.steps // 5), 2)
     if not args.no_cpu_baseline:

@@ -34,12 +34,22 @@ EXPORTED = [
     "nvfp4_decode_combine",
     "nvfp4_kv_dequant_workspace",
     "nvfp4_extend_attn",
+    "fp8kv_pool_bytes",
+    "fp8_kv_quantize",
+    "fp8_paged_decode_attn_default_splits",
+    "fp8_paged_decode_attn",
+    "fp8_paged_decode_attn_partial",
 ]
 
 
 class PoolDesc(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("num_pages", ctypes.c_int64), ("num_kv_heads", ctypes.c_int32),
                 ("global_scale", ctypes.c_float)]
+
+
+class Fp8PoolDesc(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("num_pages", ctypes.c_int64), ("num_kv_heads", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -81,6 +91,19 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_extend_attn.argtypes = [P, P, P, c.c_int32, c.c_int64, P, P, c.c_int64, c.c_int32, c.c_int32,
                                         c.c_float, P, P, P]
         L.nvfp4_extend_attn.restype = c.c_int32
+        L.fp8kv_pool_bytes.argtypes = [c.c_int64, c.c_int32]
+        L.fp8kv_pool_bytes.restype = c.c_int64
+        L.fp8_kv_quantize.argtypes = [P, P, c.c_int32, c.c_int64, c.c_int64, P, c.c_int64, c.POINTER(Fp8PoolDesc), P]
+        L.fp8_kv_quantize.restype = c.c_int32
+        L.fp8_paged_decode_attn_default_splits.argtypes = [c.c_int32, c.c_int32, c.c_int32, c.c_int32]
+        L.fp8_paged_decode_attn_default_splits.restype = c.c_int32
+        L.fp8_paged_decode_attn.argtypes = [P, P, c.c_int64, P, c.c_int32, c.c_int32, c.c_int32,
+                                            c.POINTER(Fp8PoolDesc), c.c_float, c.c_int32, P, c.c_size_t, P,
+                                            c.c_int32, P, P]
+        L.fp8_paged_decode_attn.restype = c.c_int32
+        L.fp8_paged_decode_attn_partial.argtypes = [P, P, c.c_int64, P, c.c_int32, c.c_int32, c.c_int32,
+                                                    c.POINTER(Fp8PoolDesc), c.c_float, c.c_int32, P, c.c_size_t, P]
+        L.fp8_paged_decode_attn_partial.restype = c.c_int32
         _lib = L
     return _lib
 
@@ -124,13 +147,35 @@ class Pool:
         return PoolDesc(self.data.data_ptr(), self.num_pages, self.num_kv_heads, self.global_scale)
 
 
+class Fp8Pool:
+    """FP8 E4M3 baseline pool of one layer (layout in include/nvfp4kv.h)."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, device="cuda", k_scale: float = 1.0,
+                 v_scale: float = 1.0, data: torch.Tensor | None = None):
+        nbytes = fp8kv_pool_bytes(num_pages, num_kv_heads)
+        if data is None:
+            data = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        if data.numel() != nbytes or data.dtype != torch.uint8:
+            raise ValueError("pool buffer has the wrong size or dtype")
+        self.data = data
+        self.num_pages = int(num_pages)
+        self.num_kv_heads = int(num_kv_heads)
+        self.k_scale = float(k_scale)
+        self.v_scale = float(v_scale)
+
+    def desc(self) -> Fp8PoolDesc:
+        return Fp8PoolDesc(self.data.data_ptr(), self.num_pages, self.num_kv_heads, self.k_scale, self.v_scale)
+
+
+def fp8kv_pool_bytes(num_pages: int, num_kv_heads: int) -> int:
+    return int(lib().fp8kv_pool_bytes(int(num_pages), int(num_kv_heads)))
+
+
 def nvfp4kv_pool_bytes(num_pages: int, num_kv_heads: int) -> int:
     return int(lib().nvfp4kv_pool_bytes(int(num_pages), int(num_kv_heads)))
 
 
-def nvfp4_kv_quantize(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, pool: Pool, stream=None):
-    """k, v: [T, Hkv, 128] float32 or bfloat16 on the device (last dim contiguous);
-    slot_mapping: int32 [T] (negative = skip)."""
+def _quantize(name, k, v, slot_mapping, pool, stream):
     if k.dtype != v.dtype or k.shape != v.shape or k.stride() != v.stride():
         raise ValueError("k and v must share dtype, shape and strides")
     if k.dim() != 3 or k.shape[2] != HEAD_DIM or k.stride(2) != 1:
@@ -141,9 +186,19 @@ def nvfp4_kv_quantize(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tens
     if slot_mapping.dtype != torch.int32 or slot_mapping.numel() != k.shape[0]:
         raise ValueError("slot_mapping must be int32 [T]")
     d = pool.desc()
-    _check("nvfp4_kv_quantize", lib().nvfp4_kv_quantize(_ptr(k), _ptr(v), dt, k.stride(0), k.stride(1),
-                                                         _ptr(slot_mapping), k.shape[0], ctypes.byref(d),
-                                                         _stream(stream)))
+    _check(name, getattr(lib(), name)(_ptr(k), _ptr(v), dt, k.stride(0), k.stride(1), _ptr(slot_mapping), k.shape[0],
+                                      ctypes.byref(d), _stream(stream)))
+
+
+def fp8_kv_quantize(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, pool: Fp8Pool, stream=None):
+    """As nvfp4_kv_quantize, into an FP8 baseline pool."""
+    _quantize("fp8_kv_quantize", k, v, slot_mapping, pool, stream)
+
+
+def nvfp4_kv_quantize(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, pool: Pool, stream=None):
+    """k, v: [T, Hkv, 128] float32 or bfloat16 on the device (last dim contiguous);
+    slot_mapping: int32 [T] (negative = skip)."""
+    _quantize("nvfp4_kv_quantize", k, v, slot_mapping, pool, stream)
 
 
 def nvfp4_paged_decode_attn_default_splits(batch: int, num_kv_heads: int, max_seq_len: int, num_cus: int = 0) -> int:
@@ -255,3 +310,50 @@ def nvfp4_extend_attn(q: torch.Tensor, k_prefix: torch.Tensor, v_prefix: torch.T
                                    _ptr(k_chunk), _ptr(v_chunk), C, hq, hkv, float(sm_scale), _ptr(out), _ptr(lse),
                                    _stream(stream)))
     return out
+
+
+def fp8_paged_decode_attn_default_splits(batch: int, num_kv_heads: int, max_seq_len: int, num_cus: int = 0) -> int:
+    return int(lib().fp8_paged_decode_attn_default_splits(batch, num_kv_heads, max_seq_len, num_cus))
+
+
+def fp8_paged_decode_attn(q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor, pool: Fp8Pool,
+                          sm_scale: float, max_seq_len: int, num_splits: int = 0,
+                          workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                          out_dtype: torch.dtype = torch.bfloat16, lse: torch.Tensor | None = None, stream=None):
+    """As nvfp4_paged_decode_attn, over an FP8 baseline pool."""
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [B, Hq, 128] tensor")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_contiguous():
+        raise ValueError("page_table must be contiguous int32 [B, stride]")
+    B, hq, _ = q.shape
+    if num_splits == 0:
+        num_splits = fp8_paged_decode_attn_default_splits(B, pool.num_kv_heads, max_seq_len)
+    if workspace is None:
+        nbytes = nvfp4_paged_decode_attn_workspace_bytes(B, hq, num_splits)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    odt = {torch.float32: F32, torch.bfloat16: BF16}.get(out.dtype)
+    if odt is None or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 or bfloat16")
+    d = pool.desc()
+    _check("fp8_paged_decode_attn",
+           lib().fp8_paged_decode_attn(_ptr(q), _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, hq,
+                                       int(max_seq_len), ctypes.byref(d), float(sm_scale), int(num_splits),
+                                       _ptr(workspace), workspace.numel(), _ptr(out), odt, _ptr(lse),
+                                       _stream(stream)))
+    return out
+
+
+def fp8_paged_decode_attn_partial(q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor, pool: Fp8Pool,
+                                  sm_scale: float, max_seq_len: int, num_splits: int, workspace: torch.Tensor,
+                                  stream=None):
+    """Phase 1 over an FP8 baseline pool (phase 2 is nvfp4_decode_combine)."""
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [B, Hq, 128] tensor")
+    B, hq, _ = q.shape
+    d = pool.desc()
+    _check("fp8_paged_decode_attn_partial",
+           lib().fp8_paged_decode_attn_partial(_ptr(q), _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B,
+                                               hq, int(max_seq_len), ctypes.byref(d), float(sm_scale),
+                                               int(num_splits), _ptr(workspace), workspace.numel(), _stream(stream)))

@@ -32,6 +32,82 @@ int32_t check_pool(const nvfp4kv_pool* pool) {
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? NVFP4KV_OK : NVFP4KV_ERR_HIP; }
 
+int32_t check_fp8_pool(const fp8kv_pool* pool) {
+  if (!pool || !pool->data) return NVFP4KV_ERR_NULL;
+  if (pool->num_pages < 1 || pool->num_kv_heads < 1) return NVFP4KV_ERR_SHAPE;
+  if (pool->num_pages > ((int64_t)1 << 40) / ((int64_t)pool->num_kv_heads * 2 * FP8KV_SLAB_BYTES))
+    return NVFP4KV_ERR_SHAPE;
+  if (!aligned16(pool->data)) return NVFP4KV_ERR_ALIGN;
+  if (!valid_global_scale(pool->k_scale) || !valid_global_scale(pool->v_scale)) return NVFP4KV_ERR_VALUE;
+  return NVFP4KV_OK;
+}
+
+// What the kernels need of either pool (validated by check_pool / check_fp8_pool).
+struct PoolInfo {
+  void* data;
+  int32_t num_kv_heads;
+  float k_mul;  // NVFP4: g; FP8: k_scale
+  float v_mul;  // NVFP4: g; FP8: v_scale
+  bool fp8;
+};
+PoolInfo info_of(const nvfp4kv_pool* p) {
+  return PoolInfo{p->data, p->num_kv_heads, p->global_scale, p->global_scale, false};
+}
+PoolInfo info_of(const fp8kv_pool* p) { return PoolInfo{p->data, p->num_kv_heads, p->k_scale, p->v_scale, true}; }
+
+int32_t quantize_into(const void* k_src, const void* v_src, int32_t src_dtype, int64_t token_stride,
+                      int64_t head_stride, const int32_t* slot_mapping, int64_t num_tokens, const PoolInfo& pool,
+                      void* stream) {
+  if (src_dtype != NVFP4KV_F32 && src_dtype != NVFP4KV_BF16) return NVFP4KV_ERR_DTYPE;
+  if (num_tokens < 0 || token_stride < 0 || head_stride < 0) return NVFP4KV_ERR_SHAPE;
+  if (num_tokens == 0) return NVFP4KV_OK;
+  if (!k_src || !v_src || !slot_mapping) return NVFP4KV_ERR_NULL;
+  if (num_tokens > ((int64_t)1 << 31) * 256 / ((int64_t)pool.num_kv_heads * 16)) return NVFP4KV_ERR_SHAPE;
+  const int64_t vec = src_dtype == NVFP4KV_F32 ? 4 : 8;  // elements per 16 bytes
+  if (!aligned16(k_src) || !aligned16(v_src) || token_stride % vec || head_stride % vec ||
+      (reinterpret_cast<uintptr_t>(slot_mapping) & 3u))
+    return NVFP4KV_ERR_ALIGN;
+  nvfp4kv::QuantizeArgs a;
+  a.k = k_src;
+  a.v = v_src;
+  a.bf16 = src_dtype == NVFP4KV_BF16;
+  a.token_stride = token_stride;
+  a.head_stride = head_stride;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.pool = static_cast<uint8_t*>(pool.data);
+  a.num_kv_heads = pool.num_kv_heads;
+  a.g = pool.k_mul;
+  a.fp8 = pool.fp8;
+  a.inv_k_scale = 1.0f / pool.k_mul;  // powers of two: exact
+  a.inv_v_scale = 1.0f / pool.v_mul;
+  return hip_status(nvfp4kv::launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t default_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len, int32_t num_cus, bool fp8) {
+  if (batch < 1 || num_kv_heads < 1 || max_seq_len < 1) return 1;
+  if (num_cus <= 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    num_cus = cus;
+  }
+  const int64_t pages = (max_seq_len + NVFP4KV_PAGE_SIZE - 1) / NVFP4KV_PAGE_SIZE;
+  const int64_t segments = (int64_t)batch * num_kv_heads;
+  // Splits are the grain at which the persistent workgroups' page windows are
+  // cut: about 16 splits per window keeps the windows within about 6% of each
+  // other. Consecutive splits in one window share one state, so more splits do
+  // not mean more partial-state writes. At least 4 pages per split.
+  const int64_t windows = nvfp4kv::decode_resident_workgroups(num_cus, fp8);
+  int64_t s = (16 * windows + segments - 1) / segments;
+  const int64_t max_by_pages = pages / 4 > 1 ? pages / 4 : 1;
+  if (s > max_by_pages) s = max_by_pages;
+  if (s > NVFP4KV_MAX_SPLITS) s = NVFP4KV_MAX_SPLITS;
+  if (s < 1) s = 1;
+  return (int32_t)s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -61,52 +137,31 @@ int32_t nvfp4_kv_quantize(const void* k_src, const void* v_src, int32_t src_dtyp
                           int64_t head_stride, const int32_t* slot_mapping, int64_t num_tokens,
                           const nvfp4kv_pool* pool, void* stream) {
   if (int32_t e = check_pool(pool)) return e;
-  if (src_dtype != NVFP4KV_F32 && src_dtype != NVFP4KV_BF16) return NVFP4KV_ERR_DTYPE;
-  if (num_tokens < 0 || token_stride < 0 || head_stride < 0) return NVFP4KV_ERR_SHAPE;
-  if (num_tokens == 0) return NVFP4KV_OK;
-  if (!k_src || !v_src || !slot_mapping) return NVFP4KV_ERR_NULL;
-  if (num_tokens > ((int64_t)1 << 31) * 256 / ((int64_t)pool->num_kv_heads * 16)) return NVFP4KV_ERR_SHAPE;
-  const int64_t vec = src_dtype == NVFP4KV_F32 ? 4 : 8;  // elements per 16 bytes
-  if (!aligned16(k_src) || !aligned16(v_src) || token_stride % vec || head_stride % vec ||
-      (reinterpret_cast<uintptr_t>(slot_mapping) & 3u))
-    return NVFP4KV_ERR_ALIGN;
-  nvfp4kv::QuantizeArgs a;
-  a.k = k_src;
-  a.v = v_src;
-  a.bf16 = src_dtype == NVFP4KV_BF16;
-  a.token_stride = token_stride;
-  a.head_stride = head_stride;
-  a.slots = slot_mapping;
-  a.num_tokens = num_tokens;
-  a.pool = static_cast<uint8_t*>(pool->data);
-  a.num_kv_heads = pool->num_kv_heads;
-  a.g = pool->global_scale;
-  return hip_status(nvfp4kv::launch_quantize(a, static_cast<hipStream_t>(stream)));
+  return quantize_into(k_src, v_src, src_dtype, token_stride, head_stride, slot_mapping, num_tokens, info_of(pool),
+                       stream);
+}
+
+int64_t fp8kv_pool_bytes(int64_t num_pages, int32_t num_kv_heads) {
+  if (num_pages < 0 || num_kv_heads < 0) return 0;
+  return num_pages * num_kv_heads * 2 * (int64_t)FP8KV_SLAB_BYTES;
+}
+
+int32_t fp8_kv_quantize(const void* k_src, const void* v_src, int32_t src_dtype, int64_t token_stride,
+                        int64_t head_stride, const int32_t* slot_mapping, int64_t num_tokens, const fp8kv_pool* pool,
+                        void* stream) {
+  if (int32_t e = check_fp8_pool(pool)) return e;
+  return quantize_into(k_src, v_src, src_dtype, token_stride, head_stride, slot_mapping, num_tokens, info_of(pool),
+                       stream);
 }
 
 int32_t nvfp4_paged_decode_attn_default_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
                                                int32_t num_cus) {
-  if (batch < 1 || num_kv_heads < 1 || max_seq_len < 1) return 1;
-  if (num_cus <= 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    num_cus = cus;
-  }
-  const int64_t pages = (max_seq_len + NVFP4KV_PAGE_SIZE - 1) / NVFP4KV_PAGE_SIZE;
-  const int64_t segments = (int64_t)batch * num_kv_heads;
-  // Splits are the grain at which the persistent workgroups' page windows are
-  // cut: about 16 splits per window keeps the windows within about 6% of each
-  // other. Consecutive splits in one window share one state, so more splits do
-  // not mean more partial-state writes. At least 4 pages per split.
-  const int64_t windows = nvfp4kv::decode_resident_workgroups(num_cus);
-  int64_t s = (16 * windows + segments - 1) / segments;
-  const int64_t max_by_pages = pages / 4 > 1 ? pages / 4 : 1;
-  if (s > max_by_pages) s = max_by_pages;
-  if (s > NVFP4KV_MAX_SPLITS) s = NVFP4KV_MAX_SPLITS;
-  if (s < 1) s = 1;
-  return (int32_t)s;
+  return default_splits(batch, num_kv_heads, max_seq_len, num_cus, false);
+}
+
+int32_t fp8_paged_decode_attn_default_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
+                                             int32_t num_cus) {
+  return default_splits(batch, num_kv_heads, max_seq_len, num_cus, true);
 }
 
 size_t nvfp4_paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_splits) {
@@ -133,18 +188,17 @@ int32_t finish_decode(nvfp4kv::DecodeArgs& a) {
   if (a.num_workgroups > 0) return NVFP4KV_OK;
   int cus = 0;
   if (!query_cus(&cus)) return NVFP4KV_ERR_HIP;
-  a.num_workgroups = nvfp4kv::decode_resident_workgroups(cus);
+  a.num_workgroups = nvfp4kv::decode_resident_workgroups(cus, a.fp8 != 0);
   return NVFP4KV_OK;
 }
 
 // Shared validation of the decode phases; fills `a` (without out/lse).
 int32_t prepare_decode(const void* q, const int32_t* page_table, int64_t page_table_stride, const int32_t* seq_lens,
-                       int32_t batch, int32_t num_q_heads, int32_t max_seq_len, const nvfp4kv_pool* pool,
+                       int32_t batch, int32_t num_q_heads, int32_t max_seq_len, const PoolInfo& pool,
                        float sm_scale, int32_t* num_splits, void* workspace, size_t workspace_bytes,
                        nvfp4kv::DecodeArgs& a) {
-  if (int32_t e = check_pool(pool)) return e;
   if (batch < 0 || num_q_heads < 1 || max_seq_len < 0 || page_table_stride < 1) return NVFP4KV_ERR_SHAPE;
-  const int32_t hkv = pool->num_kv_heads;
+  const int32_t hkv = pool.num_kv_heads;
   if (num_q_heads % hkv != 0) return NVFP4KV_ERR_SHAPE;
   const int32_t group = num_q_heads / hkv;
   if (group < 1 || group > NVFP4KV_MAX_GROUP) return NVFP4KV_ERR_SHAPE;
@@ -161,7 +215,7 @@ int32_t prepare_decode(const void* q, const int32_t* page_table, int64_t page_ta
   int cus = 0;
   if (*num_splits == 0) {
     if (!query_cus(&cus)) return NVFP4KV_ERR_HIP;
-    *num_splits = nvfp4_paged_decode_attn_default_splits(batch, hkv, max_seq_len, cus);
+    *num_splits = default_splits(batch, hkv, max_seq_len, cus, pool.fp8);
   }
   const size_t need = nvfp4_paged_decode_attn_workspace_bytes(batch, num_q_heads, *num_splits);
   if (need == 0 || workspace_bytes < need) return NVFP4KV_ERR_WORKSPACE;
@@ -174,11 +228,12 @@ int32_t prepare_decode(const void* q, const int32_t* page_table, int64_t page_ta
   a.num_kv_heads = hkv;
   a.group = group;
   a.max_seq_len = max_seq_len;
-  a.pool = static_cast<const uint8_t*>(pool->data);
-  a.qk_scale_log2 = (float)((double)sm_scale * 1.4426950408889634 * (double)pool->global_scale);
-  a.v_scale = pool->global_scale;
+  a.pool = static_cast<const uint8_t*>(pool.data);
+  a.qk_scale_log2 = (float)((double)sm_scale * 1.4426950408889634 * (double)pool.k_mul);
+  a.v_scale = pool.v_mul;
+  a.fp8 = pool.fp8;
   a.num_splits = *num_splits;
-  a.num_workgroups = cus > 0 ? nvfp4kv::decode_resident_workgroups(cus) : 0;  // 0: finish_decode sets it
+  a.num_workgroups = cus > 0 ? nvfp4kv::decode_resident_workgroups(cus, pool.fp8) : 0;  // 0: finish_decode sets it
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = a.part_o + (size_t)batch * num_q_heads * *num_splits * NVFP4KV_HEAD_DIM;
   a.out = nullptr;
@@ -209,14 +264,10 @@ int32_t prepare_combine(const void* workspace, size_t workspace_bytes, int32_t b
   return NVFP4KV_OK;
 }
 
-}  // namespace
 
-extern "C" {
-
-int32_t nvfp4_paged_decode_attn_partial(const void* q, const int32_t* page_table, int64_t page_table_stride,
-                                        const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
-                                        int32_t max_seq_len, const nvfp4kv_pool* pool, float sm_scale,
-                                        int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+int32_t decode_partial(const void* q, const int32_t* page_table, int64_t page_table_stride, const int32_t* seq_lens,
+                       int32_t batch, int32_t num_q_heads, int32_t max_seq_len, const PoolInfo& pool, float sm_scale,
+                       int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   if (num_splits < 1) return NVFP4KV_ERR_SHAPE;  // the caller sizes the workspace for a known count
   nvfp4kv::DecodeArgs a;
   if (int32_t e = prepare_decode(q, page_table, page_table_stride, seq_lens, batch, num_q_heads, max_seq_len, pool,
@@ -227,24 +278,12 @@ int32_t nvfp4_paged_decode_attn_partial(const void* q, const int32_t* page_table
   return hip_status(nvfp4kv::launch_decode_partial(a, static_cast<hipStream_t>(stream)));
 }
 
-int32_t nvfp4_decode_combine(const void* workspace, size_t workspace_bytes, int32_t batch, int32_t num_q_heads,
-                             int32_t num_splits, void* out, int32_t out_dtype, float* lse, void* stream) {
+int32_t decode_full(const void* q, const int32_t* page_table, int64_t page_table_stride, const int32_t* seq_lens,
+                    int32_t batch, int32_t num_q_heads, int32_t max_seq_len, const PoolInfo& pool, float sm_scale,
+                    int32_t num_splits, void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
+                    float* lse, void* stream) {
   nvfp4kv::DecodeArgs a;
-  if (int32_t e = prepare_combine(workspace, workspace_bytes, batch, num_q_heads, num_splits, out, out_dtype, lse, a))
-    return e;
-  if (batch == 0) return NVFP4KV_OK;
-  return hip_status(nvfp4kv::launch_decode_combine(a, static_cast<hipStream_t>(stream)));
-}
-
-int32_t nvfp4_paged_decode_attn(const void* q, const int32_t* page_table, int64_t page_table_stride,
-                                const int32_t* seq_lens, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
-                                const nvfp4kv_pool* pool, float sm_scale, int32_t num_splits, void* workspace,
-                                size_t workspace_bytes, void* out, int32_t out_dtype, float* lse, void* stream) {
-  nvfp4kv::DecodeArgs a;
-  if (out_dtype != NVFP4KV_F32 && out_dtype != NVFP4KV_BF16) {
-    if (int32_t e = check_pool(pool)) return e;
-    return NVFP4KV_ERR_DTYPE;
-  }
+  if (out_dtype != NVFP4KV_F32 && out_dtype != NVFP4KV_BF16) return NVFP4KV_ERR_DTYPE;
   if (int32_t e = prepare_decode(q, page_table, page_table_stride, seq_lens, batch, num_q_heads, max_seq_len, pool,
                                  sm_scale, &num_splits, workspace, workspace_bytes, a))
     return e;
@@ -257,6 +296,56 @@ int32_t nvfp4_paged_decode_attn(const void* q, const int32_t* page_table, int64_
   if (int32_t e = hip_status(nvfp4kv::launch_decode_partial(a, st))) return e;
   return hip_status(nvfp4kv::launch_decode_combine(c, st));
 }
+
+}  // namespace
+
+extern "C" {
+
+int32_t nvfp4_paged_decode_attn_partial(const void* q, const int32_t* page_table, int64_t page_table_stride,
+                                        const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                        int32_t max_seq_len, const nvfp4kv_pool* pool, float sm_scale,
+                                        int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int32_t e = check_pool(pool)) return e;
+  return decode_partial(q, page_table, page_table_stride, seq_lens, batch, num_q_heads, max_seq_len, info_of(pool),
+                        sm_scale, num_splits, workspace, workspace_bytes, stream);
+}
+
+int32_t nvfp4_paged_decode_attn(const void* q, const int32_t* page_table, int64_t page_table_stride,
+                                const int32_t* seq_lens, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
+                                const nvfp4kv_pool* pool, float sm_scale, int32_t num_splits, void* workspace,
+                                size_t workspace_bytes, void* out, int32_t out_dtype, float* lse, void* stream) {
+  if (int32_t e = check_pool(pool)) return e;
+  return decode_full(q, page_table, page_table_stride, seq_lens, batch, num_q_heads, max_seq_len, info_of(pool),
+                     sm_scale, num_splits, workspace, workspace_bytes, out, out_dtype, lse, stream);
+}
+
+int32_t fp8_paged_decode_attn_partial(const void* q, const int32_t* page_table, int64_t page_table_stride,
+                                      const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                      int32_t max_seq_len, const fp8kv_pool* pool, float sm_scale,
+                                      int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int32_t e = check_fp8_pool(pool)) return e;
+  return decode_partial(q, page_table, page_table_stride, seq_lens, batch, num_q_heads, max_seq_len, info_of(pool),
+                        sm_scale, num_splits, workspace, workspace_bytes, stream);
+}
+
+int32_t fp8_paged_decode_attn(const void* q, const int32_t* page_table, int64_t page_table_stride,
+                              const int32_t* seq_lens, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
+                              const fp8kv_pool* pool, float sm_scale, int32_t num_splits, void* workspace,
+                              size_t workspace_bytes, void* out, int32_t out_dtype, float* lse, void* stream) {
+  if (int32_t e = check_fp8_pool(pool)) return e;
+  return decode_full(q, page_table, page_table_stride, seq_lens, batch, num_q_heads, max_seq_len, info_of(pool),
+                     sm_scale, num_splits, workspace, workspace_bytes, out, out_dtype, lse, stream);
+}
+
+int32_t nvfp4_decode_combine(const void* workspace, size_t workspace_bytes, int32_t batch, int32_t num_q_heads,
+                             int32_t num_splits, void* out, int32_t out_dtype, float* lse, void* stream) {
+  nvfp4kv::DecodeArgs a;
+  if (int32_t e = prepare_combine(workspace, workspace_bytes, batch, num_q_heads, num_splits, out, out_dtype, lse, a))
+    return e;
+  if (batch == 0) return NVFP4KV_OK;
+  return hip_status(nvfp4kv::launch_decode_combine(a, static_cast<hipStream_t>(stream)));
+}
+
 
 int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page_table, int64_t page_table_stride,
                                    const int32_t* seq_lens, const int64_t* row_offsets, int32_t n_seqs,

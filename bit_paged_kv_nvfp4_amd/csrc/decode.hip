@@ -43,56 +43,13 @@ constexpr float kLazyRescaleLog2 = 8.0f;
 
 __device__ __forceinline__ f16x2 pk_mul(uint32_t a, uint32_t b) { return as_f16x2(a) * as_f16x2(b); }
 
-struct PageRegs {
-  uint4 kc;     // K codes: 32 channels of one token
-  uint32_t ks;  // its two K scale bytes
-  uint4 vc;     // V codes: 8 channels (one half block) x 4 tokens
-  uint32_t vs;  // the block's scale bytes of those 4 tokens
-};
-
-// LDS ring of pages, per wave. A slot holds one (page, head) K+V slab pair as
-// the lanes will consume it: [K code chunk of lane 0..63 | V code chunk of lane
-// 0..63 | 128 K scale bytes | 128 V scale bytes].
-constexpr int kSlotBytes = 2 * kSlab;  // 2304
-#ifndef NVFP4KV_DECODE_WAVES
-#define NVFP4KV_DECODE_WAVES 4
-#endif
 #ifndef NVFP4KV_DECODE_PAIRS_AHEAD
 #define NVFP4KV_DECODE_PAIRS_AHEAD 1
 #endif
 constexpr int kPairsAhead = NVFP4KV_DECODE_PAIRS_AHEAD;  // pairs of pages in flight while one is computed
 constexpr int kRing = 2 * (kPairsAhead + 1);              // LDS slots (pages) per wave
-// Waves per workgroup. The workgroup owns one split; each wave takes a contiguous
-// quarter (for 4 waves) of its pages with its own LDS region, and the last wave
-// to finish merges the waves' online-softmax states in LDS, so a split writes
-// one partial state. Partial states are the only HBM writes of the kernel, and
-// written mid-stream they cost far more read bandwidth than their size.
-constexpr int kWaves = NVFP4KV_DECODE_WAVES;
-constexpr int kDmaPerPage = 3;
 constexpr int kQDmas = 4;  // 1 KB copies of the group's queries (up to 16 heads x 256 B)
 static_assert(kRing >= 4, "the query staging area takes the ring's last two slots");
-static_assert(kRing * kSlotBytes >= 8 * 64 * 16 + 16 * 8, "a wave's state must fit its ring region");
-
-struct DmaOffsets {
-  uint32_t k, v, s;  // per-lane source offsets inside a (page, head) K+V slab pair
-};
-
-__device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
-  const int n = lane & 15, G = lane >> 4;
-  DmaOffsets o;
-  o.k = n * 64 + G * 16;                          // 32 K channels of token n
-  o.v = kSlab + 16 * lane;                        // V chunk: channels 8n..8n+7, tokens 4G..4G+3
-  o.s = lane < 8 ? kCodeBytes + 16 * lane         // lanes 0..7: K scale bytes
-                 : kSlab + kCodeBytes + 16 * (lane - 8);  // lanes 8..15: V scale bytes
-  return o;
-}
-
-// Issue the copies of one (page, head) slab pair into an LDS slot (3 vmcnt events).
-__device__ __forceinline__ void issue_page(const uint8_t* slab, const DmaOffsets& o, uint32_t slot, int lane) {
-  dma16(slab, o.k, slot);
-  dma16(slab, o.v, slot + kCodeBytes);
-  if (lane < 16) dma16(slab, o.s, slot + 2 * kCodeBytes);
-}
 
 // Page ids reach the wave the same way as page bytes: 64 at a time, copied into
 // one of two LDS id buffers one chunk ahead of use. When the issue pointer enters
@@ -114,15 +71,6 @@ __device__ __forceinline__ const uint8_t* slab_of(const uint8_t* pool_h, int ids
   return pool_h + (int64_t)pid * page_bytes;
 }
 
-__device__ __forceinline__ PageRegs read_page(const uint8_t* slot, int lane) {
-  const int n = lane & 15, G = lane >> 4;
-  PageRegs r;
-  r.kc = *reinterpret_cast<const uint4*>(slot + 16 * lane);
-  r.vc = *reinterpret_cast<const uint4*>(slot + kCodeBytes + 16 * lane);
-  r.ks = *reinterpret_cast<const uint16_t*>(slot + 2 * kCodeBytes + n * 8 + G * 2);
-  r.vs = *reinterpret_cast<const uint32_t*>(slot + 2 * kCodeBytes + 128 + (n >> 1) * 16 + G * 4);
-  return r;
-}
 
 // K^ rows of one MFMA step: channels 32G + 8s .. +7 of the lane's token, exact f16
 // (E2M1 code times E4M3 scale / 256).
@@ -167,28 +115,203 @@ __device__ __forceinline__ void pv_tile(const uint4& va, const uint4& vb, uint32
   acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, pf, acc, 0, 0, 0);
 }
 
-// Two pages (32 tokens) per step: S^T = K^ Q^T for each page (two independent
-// MFMA chains), one online-softmax update over the 32 tokens, and O^T += V^T P^T
-// with the 32 tokens as the MFMA reduction (k slots 8G..8G+7 = page A tokens
-// 4G+0, +2, +1, +3, then the same of page B). Tokens at or past `lim` (the end of
-// the split or of the sequence) are masked.
-__device__ __forceinline__ void pair_step(const PageRegs& ra, const PageRegs& rb, int tok_a, int lim, int G,
-                                          const f16x8 (&qf)[4], float c, float& m_ref, float& lsum,
-                                          f32x4 (&acc)[8]) {
-  // ---- S^T = K^ Q^T ----
-  // scale bytes of finite E4M3 values are <= 0x7E; bit 7 is dropped so that even
-  // bytes of never-written (masked) rows decode to finite values
-  const uint32_t ska0 = k_scale_pair<0>(ra.ks), ska1 = k_scale_pair<1>(ra.ks);
-  const uint32_t skb0 = k_scale_pair<0>(rb.ks), skb1 = k_scale_pair<1>(rb.ks);
-  const uint32_t kwa[4] = {ra.kc.x, ra.kc.y, ra.kc.z, ra.kc.w};
-  const uint32_t kwb[4] = {rb.kc.x, rb.kc.y, rb.kc.z, rb.kc.w};
-  f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(kwa[s], s < 2 ? ska0 : ska1), qf[s], sa, 0, 0, 0);
-    sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(kwb[s], s < 2 ? skb0 : skb1), qf[s], sb, 0, 0, 0);
+// ---- page formats ----------------------------------------------------------
+// A format says how one (page, KV head) K+V slab pair travels: its bytes in the
+// pool, the per-lane copies into an LDS slot, the registers a lane takes from
+// the slot, and the two products of a pair of pages. Lane (n = lane % 16,
+// G = lane / 16) computes S^T rows = tokens 4G..4G+3 of both pages for head n,
+// and the PV products take channel 8n + q as row n of output tile q.
+
+// NVFP4 pages. An LDS slot holds [K code chunk of lane 0..63 | V code chunk of
+// lane 0..63 | 128 K scale bytes | 128 V scale bytes].
+struct Nvfp4Page {
+  static constexpr int kSlotBytes = 2 * kSlab;  // 2304
+  static constexpr int kHeadBytes = 2 * kSlab;  // pool bytes of one (page, head)
+  static constexpr int kDmaPerPage = 3;
+  static constexpr int kScaleLog2 = 8;          // K and V operands carry E4M3 scale / 256
+  // Four workgroups of four waves per CU: LDS (under 40 KB per workgroup of the
+  // CU's 160 KB) and registers (at most 128 VGPRs, four waves per SIMD).
+  static constexpr int kWaves = 4;
+  static constexpr int kWorkgroupsPerCu = 4;
+
+  struct Offsets {
+    uint32_t k, v, s;  // per-lane source offsets inside a (page, head) K+V slab pair
+  };
+  struct Regs {
+    uint4 kc;     // K codes: 32 channels of one token
+    uint32_t ks;  // its two K scale bytes
+    uint4 vc;     // V codes: 8 channels (one half block) x 4 tokens
+    uint32_t vs;  // the block's scale bytes of those 4 tokens
+  };
+
+  __device__ static __forceinline__ Offsets offsets(int lane) {
+    const int n = lane & 15, G = lane >> 4;
+    Offsets o;
+    o.k = n * 64 + G * 16;                          // 32 K channels of token n
+    o.v = kSlab + 16 * lane;                        // V chunk: channels 8n..8n+7, tokens 4G..4G+3
+    o.s = lane < 8 ? kCodeBytes + 16 * lane         // lanes 0..7: K scale bytes
+                   : kSlab + kCodeBytes + 16 * (lane - 8);  // lanes 8..15: V scale bytes
+    return o;
   }
 
+  // The copies of one (page, head) slab pair into an LDS slot (3 vmcnt events).
+  __device__ static __forceinline__ void issue(const uint8_t* slab, const Offsets& o, uint32_t slot, int lane) {
+    dma16(slab, o.k, slot);
+    dma16(slab, o.v, slot + kCodeBytes);
+    if (lane < 16) dma16(slab, o.s, slot + 2 * kCodeBytes);
+  }
+
+  __device__ static __forceinline__ Regs read(const uint8_t* slot, int lane) {
+    const int n = lane & 15, G = lane >> 4;
+    Regs r;
+    r.kc = *reinterpret_cast<const uint4*>(slot + 16 * lane);
+    r.vc = *reinterpret_cast<const uint4*>(slot + kCodeBytes + 16 * lane);
+    r.ks = *reinterpret_cast<const uint16_t*>(slot + 2 * kCodeBytes + n * 8 + G * 2);
+    r.vs = *reinterpret_cast<const uint32_t*>(slot + 2 * kCodeBytes + 128 + (n >> 1) * 16 + G * 4);
+    return r;
+  }
+
+  // S^T = K^ Q^T for each page (two independent MFMA chains).
+  __device__ static __forceinline__ void scores(const Regs& ra, const Regs& rb, const f16x8 (&qf)[4], f32x4& sa,
+                                                f32x4& sb) {
+    // scale bytes of finite E4M3 values are <= 0x7E; bit 7 is dropped so that even
+    // bytes of never-written (masked) rows decode to finite values
+    const uint32_t ska0 = k_scale_pair<0>(ra.ks), ska1 = k_scale_pair<1>(ra.ks);
+    const uint32_t skb0 = k_scale_pair<0>(rb.ks), skb1 = k_scale_pair<1>(rb.ks);
+    const uint32_t kwa[4] = {ra.kc.x, ra.kc.y, ra.kc.z, ra.kc.w};
+    const uint32_t kwb[4] = {rb.kc.x, rb.kc.y, rb.kc.z, rb.kc.w};
+    sa = f32x4{0.f, 0.f, 0.f, 0.f};
+    sb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(kwa[s], s < 2 ? ska0 : ska1), qf[s], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(kwb[s], s < 2 ? skb0 : skb1), qf[s], sb, 0, 0, 0);
+    }
+  }
+
+  // O^T += V^T P^T with the 32 tokens as the MFMA reduction: k slots 8G..8G+7 =
+  // page A tokens 4G+0, +2, +1, +3, then the same of page B (two codes of one
+  // channel share a V code byte: rows 4G+0 | 4G+2 and 4G+1 | 4G+3).
+  __device__ static __forceinline__ void pv(const Regs& ra, const Regs& rb, const float (&p)[8], f32x4 (&acc)[8]) {
+    const f16x8 pf = {(_Float16)p[0], (_Float16)p[2], (_Float16)p[1], (_Float16)p[3],
+                      (_Float16)p[4], (_Float16)p[6], (_Float16)p[5], (_Float16)p[7]};
+    const uint32_t sa02 = v_scales02(ra.vs), sa13 = v_scales13(ra.vs);
+    const uint32_t sb02 = v_scales02(rb.vs), sb13 = v_scales13(rb.vs);
+    pv_tile<0>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[0]);
+    pv_tile<1>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[1]);
+    pv_tile<2>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[2]);
+    pv_tile<3>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[3]);
+    pv_tile<4>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[4]);
+    pv_tile<5>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[5]);
+    pv_tile<6>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[6]);
+    pv_tile<7>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[7]);
+  }
+};
+
+// FP8 E4M3 pages, the baseline the pages compare against (one byte per value,
+// per-tensor scales folded into the softmax scale and the output). Pool slab
+// pair of one (page, head): K [16 rows][128 channels], then V as 64 chunks of
+// 32 B, chunk 16g + n = channels 8n..8n+7 of rows 4g..4g+3, word q = rows
+// 4g..4g+3 of channel 8n + q. An LDS slot holds [K channels 32G..32G+15 of
+// token n, lane 0..63 | K channels 32G+16..32G+31 | V chunk words 0..3 | V chunk
+// words 4..7], 1 KB each.
+struct Fp8Page {
+  static constexpr int kSlabBytes = 2048;
+  static constexpr int kSlotBytes = 2 * kSlabBytes;
+  static constexpr int kHeadBytes = 2 * kSlabBytes;
+  static constexpr int kDmaPerPage = 4;
+  static constexpr int kScaleLog2 = 0;
+  // Twice the slot of an NVFP4 page: two waves per workgroup keep a workgroup's
+  // LDS at 34 KB, and four workgroups per CU give the same 8 waves' worth of
+  // pages in flight per CU in bytes (VGPRs up to 256, two waves per SIMD).
+  static constexpr int kWaves = 2;
+  static constexpr int kWorkgroupsPerCu = 4;
+
+  struct Offsets {
+    uint32_t k, v;
+  };
+  struct Regs {
+    uint4 k0, k1;  // K channels 32G..32G+15 and 32G+16..32G+31 of token n
+    uint4 v0, v1;  // V chunk (G, n): words 0..3 and 4..7
+  };
+
+  __device__ static __forceinline__ Offsets offsets(int lane) {
+    const int n = lane & 15, G = lane >> 4;
+    Offsets o;
+    o.k = n * 128 + G * 32;
+    o.v = kSlabBytes + 32 * lane;
+    return o;
+  }
+
+  __device__ static __forceinline__ void issue(const uint8_t* slab, const Offsets& o, uint32_t slot, int) {
+    dma16(slab, o.k, slot);
+    dma16(slab, o.k + 16, slot + 1024);
+    dma16(slab, o.v, slot + 2048);
+    dma16(slab, o.v + 16, slot + 3072);
+  }
+
+  __device__ static __forceinline__ Regs read(const uint8_t* slot, int lane) {
+    Regs r;
+    r.k0 = *reinterpret_cast<const uint4*>(slot + 16 * lane);
+    r.k1 = *reinterpret_cast<const uint4*>(slot + 1024 + 16 * lane);
+    r.v0 = *reinterpret_cast<const uint4*>(slot + 2048 + 16 * lane);
+    r.v1 = *reinterpret_cast<const uint4*>(slot + 3072 + 16 * lane);
+    return r;
+  }
+
+  // Four E4M3 bytes of w as exact f16 (the converter's scale operand stays 1.0).
+  __device__ static __forceinline__ void f16x4_of(uint32_t w, f16x2& lo, f16x2& hi) {
+    lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  }
+  // K rows of MFMA step s: channels 32G + 8s .. +7 of the lane's token.
+  __device__ static __forceinline__ f16x8 k_op(uint32_t w0, uint32_t w1) {
+    f16x2 a, b, c, d;
+    f16x4_of(w0, a, b);
+    f16x4_of(w1, c, d);
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  }
+
+  __device__ static __forceinline__ void scores(const Regs& ra, const Regs& rb, const f16x8 (&qf)[4], f32x4& sa,
+                                                f32x4& sb) {
+    const uint32_t ka[8] = {ra.k0.x, ra.k0.y, ra.k0.z, ra.k0.w, ra.k1.x, ra.k1.y, ra.k1.z, ra.k1.w};
+    const uint32_t kb[8] = {rb.k0.x, rb.k0.y, rb.k0.z, rb.k0.w, rb.k1.x, rb.k1.y, rb.k1.z, rb.k1.w};
+    sa = f32x4{0.f, 0.f, 0.f, 0.f};
+    sb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_op(ka[2 * s], ka[2 * s + 1]), qf[s], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_op(kb[2 * s], kb[2 * s + 1]), qf[s], sb, 0, 0, 0);
+    }
+  }
+
+  // k slots 8G..8G+7 = page A tokens 4G..4G+3, then page B's; tile q takes word q
+  // of each page's chunk (tokens 4G..4G+3 of channel 8n + q).
+  __device__ static __forceinline__ void pv(const Regs& ra, const Regs& rb, const float (&p)[8], f32x4 (&acc)[8]) {
+    const f16x8 pf = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
+                      (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
+    const uint32_t va[8] = {ra.v0.x, ra.v0.y, ra.v0.z, ra.v0.w, ra.v1.x, ra.v1.y, ra.v1.z, ra.v1.w};
+    const uint32_t vb[8] = {rb.v0.x, rb.v0.y, rb.v0.z, rb.v0.w, rb.v1.x, rb.v1.y, rb.v1.z, rb.v1.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      f16x2 a0, a1, b0, b1;
+      f16x4_of(va[q], a0, a1);
+      f16x4_of(vb[q], b0, b1);
+      const f16x8 v = {a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, pf, acc[q], 0, 0, 0);
+    }
+  }
+};
+
+// Two pages (32 tokens) per step: the format's S^T products, one online-softmax
+// update over the 32 tokens, and the format's PV products. Tokens at or past
+// `lim` (the end of the split or of the sequence) are masked.
+template <class F>
+__device__ __forceinline__ void pair_step(const typename F::Regs& ra, const typename F::Regs& rb, int tok_a, int lim,
+                                          int G, const f16x8 (&qf)[4], float c, float& m_ref, float& lsum,
+                                          f32x4 (&acc)[8]) {
+  f32x4 sa, sb;
+  F::scores(ra, rb, qf, sa, sb);
 
   // ---- online softmax (base 2) over tokens 4G..4G+3 of both pages, head n ----
   // Logits are z = s * c with c > 0 (the query sign absorbs the sign of the
@@ -233,20 +356,7 @@ __device__ __forceinline__ void pair_step(const PageRegs& ra, const PageRegs& rb
     }
   }
   lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-  const f16x8 pf = {(_Float16)p[0], (_Float16)p[2], (_Float16)p[1], (_Float16)p[3],
-                    (_Float16)p[4], (_Float16)p[6], (_Float16)p[5], (_Float16)p[7]};
-
-  // ---- O^T += V^T P^T, 32 tokens per MFMA; tile q holds channels 8m + q ----
-  const uint32_t sa02 = v_scales02(ra.vs), sa13 = v_scales13(ra.vs);
-  const uint32_t sb02 = v_scales02(rb.vs), sb13 = v_scales13(rb.vs);
-  pv_tile<0>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[0]);
-  pv_tile<1>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[1]);
-  pv_tile<2>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[2]);
-  pv_tile<3>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[3]);
-  pv_tile<4>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[4]);
-  pv_tile<5>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[5]);
-  pv_tile<6>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[6]);
-  pv_tile<7>(ra.vc, rb.vc, sa02, sa13, sb02, sb13, pf, acc[7]);
+  F::pv(ra, rb, p, acc);
 }
 
 // A value every lane holds the same copy of, moved to scalar registers so that
@@ -288,6 +398,7 @@ __device__ __forceinline__ void set_priority(int left, int quota) {
 
 // Pages [pg0, pg1) of sequence b, KV head h, for one wave: online-softmax state
 // (acc, m_ref, lsum; lsum still per lane) of all query heads of the group.
+template <class F>
 __device__ __forceinline__ void wave_share(const DecodeArgs& a, int b, int h, int pg0, int pg1, int lane,
                                            uint8_t* ring, int32_t* ids, f32x4 (&acc)[8], float& m_ref,
                                            float& lsum, int& left, int quota) {
@@ -305,11 +416,11 @@ __device__ __forceinline__ void wave_share(const DecodeArgs& a, int b, int h, in
 
   const int L = load_uniform(a.seq_lens, b);
   const bool head_ok = n < a.group;
-  const uint8_t* pool_h = a.pool + (int64_t)h * (2 * kSlab);
-  const int64_t page_bytes = (int64_t)a.num_kv_heads * (2 * kSlab);
+  const uint8_t* pool_h = a.pool + (int64_t)h * F::kHeadBytes;
+  const int64_t page_bytes = (int64_t)a.num_kv_heads * F::kHeadBytes;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   const uint32_t ids_lds = (uint32_t)(uintptr_t)ids;
-  const DmaOffsets off = dma_offsets(lane);
+  const typename F::Offsets off = F::offsets(lane);
   const int n_pages = pg1 - pg0;
   const int n_pairs = (n_pages + 1) / 2;
   const int lim = min(L, pg1 * kPage);  // tokens of this share end here
@@ -320,7 +431,7 @@ __device__ __forceinline__ void wave_share(const DecodeArgs& a, int b, int h, in
   // are converted while those pages are in flight. The queries are staged in the
   // ring's last two slots, which the loop's first refill overwrites only after
   // they have been read.
-  const uint32_t q_lds = ring_lds + (kRing - 2) * kSlotBytes;
+  const uint32_t q_lds = ring_lds + (kRing - 2) * F::kSlotBytes;
   const uint8_t* qsrc =
       reinterpret_cast<const uint8_t*>(a.q + ((size_t)b * a.num_q_heads + (size_t)h * a.group) * kHeadDim);
   const uint32_t qbytes = (uint32_t)a.group * (kHeadDim * 2);  // 256 .. 4096
@@ -337,13 +448,13 @@ __device__ __forceinline__ void wave_share(const DecodeArgs& a, int b, int h, in
   // constant.
 #pragma unroll
   for (int j = 0; j < 2 * kPairsAhead; ++j)
-    issue_page(slab_of(pool_h, ids_v, min(j, n_pages - 1), page_bytes), off, ring_lds + j * kSlotBytes, lane);
-  wait_dma<2 * kPairsAhead * kDmaPerPage>();  // the queries have landed
+    F::issue(slab_of(pool_h, ids_v, min(j, n_pages - 1), page_bytes), off, ring_lds + j * F::kSlotBytes, lane);
+  wait_dma<2 * kPairsAhead * F::kDmaPerPage>();  // the queries have landed
 
   // ---- Q: head n of the group, channels 32G..32G+31, as f16 after rescale ----
   float qv[32];
   {
-    const uint4* qp = reinterpret_cast<const uint4*>(ring + (kRing - 2) * kSlotBytes + n * (kHeadDim * 2) + 64 * G);
+    const uint4* qp = reinterpret_cast<const uint4*>(ring + (kRing - 2) * F::kSlotBytes + n * (kHeadDim * 2) + 64 * G);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4 u = head_ok ? qp[i] : make_uint4(0, 0, 0, 0);
@@ -375,8 +486,9 @@ __device__ __forceinline__ void wave_share(const DecodeArgs& a, int b, int h, in
   for (int st = 0; st < 4; ++st)
 #pragma unroll
     for (int e = 0; e < 8; ++e) qf[st][e] = (_Float16)(qv[8 * st + e] * qmul);
-  // z (base-2 logit) = S_acc * c: undoes the Q rescale and the 1/256 of the K scales
-  const float c = __builtin_ldexpf(__builtin_fabsf(a.qk_scale_log2), qexp + 8);
+  // z (base-2 logit) = S_acc * c: undoes the Q rescale and the format's scaling
+  // of the K operand (1/256 of the E4M3 block scales for NVFP4)
+  const float c = __builtin_ldexpf(__builtin_fabsf(a.qk_scale_log2), qexp + F::kScaleLog2);
 
   int cur = 0;  // ring slot of the current pair's first page
   for (int i = 0; i < n_pairs; ++i) {
@@ -393,13 +505,14 @@ __device__ __forceinline__ void wave_share(const DecodeArgs& a, int b, int h, in
       issue_ids(pt_split, ahead / kIdChunk + 1, n_pages, ids_lds, lane);
     }
     const int nxt = cur == 0 ? kRing - 2 : cur - 2;  // the slot pair freed last iteration
-    issue_page(slab_of(pool_h, ids_v, min(ahead, n_pages - 1), page_bytes), off, ring_lds + nxt * kSlotBytes, lane);
-    issue_page(slab_of(pool_h, ids_v, min(ahead + 1, n_pages - 1), page_bytes), off,
-               ring_lds + (nxt + 1) * kSlotBytes, lane);
-    wait_dma<2 * kPairsAhead * kDmaPerPage>();  // the current pair's copies have landed
-    const PageRegs ra = read_page(ring + cur * kSlotBytes, lane);
-    const PageRegs rb = read_page(ring + (cur + 1) * kSlotBytes, lane);
-    pair_step(ra, rb, (pg0 + 2 * i) * kPage, lim, G, qf, c, m_ref, lsum, acc);
+    F::issue(slab_of(pool_h, ids_v, min(ahead, n_pages - 1), page_bytes), off, ring_lds + nxt * F::kSlotBytes,
+             lane);
+    F::issue(slab_of(pool_h, ids_v, min(ahead + 1, n_pages - 1), page_bytes), off,
+             ring_lds + (nxt + 1) * F::kSlotBytes, lane);
+    wait_dma<2 * kPairsAhead * F::kDmaPerPage>();  // the current pair's copies have landed
+    const typename F::Regs ra = F::read(ring + cur * F::kSlotBytes, lane);
+    const typename F::Regs rb = F::read(ring + (cur + 1) * F::kSlotBytes, lane);
+    pair_step<F>(ra, rb, (pg0 + 2 * i) * kPage, lim, G, qf, c, m_ref, lsum, acc);
     cur = cur + 2 == kRing ? 0 : cur + 2;
   }
   wait_dma<0>();  // no copy may outlive the wave's use of its LDS
@@ -434,7 +547,11 @@ struct Cursor {
 
 // Four waves per SIMD (at most 128 VGPRs): the persistent grid assumes four
 // resident workgroups per CU.
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_split(DecodeArgs a) {
+template <class F>
+__device__ __forceinline__ void decode_split(const DecodeArgs& a) {
+  constexpr int kWaves = F::kWaves;
+  static_assert(kRing * F::kSlotBytes >= 8 * 64 * 16 + 16 * 8, "a wave's state must fit its ring region");
+  static_assert(2 * F::kSlotBytes >= 16 * kHeadDim * 2, "the group's queries must fit two ring slots");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform by construction
   const int lane = threadIdx.x & 63;
   const int S = a.num_splits;
@@ -443,7 +560,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
   const int W = gridDim.x;
 
   __shared__ int waves_done;
-  __shared__ __attribute__((aligned(16))) uint8_t ring_all[kWaves][kRing * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring_all[kWaves][kRing * F::kSlotBytes];
   __shared__ __attribute__((aligned(16))) int32_t ids_all[kWaves][2 * kIdChunk];
   if (threadIdx.x == 0) waves_done = 0;
   __syncthreads();
@@ -543,7 +660,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
     const int G = ln >> 4;
     f32x4 acc[8];
     float m_ref, lsum;
-    wave_share(a, cu.b, h, pg0, pg1, ln, ring, ids, acc, m_ref, lsum, left, quota);
+    wave_share<F>(a, cu.b, h, pg0, pg1, ln, ring, ids, acc, m_ref, lsum, left, quota);
 
     // ---- merge the waves' states; the last wave to finish writes the run's ----
     lsum = xor16_sum(lsum);
@@ -593,9 +710,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
         const int qh = h * a.group + n;
         const size_t unit = ((size_t)cu.b * a.num_q_heads + qh) * S + s;
         float* po = a.part_o + unit * kHeadDim;
-        // o_all[q][r] is O^T[channel 8 (4G + r) + q][head n], in units of 1/256 of
-        // the value scale (the V scales were carried as E4M3/256)
-        const float vs = a.v_scale * 256.0f;
+        // o_all[q][r] is O^T[channel 8 (4G + r) + q][head n], in units of
+        // 2^-kScaleLog2 of the value scale (NVFP4 V scales travel as E4M3/256)
+        const float vs = __builtin_ldexpf(a.v_scale, F::kScaleLog2);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float4 v0 = make_float4(o_all[0][r] * vs, o_all[1][r] * vs, o_all[2][r] * vs, o_all[3][r] * vs);
@@ -614,24 +731,44 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
   }
 }
 
+template <class F>
+constexpr int lds_per_workgroup() {
+  return F::kWaves * (kRing * F::kSlotBytes + 2 * kIdChunk * 4) + 16;
+}
+static_assert(Nvfp4Page::kWorkgroupsPerCu * lds_per_workgroup<Nvfp4Page>() <= 160 * 1024,
+              "the NVFP4 workgroups of a CU must fit its LDS");
+static_assert(Fp8Page::kWorkgroupsPerCu * lds_per_workgroup<Fp8Page>() <= 160 * 1024,
+              "the FP8 workgroups of a CU must fit its LDS");
+static_assert(lds_per_workgroup<Nvfp4Page>() <= 64 * 1024 && lds_per_workgroup<Fp8Page>() <= 64 * 1024,
+              "a workgroup addresses at most 64 KB of LDS");
+
+// Four NVFP4 workgroups of four waves per CU (at most 128 VGPRs: four waves per
+// SIMD); four FP8 workgroups of two waves (at most 256 VGPRs).
+__global__ __launch_bounds__(64 * Nvfp4Page::kWaves) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_split(
+    DecodeArgs a) {
+  decode_split<Nvfp4Page>(a);
+}
+__global__ __launch_bounds__(64 * Fp8Page::kWaves) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_split_fp8(
+    DecodeArgs a) {
+  decode_split<Fp8Page>(a);
+}
+
 }  // namespace
 
-int decode_waves_per_split() { return kWaves; }
+int decode_waves_per_split(bool fp8) { return fp8 ? Fp8Page::kWaves : Nvfp4Page::kWaves; }
 
-// Four workgroups of four waves per CU: LDS (under 40 KB per workgroup of the
-// CU's 160 KB) and registers (at most 128 VGPRs, i.e. four waves per SIMD) both
-// allow exactly that. More workgroups than fit would only queue behind the
-// resident ones; the kernel's result does not depend on the count.
-constexpr int kWorkgroupsPerCu = 4;
-constexpr int kLdsPerWorkgroup = kWaves * (kRing * kSlotBytes + 2 * kIdChunk * 4) + 16;
-static_assert(kWorkgroupsPerCu * kLdsPerWorkgroup <= 160 * 1024, "four workgroups must fit a CU's LDS");
-static_assert(kLdsPerWorkgroup <= 64 * 1024, "a workgroup addresses at most 64 KB of LDS");
-
-int decode_resident_workgroups(int num_cus) { return kWorkgroupsPerCu * (num_cus > 0 ? num_cus : 1); }
+// More workgroups than fit would only queue behind the resident ones; the
+// kernel's result does not depend on the count.
+int decode_resident_workgroups(int num_cus, bool fp8) {
+  return (fp8 ? Fp8Page::kWorkgroupsPerCu : Nvfp4Page::kWorkgroupsPerCu) * (num_cus > 0 ? num_cus : 1);
+}
 
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_decode_split, dim3(a.num_workgroups), dim3(64 * kWaves), 0, stream, a);
+  if (a.fp8)
+    hipLaunchKernelGGL(k_decode_split_fp8, dim3(a.num_workgroups), dim3(64 * Fp8Page::kWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_decode_split, dim3(a.num_workgroups), dim3(64 * Nvfp4Page::kWaves), 0, stream, a);
   return hipGetLastError();
 }
 

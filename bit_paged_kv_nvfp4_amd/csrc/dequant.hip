@@ -17,31 +17,6 @@
 namespace nvfp4kv {
 namespace {
 
-// E4M3 ("fn") code of x: nearest value, ties to the even code, magnitudes above
-// 448 saturate to 448, sign kept (also of zero). x must be finite. Written out
-// from the format: normal codes 8..126 hold (1 + m/8) 2^(e-7), codes 0..7 hold
-// m 2^-9; rounding the binary32 significand to 3 bits with a carry into the
-// exponent covers every normal case, and below 2^-6 the value is rounded to a
-// multiple of 2^-9 (which reaches code 8 = 2^-6 exactly when it rounds up).
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = __builtin_fabsf(x);
-  uint32_t code;
-  if (a >= 448.0f) {
-    code = 0x7Eu;
-  } else if (a < 0x1p-6f) {
-    code = (uint32_t)__builtin_rintf(a * 512.0f);  // exact product, nearest-even integer 0..8
-  } else {
-    const uint32_t bits = u & 0x7FFFFFFFu;
-    const uint32_t e = (bits >> 23) - 127u + 7u;  // 1..15 here
-    const uint32_t m = bits & 0x7FFFFFu;
-    const uint32_t r = m >> 20, rem = m & 0xFFFFFu;
-    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ? 1u : 0u;
-    code = (e << 3) + r + up;  // a carry out of the mantissa moves to the next exponent
-  }
-  return sign | code;
-}
 
 // Eight consecutive values of one output row, as one 16-byte store (bf16), two
 // (f32) or one 8-byte store (FP8 E4M3).

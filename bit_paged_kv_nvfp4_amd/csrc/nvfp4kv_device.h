@@ -76,6 +76,32 @@ __device__ __forceinline__ void wait_dma() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// E4M3 ("fn") code of x: nearest value, ties to the even code, magnitudes above
+// 448 saturate to 448, sign kept (also of zero). x must be finite. Written out
+// from the format: normal codes 8..126 hold (1 + m/8) 2^(e-7), codes 0..7 hold
+// m 2^-9; rounding the binary32 significand to 3 bits with a carry into the
+// exponent covers every normal case, and below 2^-6 the value is rounded to a
+// multiple of 2^-9 (which reaches code 8 = 2^-6 exactly when it rounds up).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __builtin_fabsf(x);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7Eu;
+  } else if (a < 0x1p-6f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);  // exact product, nearest-even integer 0..8
+  } else {
+    const uint32_t bits = u & 0x7FFFFFFFu;
+    const uint32_t e = (bits >> 23) - 127u + 7u;  // 1..15 here
+    const uint32_t m = bits & 0x7FFFFFu;
+    const uint32_t r = m >> 20, rem = m & 0xFFFFFu;
+    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ? 1u : 0u;
+    code = (e << 3) + r + up;  // a carry out of the mantissa moves to the next exponent
+  }
+  return sign | code;
+}
+
 struct QuantizeArgs {
   const void* k;
   const void* v;
@@ -87,6 +113,9 @@ struct QuantizeArgs {
   uint8_t* pool;
   int32_t num_kv_heads;
   float g;
+  int32_t fp8;             // 1: the pool is the FP8 baseline
+  float inv_k_scale;       // FP8 baseline: 1 / k_scale, 1 / v_scale (powers of two)
+  float inv_v_scale;
 };
 
 struct DecodeArgs {
@@ -104,6 +133,8 @@ struct DecodeArgs {
   float v_scale;           // g (the partial states carry V in true units)
   int32_t num_splits;
   int32_t num_workgroups;  // persistent workgroups of the decode kernel
+  int32_t fp8;             // 1: the pool is the FP8 baseline (K/V scales folded into
+                           // qk_scale_log2 and v_scale)
   float* part_o;           // [B][Hq][S][128]
   float* part_ml;          // [B][Hq][S][2]: running max (log2 units), sum
   void* out;
@@ -147,10 +178,10 @@ struct ExtendArgs {
 };
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
-// Waves that share one split of the decode kernel (one workgroup per split).
-int decode_waves_per_split();
-// Workgroups of the decode kernel that fit on the device at once.
-int decode_resident_workgroups(int num_cus);
+// Waves of one decode workgroup, per page format.
+int decode_waves_per_split(bool fp8);
+// Workgroups of the decode kernel that fit on the device at once, per page format.
+int decode_resident_workgroups(int num_cus, bool fp8);
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);

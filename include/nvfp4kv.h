@@ -22,6 +22,8 @@
  *     prefix into a dense workspace ([LMSYS] "Interpretation").
  *   - nvfp4_extend_attn: the extend path's attention of a chunk of queries over
  *     that workspace and the chunk itself ([LMSYS] "Interpretation").
+ * and, as the baseline the pages compare against, an FP8 E4M3 paged cache with
+ * the same decode machinery (fp8_kv_quantize, fp8_paged_decode_attn).
  *
  * NVFP4 ([EUROK] "Bytes pro Token"; [LMSYS] "Interpretation", "Perspective"):
  * each value is E2M1 (1 sign, 2 exponent, 1 mantissa bit; magnitudes 0, 0.5, 1,
@@ -243,6 +245,59 @@ int32_t nvfp4_decode_combine(const void* workspace, size_t workspace_bytes, int3
 int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page_table, int64_t page_table_stride,
                                    const int32_t* seq_lens, const int64_t* row_offsets, int32_t n_seqs,
                                    int32_t max_seq_len, void* k_out, void* v_out, int32_t out_dtype, void* stream);
+
+/*
+ * ---- FP8 E4M3 baseline ------------------------------------------------------
+ * The cache the pages compare NVFP4 against ([LMSYS] "Synopsis", "Perspective";
+ * [EUROK] "Bytes pro Token": one byte per value), built with the same decode
+ * machinery so that the comparison is between formats, not kernels. Each value
+ * is stored as the E4M3 ("fn") code of x / s, with s the per-tensor scale of K
+ * or V: the nearest E4M3 value, ties to the even code, magnitudes above 448
+ * saturate to +-448, sign kept. It decodes to E4M3(code) * s.
+ *
+ * FP8 pool layout: each page holds, for each KV head h, a K slab then a V slab
+ * of 2048 bytes each: slab(p, h, kind) at byte ((p * Hkv + h) * 2 + kind) * 2048,
+ * one code byte per value:
+ *   K (row r, channel d): byte r*128 + d
+ *   V (row r, channel d): byte ((r/4)*16 + d/8)*32 + (d%8)*4 + r%4
+ * (a 32-byte V chunk holds channels 8n..8n+7 of rows 4g..4g+3, channel-major,
+ * so that one 32-bit word is the four rows of one channel). Each byte belongs to
+ * one value: writes of distinct tokens never touch each other's bytes.
+ */
+#define FP8KV_SLAB_BYTES 2048
+
+typedef struct fp8kv_pool {
+  void* data;            /* device, 16-byte aligned, num_pages*num_kv_heads*2*2048 bytes */
+  int64_t num_pages;     /* >= 1 */
+  int32_t num_kv_heads;  /* >= 1 */
+  float k_scale;         /* per-tensor scales: powers of two in [2^-64, 2^64] */
+  float v_scale;
+} fp8kv_pool;
+
+/* Bytes of an FP8 pool of num_pages pages and num_kv_heads heads. */
+int64_t fp8kv_pool_bytes(int64_t num_pages, int32_t num_kv_heads);
+
+/* Quantize-on-write into the FP8 pool: arguments, slots and errors as
+ * nvfp4_kv_quantize (ERR_VALUE: a scale that is not a power of two in range). */
+int32_t fp8_kv_quantize(const void* k_src, const void* v_src, int32_t src_dtype, int64_t token_stride,
+                        int64_t head_stride, const int32_t* slot_mapping, int64_t num_tokens, const fp8kv_pool* pool,
+                        void* stream);
+
+/* Decode attention over the FP8 pool: arguments, outputs, partial-state format
+ * (phase 2 is nvfp4_decode_combine), workspace size and errors as
+ * nvfp4_paged_decode_attn / _partial. The kernel runs four workgroups of two
+ * waves per CU (an FP8 page slot is 4 KB of LDS), so its default split count
+ * comes from fp8_paged_decode_attn_default_splits. */
+int32_t fp8_paged_decode_attn_default_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
+                                             int32_t num_cus);
+int32_t fp8_paged_decode_attn(const void* q, const int32_t* page_table, int64_t page_table_stride,
+                              const int32_t* seq_lens, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
+                              const fp8kv_pool* pool, float sm_scale, int32_t num_splits, void* workspace,
+                              size_t workspace_bytes, void* out, int32_t out_dtype, float* lse, void* stream);
+int32_t fp8_paged_decode_attn_partial(const void* q, const int32_t* page_table, int64_t page_table_stride,
+                                      const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                      int32_t max_seq_len, const fp8kv_pool* pool, float sm_scale,
+                                      int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Extend-path attention ([LMSYS] "Interpretation": after the cached prefix is

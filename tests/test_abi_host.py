@@ -19,7 +19,7 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced by validation
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(nvfp4[a-z_0-9]*)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*((?:nvfp4|fp8)[a-z_0-9]*)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -164,3 +164,30 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         B.lib()
+
+
+def fp8_pool(num_pages=4, hkv=1, ks=1.0, vs=1.0, data=FAKE):
+    return B.Fp8PoolDesc(data, num_pages, hkv, ks, vs)
+
+
+def test_fp8_baseline_validation(L):
+    assert L.fp8kv_pool_bytes(10, 8) == 10 * 8 * 2 * 2048
+    assert L.fp8_paged_decode_attn_default_splits(44, 8, 32768, 256) == 47
+    q = lambda p, **kw: L.fp8_kv_quantize(kw.get("k", FAKE), FAKE, kw.get("dt", 0), 1024, 128, FAKE, kw.get("T", 16),
+                                          ctypes.byref(p) if p is not None else None, None)
+    assert q(None) == ERR_NULL
+    assert q(fp8_pool(data=0)) == ERR_NULL
+    assert q(fp8_pool(ks=3.0)) == ERR_VALUE
+    assert q(fp8_pool(vs=0.0)) == ERR_VALUE
+    assert q(fp8_pool(hkv=0)) == ERR_SHAPE
+    assert q(fp8_pool(), dt=2) == ERR_DTYPE
+    assert q(fp8_pool(), T=0) == OK
+    assert q(fp8_pool(), k=FAKE + 4) == ERR_ALIGN
+    d = lambda p, **kw: L.fp8_paged_decode_attn(FAKE, FAKE, 8, FAKE, kw.get("B", 2), kw.get("hq", 8), 100,
+                                                ctypes.byref(p) if p is not None else None, 0.088, 2, FAKE, 1 << 30,
+                                                FAKE, kw.get("odt", 1), None, None)
+    assert d(None) == ERR_NULL
+    assert d(fp8_pool(vs=0.75)) == ERR_VALUE
+    assert d(fp8_pool(), odt=2) == ERR_DTYPE
+    assert d(fp8_pool(hkv=3), hq=8) == ERR_SHAPE
+    assert d(fp8_pool(), B=0) == OK

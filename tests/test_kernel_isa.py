@@ -27,10 +27,12 @@ def _asm(tmp_path, src):
 
 
 def _function(asm, name):
+    """Body of the kernel whose mangled name holds `name` (a length-prefixed
+    identifier, e.g. 14k_decode_split), up to the end of the function."""
     m = re.search(rf"^(_Z\S*{name}\S*):", asm, flags=re.M)
     assert m, name
     start = m.end()
-    end = asm.index("s_endpgm", start)
+    end = asm.index(".Lfunc_end", start)
     return asm[start:end]
 
 
@@ -41,8 +43,13 @@ def decode_asm(tmp_path_factory):
     return _asm(tmp_path_factory.mktemp("isa"), os.path.join(B.CSRC, "decode.hip"))
 
 
-def test_copies_use_sgpr_base(decode_asm):
-    body = _function(decode_asm, "k_decode_split")
+# the NVFP4 kernel and the FP8 baseline's instance of the same template
+KERNELS = ["14k_decode_split", "18k_decode_split_fp8"]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_copies_use_sgpr_base(decode_asm, kernel):
+    body = _function(decode_asm, kernel)
     copies = re.findall(r"global_load_lds_dword\S*\s+([^\n]+)", body)
     assert copies, "no asynchronous copies found"
     for operands in copies:
@@ -83,8 +90,9 @@ def _innermost_loops(body):
     return loops
 
 
-def test_page_loop_never_drains_copies(decode_asm):
-    body = _function(decode_asm, "k_decode_split")
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_page_loop_never_drains_copies(decode_asm, kernel):
+    body = _function(decode_asm, kernel)
     # the page loops: innermost loops that issue copies and run the MFMAs
     page_loops = [t for t in _innermost_loops(body).values() if "v_mfma" in t and "global_load_lds" in t]
     assert page_loops, "page loop not found"
@@ -93,12 +101,14 @@ def test_page_loop_never_drains_copies(decode_asm):
         assert waits and all(int(w) > 0 for w in waits), waits
 
 
-def test_four_waves_per_simd(decode_asm):
-    # the persistent grid launches four workgroups of four waves per CU
-    body_start = re.search(r"^_Z\S*k_decode_split\S*:", decode_asm, flags=re.M).start()
+@pytest.mark.parametrize("kernel,max_vgprs", [(KERNELS[0], 128), (KERNELS[1], 256)])
+def test_waves_per_simd(decode_asm, kernel, max_vgprs):
+    # the persistent grids: four NVFP4 workgroups of four waves per CU (four waves
+    # per SIMD), four FP8 workgroups of two waves (two per SIMD)
+    body_start = re.search(rf"^_Z\S*{kernel}\S*:", decode_asm, flags=re.M).start()
     meta = decode_asm[body_start:]
     vgprs = int(re.search(r"; NumVgprs:\s*(\d+)", meta).group(1))
-    assert vgprs <= 128, vgprs
+    assert vgprs <= max_vgprs, vgprs
 
 
 def test_no_packed_fp32_and_no_scratch(decode_asm):
