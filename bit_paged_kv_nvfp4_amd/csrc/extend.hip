@@ -7,21 +7,22 @@
 // a P-token prefix attends over all P workspace rows and over chunk rows 0..i
 // (causal), with query head q reading KV head q / (Hq / Hkv).
 //
-// Work item: one workgroup of four waves per (KV head, block of chunk tokens);
-// two workgroups share a CU. Consecutive workgroups take consecutive KV heads,
+// Work item: one workgroup of eight waves per (KV head, block of chunk tokens),
+// one per CU (two waves per SIMD); the eight waves share every K/V tile, so the
+// copies and conversions of a tile serve 256 rows. Consecutive workgroups take consecutive KV heads,
 // so with Hkv = 8 every block of one head runs on one XCD and the head's K/V
 // stream is shared through that XCD's L2. A wave owns 32 rows, row =
-// token_in_block * group + head, and per 32-key tile computes
-//   S^T[32 keys x 32 rows] = K[32 x 128] Q^T      16 x v_mfma_f32_16x16x32_bf16
-//   O^T[128 x 32 rows]    += V^T[128 x 32] P^T    16 x v_mfma_f32_16x16x32_f16
+// token_in_block * group + head, and per 64-key tile computes
+//   S^T[64 keys x 32 rows] = K[64 x 128] Q^T      32 x v_mfma_f32_16x16x32_bf16
+//   O^T[128 x 32 rows]    += V^T[128 x 64] P^T    32 x v_mfma_f32_16x16x32_f16
 // A 16x16x32 MFMA lane (n = lane % 16, G = lane / 16) holds row n of A and
 // column n of B with k slots 8G..8G+7, and column n, rows 4G..4G+3 of C. So the
 // S^T fragment of a lane (row n; keys 4G..4G+3 of each 16-key block) is already
-// a P^T operand: its k slots are keys 4G..4G+3 of block 0, then of block 1, and
-// the V^T operand is read with the same key order.
+// a P^T operand: its k slots are keys 4G..4G+3 of block 2ks, then of block
+// 2ks+1, and the V^T operand is read with the same key order.
 //
-// Tiles: the prefix in 32-key tiles (the last one may be partial), then the
-// chunk in 32-key tiles, so that every tile has one source dtype. Each tile's
+// Tiles: the prefix in 64-key tiles (the last one may be partial), then the
+// chunk in 64-key tiles, so that every tile has one source dtype. Each tile's
 // K and V rows are copied global -> LDS asynchronously (global_load_lds) into a
 // three-stage ring, two tiles ahead of the one being computed. A bf16 K tile
 // lands directly in the layout the first product reads; raw V (and FP8 K) are
@@ -45,9 +46,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kXWaves = 4;
+constexpr int kXWaves = 8;
+constexpr int kXThreads = 64 * kXWaves;
 constexpr int kXRows = 32;                  // rows per wave
-constexpr int kTile = 32;                   // keys per tile
+constexpr int kTile = 64;                   // keys per tile
 constexpr int kStages = 3;                  // copies run two tiles ahead
 constexpr int kStageBytes = kTile * 256;    // a tile of bf16 rows of one head
 constexpr float kXLazyLog2 = 8.0f;
@@ -108,8 +110,8 @@ __device__ __forceinline__ Tile tile_of(const ExtendArgs& a, int h, int n_pre, i
   return x;
 }
 
-// Copies of a tile into one ring stage by wave w: 4 per wave for bf16 rows, 2
-// for FP8 rows. LDS layouts of a stage:
+// Copies of a tile into one ring stage by wave w (of 8): 4 per wave for bf16
+// rows, 2 for FP8 rows. LDS layouts of a stage:
 //   K bf16: piece (16 B) c of key r at 16-byte slot r * 16 + (c ^ (r & 15))
 //   V bf16: piece c of key r at slot r * 16 + (c ^ ((r >> 1) & 15))
 //   K FP8:  piece (16 B = 16 channels) j of key r at slot r * 8 + j
@@ -137,20 +139,20 @@ __device__ __forceinline__ void issue_tile(const Tile& x, int hkv, uint32_t k_ld
   }
 }
 
-// V^T tile (f16): channel d, keys 4q .. 4q+3 (one 8-byte piece) at byte
-// d * 64 + 8 (q ^ ((d >> 2) & 3)).
-__device__ __forceinline__ uint32_t vt_piece(int d, int q) { return d * 64 + 8 * (q ^ ((d >> 2) & 3)); }
+// V^T tile (f16): channel d, keys 4q .. 4q+3 (one 8-byte piece of the 128-byte
+// row) at byte d * 128 + 8 (q ^ (d & 15)).
+__device__ __forceinline__ uint32_t vt_piece(int d, int q) { return d * 128 + 8 * (q ^ (d & 15)); }
 
 // Workgroup pass over a landed stage: raw V -> V^T (f16); FP8 K -> bf16 K in the
-// K-operand layout. Thread t: channels 8c .. 8c+7 (c = t / 16) of keys 2m, 2m+1
-// (m = t % 16).
+// K-operand layout. Thread t: channels 8c .. 8c+7 (c = t / 32) of keys 2m, 2m+1
+// (m = t % 32).
 __device__ __forceinline__ void convert_tile(bool fp8, int t, const uint8_t* k_st, const uint8_t* v_st,
                                              uint8_t* vt, uint8_t* kconv) {
-  const int c = t >> 4, m = t & 15;
+  const int c = t >> 5, m = t & 31;
   uint32_t lo[4], hi[4];  // channels (8c + 2e, 8c + 2e + 1) of key 2m and of key 2m + 1, as f16 pairs
   if (!fp8) {
-    const uint4 a0 = *reinterpret_cast<const uint4*>(v_st + 16 * ((2 * m) * 16 + (c ^ m)));
-    const uint4 a1 = *reinterpret_cast<const uint4*>(v_st + 16 * ((2 * m + 1) * 16 + (c ^ m)));
+    const uint4 a0 = *reinterpret_cast<const uint4*>(v_st + 16 * ((2 * m) * 16 + (c ^ (m & 15))));
+    const uint4 a1 = *reinterpret_cast<const uint4*>(v_st + 16 * ((2 * m + 1) * 16 + (c ^ (m & 15))));
     const uint32_t w0[4] = {a0.x, a0.y, a0.z, a0.w}, w1[4] = {a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -193,7 +195,7 @@ __device__ __forceinline__ void convert_tile(bool fp8, int t, const uint8_t* k_s
 }
 
 template <bool kPreFp8>
-__global__ __launch_bounds__(64 * kXWaves) __attribute__((amdgpu_waves_per_eu(2))) void k_extend_attn(ExtendArgs a) {
+__global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_extend_attn(ExtendArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -211,6 +213,8 @@ __global__ __launch_bounds__(64 * kXWaves) __attribute__((amdgpu_waves_per_eu(2)
   __shared__ __attribute__((aligned(16))) uint8_t k_ring[kStages][kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t v_ring[kStages][kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t vt[kTile * kHeadDim * 2];
+  static_assert(kStages * 2 * kStageBytes + kTile * kHeadDim * 2 + kStageBytes <= 160 * 1024,
+                "the workgroup's LDS fits a CU");
   __shared__ __attribute__((aligned(16))) uint8_t kconv[kPreFp8 ? kStageBytes : 16];
   const uint32_t k_ring_lds = (uint32_t)reinterpret_cast<uintptr_t>(&k_ring[0][0]);
   const uint32_t v_ring_lds = (uint32_t)reinterpret_cast<uintptr_t>(&v_ring[0][0]);
@@ -291,15 +295,15 @@ __global__ __launch_bounds__(64 * kXWaves) __attribute__((amdgpu_waves_per_eu(2)
 
     // ---- S^T = K Q^T ----
     const uint4* kt = reinterpret_cast<const uint4*>(x.fp8 ? kconv : k_ring[st]);
-    f32x4 sacc[2][2];
+    f32x4 sacc[4][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) sacc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 4; ++kb) {
         const bf16x8 kf = __builtin_bit_cast(bf16x8, kt[(16 * kb + n) * 16 + ((4 * s + G) ^ n)]);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(64 * kXWaves) __attribute__((amdgpu_waves_per_eu(2)
     // ---- mask: missing keys; chunk key j is visible to token i iff j <= i ----
     if (x.n_valid < kTile || (x.chunk && x.first + kTile - 1 > t_first)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = 16 * kb + 4 * G + r;
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(64 * kXWaves) __attribute__((amdgpu_waves_per_eu(2)
     for (int rb = 0; rb < 2; ++rb) {
       float mx = -__builtin_inff();
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = __builtin_fmaxf(mx, sacc[kb][rb][r]);
       mx = xor32_max(xor16_max(mx));
@@ -343,32 +347,35 @@ __global__ __launch_bounds__(64 * kXWaves) __attribute__((amdgpu_waves_per_eu(2)
         for (int d = 0; d < 8; ++d) oacc[d][rb] *= alpha;
       }
     }
-    // P^T operands: k slots = keys 4G..4G+3 of block 0, then of block 1
-    f16x8 pf[2];
+    // P^T operands of key half ks: k slots = keys 4G..4G+3 of block 2ks, then of
+    // block 2ks + 1
+    f16x8 pf[2][2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const float mu = m_ref[rb] == -__builtin_inff() ? 0.0f : m_ref[rb];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][r], c2, -mu));
-          pf[rb][4 * kb + r] = p;
+          pf[kb >> 1][rb][4 * (kb & 1) + r] = p;
           lsum[rb] += (float)p;
         }
     }
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const int dim = 16 * d + n;
-      const uint2 v0 = *reinterpret_cast<const uint2*>(vt + vt_piece(dim, G));
-      const uint2 v1 = *reinterpret_cast<const uint2*>(vt + vt_piece(dim, 4 + G));
-      const f16x8 vf = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        oacc[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[rb], oacc[d][rb], 0, 0, 0);
-    }
+      for (int d = 0; d < 8; ++d) {
+        const int dim = 16 * d + n;
+        const uint2 v0 = *reinterpret_cast<const uint2*>(vt + vt_piece(dim, 8 * ks + G));
+        const uint2 v1 = *reinterpret_cast<const uint2*>(vt + vt_piece(dim, 8 * ks + 4 + G));
+        const f16x8 vf = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          oacc[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[ks][rb], oacc[d][rb], 0, 0, 0);
+      }
   }
 
   // ---- epilogue: O / l as bf16; lse in natural log ----
@@ -395,7 +402,7 @@ int extend_tokens_per_block(int group) { return kXWaves * kXRows / group; }
 
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream) {
   if (a.chunk_len == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.num_token_blocks * (unsigned)a.num_kv_heads), block(64 * kXWaves);
+  const dim3 grid((unsigned)a.num_token_blocks * (unsigned)a.num_kv_heads), block(kXThreads);
   if (a.pre_fp8)
     hipLaunchKernelGGL(k_extend_attn<true>, grid, block, 0, stream, a);
   else
