@@ -36,7 +36,7 @@
 // only when a tile's max exceeds it by more than 2^8, so P <= 256); P enters
 // the second product as f16 (11 significant bits, where bf16 would keep 8 and
 // miss the error bar when few keys share the weight), and the row sums add up
-// the same rounded values.
+// the same rounded values, on the matrix cores (an all-ones operand).
 #include "nvfp4kv.h"
 #include "nvfp4kv_device.h"
 
@@ -267,7 +267,11 @@ __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) oacc[d][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref[2] = {-__builtin_inff(), -__builtin_inff()};
-  float lsum[2] = {0.f, 0.f};
+  // row sums of P on the matrix cores: an all-ones A operand times P^T gives each
+  // row's sum in every element of the accumulator column
+  f32x4 lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const f16x8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                      (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
 
   // prologue: tiles 0 and 1 in flight
   for (int i = 0; i < 2 && i < n_tiles; ++i)
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       for (int rb = 0; rb < 2; ++rb) {
         const float alpha = need[rb] ? __builtin_amdgcn_exp2f(m_ref[rb] - mt[rb]) : 1.0f;
         m_ref[rb] = need[rb] ? mt[rb] : m_ref[rb];
-        lsum[rb] *= alpha;
+        lacc[rb] *= alpha;
 #pragma unroll
         for (int d = 0; d < 8; ++d) oacc[d][rb] *= alpha;
       }
@@ -357,9 +361,7 @@ __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][r], c2, -mu));
-          pf[kb >> 1][rb][4 * (kb & 1) + r] = p;
-          lsum[rb] += (float)p;
+          pf[kb >> 1][rb][4 * (kb & 1) + r] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][r], c2, -mu));
         }
     }
 
@@ -376,12 +378,16 @@ __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2))) 
         for (int rb = 0; rb < 2; ++rb)
           oacc[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[ks][rb], oacc[d][rb], 0, 0, 0);
       }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) lacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[ks][rb], lacc[rb], 0, 0, 0);
   }
 
   // ---- epilogue: O / l as bf16; lse in natural log ----
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const float l = xor32_sum(xor16_sum(lsum[rb]));
+    const float l = lacc[rb][0];  // the same row sum in every element
     if (!valid[rb]) continue;
     const float inv = 1.0f / l;
     uint16_t* o = a.out + (tok[rb] * a.num_q_heads + qh[rb]) * kHeadDim;
