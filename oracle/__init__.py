@@ -19,6 +19,8 @@ Parity status of each function (what pins it is listed in the tests):
   fp8_* (FP8 baseline pool)        pinned (codes vs library float8 cast of x/s;
                                    layout bijection; attention vs fp64 SDPA on
                                    E4M3-representable K/V with scales)
+  amax, global_scale_for_amax      pinned (library max; closed forms and
+                                   minimality over powers of two)
   extend_attn                      pinned (fp64 library SDPA with an explicit
                                    prefix + causal mask, all three workspace
                                    dtypes; single-row and equal-key closed forms)
@@ -107,6 +109,10 @@ def _load(path: str) -> ctypes.CDLL:
     L.orc_fp8_decode_attn.argtypes = [P, P, c.c_int64, P, c.c_int, c.c_int, c.c_int, P, c.c_float, c.c_float,
                                       c.c_double, P, P, P, c.c_int, c.c_int]
     L.orc_fp8_decode_attn.restype = None
+    L.orc_amax.argtypes = [P, c.c_int, c.c_int64, c.c_int64, c.c_int64, c.c_int]
+    L.orc_amax.restype = c.c_double
+    L.orc_global_scale_for_amax.argtypes = [c.c_double]
+    L.orc_global_scale_for_amax.restype = c.c_double
     return L
 
 
@@ -379,3 +385,16 @@ def fp8_decode_attn(q_bf16_bits: np.ndarray, page_table: np.ndarray, seq_lens: n
                               float(k_scale), float(v_scale), float(sm_scale), _ptr(out), _ptr(lse), u_ptr, n_u,
                               int(n_threads))
     return out, lse
+
+
+# ---- global-scale calibration -------------------------------------------------
+def amax(x: np.ndarray) -> float:
+    """max |x| of a [T, H, 128] float32 or uint16 (bf16 bits) array."""
+    x = np.ascontiguousarray(x)
+    T, H, d = x.shape
+    assert d == HEAD_DIM and x.dtype in (np.float32, np.uint16)
+    return float(lib().orc_amax(_ptr(x), 0 if x.dtype == np.float32 else 1, H * HEAD_DIM, HEAD_DIM, T, H))
+
+
+def global_scale_for_amax(a: float) -> float:
+    return float(lib().orc_global_scale_for_amax(float(a)))

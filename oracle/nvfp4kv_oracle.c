@@ -48,6 +48,12 @@
  *      mask and no precision for the chunk's own keys and values): the mask is
  *      causal over the chunk, and the chunk's keys and values enter as the
  *      bf16 values they arrive in, not via the NVFP4 cache.
+ *  10. Global-scale calibration ([LMSYS] "Perspective": the experiments left
+ *      the per-tensor FP32 global scale at 1.0 and calibrating it may narrow
+ *      the accuracy gap). Reading: the calibrated g is the smallest power of
+ *      two with amax / (6 g) <= 448, amax = max |x| over the tensor, so that no
+ *      block scale saturates and the largest block scales use the top of the
+ *      E4M3 range; g = 1 for an all-zero tensor.
  *   9. FP8 baseline ([LMSYS] "Perspective" and "Synopsis" compare NVFP4 KV
  *      against an FP8 KV cache; [EUROK] "Bytes pro Token" gives FP8 one byte
  *      per value). Each value is stored as the E4M3 code of x / s, s the
@@ -657,4 +663,33 @@ void orc_fp8_dequant_row(const uint8_t* pool, int64_t page, int row, int head, i
   const uint8_t* slab = pool + orc_fp8_slab_offset(page, head, kind, num_kv_heads);
   int d;
   for (d = 0; d < ORC_D; ++d) out128[d] = orc_e4m3_value(slab[orc_fp8_byte_offset(kind, row, d)]) * (double)scale;
+}
+
+
+/* ---- 10. global-scale calibration -------------------------------------- */
+/* max |x| over T tokens x H heads x 128 channels (element strides given);
+ * src_dtype 0 = float32, 1 = bfloat16 bits. */
+double orc_amax(const void* src, int src_dtype, int64_t token_stride, int64_t head_stride, int64_t num_tokens,
+                int num_heads) {
+  double m = 0.0;
+  int64_t t;
+  int h, d;
+  for (t = 0; t < num_tokens; ++t)
+    for (h = 0; h < num_heads; ++h)
+      for (d = 0; d < ORC_D; ++d) {
+        int64_t idx = t * token_stride + h * head_stride + d;
+        double x = src_dtype == 0 ? (double)((const float*)src)[idx]
+                                  : (double)orc_bf16_to_float(((const uint16_t*)src)[idx]);
+        if (fabs(x) > m) m = fabs(x);
+      }
+  return m;
+}
+
+/* Smallest power of two g with amax / (6 g) <= 448 (g = 1 for amax = 0). */
+double orc_global_scale_for_amax(double amax) {
+  double g = 1.0;
+  if (amax <= 0.0) return 1.0;
+  while (amax / (6.0 * g) > 448.0) g *= 2.0;
+  while (amax / (6.0 * (g / 2.0)) <= 448.0) g /= 2.0;
+  return g;
 }

@@ -5,6 +5,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_attention as TA
+from tests import test_oracle_calibration as TC
 from tests import test_oracle_extend as TE
 from tests import test_oracle_fp8 as T8
 from tests import test_oracle_format as TF
@@ -68,6 +69,10 @@ MUTANTS = [
     ("fp8_attn_v_scale_for_k", "kind ? J->v_scale : J->k_scale", "J->v_scale"),
     ("fp8_slab_kind_ignored", "((page * num_kv_heads + head) * 2 + kind) * (int64_t)ORC_FP8_SLAB",
      "((page * num_kv_heads + head) * 2) * (int64_t)ORC_FP8_SLAB"),
+    ("amax_ignores_sign", "if (fabs(x) > m) m = fabs(x);", "if (x > m) m = x;"),
+    ("calibration_stops_before_ties", "while (amax / (6.0 * (g / 2.0)) <= 448.0) g /= 2.0;",
+     "while (amax / (6.0 * (g / 2.0)) < 448.0) g /= 2.0;"),
+    ("calibration_divisor_4", "while (amax / (6.0 * g) > 448.0) g *= 2.0;", "while (amax / (4.0 * g) > 448.0) g *= 2.0;"),
     ("slab_kind_ignored", "return ((page * num_kv_heads + head) * 2 + kind) * (int64_t)ORC_SLAB;",
      "return ((page * num_kv_heads + head) * 2) * (int64_t)ORC_SLAB;"),
 ]
@@ -88,6 +93,8 @@ def _pins(o):
     yield lambda: TA.test_seq_len_one_returns_first_value_row(o)
     yield lambda: TE.test_first_chunk_query_without_prefix_sees_only_itself(o)
     yield lambda: TE.test_constant_keys_give_running_mean_of_values(o)
+    yield lambda: TC.test_amax_vs_library(o)
+    yield lambda: TC.test_global_scale_closed_forms(o)
     yield lambda: T8.test_fp8_layout_is_a_bijection(o)
     yield lambda: T8.test_fp8_codes_vs_library_cast(o, 0.5)
     yield lambda: T8.test_fp8_codes_saturate_and_keep_sign(o)
