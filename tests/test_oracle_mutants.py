@@ -72,7 +72,8 @@ MUTANTS = [
     ("amax_ignores_sign", "if (fabs(x) > m) m = fabs(x);", "if (x > m) m = x;"),
     ("calibration_stops_before_ties", "while (amax / (6.0 * (g / 2.0)) <= 448.0) g /= 2.0;",
      "while (amax / (6.0 * (g / 2.0)) < 448.0) g /= 2.0;"),
-    ("calibration_divisor_4", "while (amax / (6.0 * g) > 448.0) g *= 2.0;", "while (amax / (4.0 * g) > 448.0) g *= 2.0;"),
+    ("calibration_limit_halved", "while (amax / (6.0 * (g / 2.0)) <= 448.0) g /= 2.0;",
+     "while (amax / (6.0 * (g / 2.0)) <= 224.0) g /= 2.0;"),
     ("slab_kind_ignored", "return ((page * num_kv_heads + head) * 2 + kind) * (int64_t)ORC_SLAB;",
      "return ((page * num_kv_heads + head) * 2) * (int64_t)ORC_SLAB;"),
 ]
