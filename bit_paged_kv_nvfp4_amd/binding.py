@@ -34,6 +34,9 @@ EXPORTED = [
     "nvfp4_decode_combine",
     "nvfp4_kv_dequant_workspace",
     "nvfp4_extend_attn",
+    "nvfp4_kv_amax_workspace_bytes",
+    "nvfp4_kv_amax",
+    "nvfp4kv_global_scale_for_amax",
     "fp8kv_pool_bytes",
     "fp8_kv_quantize",
     "fp8_paged_decode_attn_default_splits",
@@ -91,6 +94,12 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_extend_attn.argtypes = [P, P, P, c.c_int32, c.c_int64, P, P, c.c_int64, c.c_int32, c.c_int32,
                                         c.c_float, P, P, P]
         L.nvfp4_extend_attn.restype = c.c_int32
+        L.nvfp4_kv_amax_workspace_bytes.argtypes = []
+        L.nvfp4_kv_amax_workspace_bytes.restype = c.c_size_t
+        L.nvfp4_kv_amax.argtypes = [P, P, c.c_int32, c.c_int64, c.c_int64, c.c_int64, c.c_int32, P, P, c.c_size_t, P]
+        L.nvfp4_kv_amax.restype = c.c_int32
+        L.nvfp4kv_global_scale_for_amax.argtypes = [c.c_float]
+        L.nvfp4kv_global_scale_for_amax.restype = c.c_float
         L.fp8kv_pool_bytes.argtypes = [c.c_int64, c.c_int32]
         L.fp8kv_pool_bytes.restype = c.c_int64
         L.fp8_kv_quantize.argtypes = [P, P, c.c_int32, c.c_int64, c.c_int64, P, c.c_int64, c.POINTER(Fp8PoolDesc), P]
@@ -357,3 +366,25 @@ def fp8_paged_decode_attn_partial(q: torch.Tensor, page_table: torch.Tensor, seq
            lib().fp8_paged_decode_attn_partial(_ptr(q), _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B,
                                                hq, int(max_seq_len), ctypes.byref(d), float(sm_scale),
                                                int(num_splits), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def nvfp4_kv_amax(k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """max |K| and max |V| of [T, Hkv, 128] float32/bfloat16 tensors, as a device
+    float32 [2] tensor (NaN elements ignored)."""
+    if k.dtype != v.dtype or k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must share dtype, shape and strides")
+    if k.dim() != 3 or k.shape[2] != HEAD_DIM or k.stride(2) != 1:
+        raise ValueError("k, v must be [T, Hkv, 128] with a contiguous last dimension")
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(k.dtype)
+    if dt is None:
+        raise ValueError("k, v must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty(2, dtype=torch.float32, device=k.device)
+    ws = torch.empty(int(lib().nvfp4_kv_amax_workspace_bytes()), dtype=torch.uint8, device=k.device)
+    _check("nvfp4_kv_amax", lib().nvfp4_kv_amax(_ptr(k), _ptr(v), dt, k.stride(0), k.stride(1), k.shape[0], k.shape[1],
+                                                _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def nvfp4kv_global_scale_for_amax(amax: float) -> float:
+    return float(lib().nvfp4kv_global_scale_for_amax(float(amax)))

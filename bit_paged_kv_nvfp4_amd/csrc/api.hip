@@ -141,6 +141,43 @@ int32_t nvfp4_kv_quantize(const void* k_src, const void* v_src, int32_t src_dtyp
                        stream);
 }
 
+size_t nvfp4_kv_amax_workspace_bytes(void) { return (size_t)nvfp4kv::kAmaxBlocks * 2 * sizeof(float); }
+
+int32_t nvfp4_kv_amax(const void* k_src, const void* v_src, int32_t src_dtype, int64_t token_stride,
+                      int64_t head_stride, int64_t num_tokens, int32_t num_kv_heads, float* amax_out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (src_dtype != NVFP4KV_F32 && src_dtype != NVFP4KV_BF16) return NVFP4KV_ERR_DTYPE;
+  if (num_tokens < 0 || token_stride < 0 || head_stride < 0 || num_kv_heads < 1) return NVFP4KV_ERR_SHAPE;
+  if (num_tokens > ((int64_t)1 << 40) / ((int64_t)num_kv_heads * 128)) return NVFP4KV_ERR_SHAPE;
+  if (!amax_out || !workspace || (num_tokens > 0 && (!k_src || !v_src))) return NVFP4KV_ERR_NULL;
+  if (workspace_bytes < nvfp4_kv_amax_workspace_bytes()) return NVFP4KV_ERR_WORKSPACE;
+  const int64_t vec = src_dtype == NVFP4KV_F32 ? 4 : 8;
+  if ((num_tokens > 0 && (!aligned16(k_src) || !aligned16(v_src))) || token_stride % vec || head_stride % vec ||
+      !aligned16(workspace) || (reinterpret_cast<uintptr_t>(amax_out) & 3u))
+    return NVFP4KV_ERR_ALIGN;
+  nvfp4kv::AmaxArgs a;
+  a.k = k_src;
+  a.v = v_src;
+  a.bf16 = src_dtype == NVFP4KV_BF16;
+  a.token_stride = token_stride;
+  a.head_stride = head_stride;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.partial = static_cast<float*>(workspace);
+  a.out = amax_out;
+  return hip_status(nvfp4kv::launch_amax(a, static_cast<hipStream_t>(stream)));
+}
+
+float nvfp4kv_global_scale_for_amax(float amax) {
+  if (!(amax >= 0.0f) || !isfinite(amax)) return 0.0f;
+  if (amax == 0.0f) return 1.0f;
+  double g = 1.0;
+  while ((double)amax / (6.0 * g) > 448.0) g *= 2.0;
+  while ((double)amax / (6.0 * (g / 2.0)) <= 448.0) g /= 2.0;
+  const float gf = (float)g;
+  return valid_global_scale(gf) ? gf : 0.0f;
+}
+
 int64_t fp8kv_pool_bytes(int64_t num_pages, int32_t num_kv_heads) {
   if (num_pages < 0 || num_kv_heads < 0) return 0;
   return num_pages * num_kv_heads * 2 * (int64_t)FP8KV_SLAB_BYTES;

@@ -118,6 +118,19 @@ struct QuantizeArgs {
   float inv_v_scale;
 };
 
+struct AmaxArgs {
+  const void* k;
+  const void* v;
+  int32_t bf16;            // 1: sources are bfloat16, 0: float32
+  int64_t token_stride;    // elements
+  int64_t head_stride;     // elements
+  int64_t num_tokens;
+  int32_t num_kv_heads;
+  float* partial;          // [kAmaxBlocks][2] workspace
+  float* out;              // [2]: max |K|, max |V|
+};
+constexpr int kAmaxBlocks = 256;
+
 struct DecodeArgs {
   const uint16_t* q;       // bf16 bits [B][Hq][128]
   const int32_t* page_table;
@@ -178,6 +191,7 @@ struct ExtendArgs {
 };
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
+hipError_t launch_amax(const AmaxArgs& a, hipStream_t stream);
 // Waves of one decode workgroup, per page format.
 int decode_waves_per_split(bool fp8);
 // Workgroups of the decode kernel that fit on the device at once, per page format.

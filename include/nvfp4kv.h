@@ -247,6 +247,26 @@ int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page
                                    int32_t max_seq_len, void* k_out, void* v_out, int32_t out_dtype, void* stream);
 
 /*
+ * Global-scale calibration hook ([LMSYS] "Perspective": the experiments left
+ * the per-tensor FP32 global scale at 1.0, and calibrating it may narrow the
+ * accuracy gap to FP8). nvfp4_kv_amax writes max |K| and max |V| over T tokens
+ * of every KV head (same source arguments as nvfp4_kv_quantize) to amax_out[0]
+ * and amax_out[1] (device f32); NaN elements are ignored. It takes a device
+ * workspace of nvfp4_kv_amax_workspace_bytes() bytes (two launches, no atomics,
+ * no memset; nothing is allocated). nvfp4kv_global_scale_for_amax (host, pure)
+ * returns the smallest power of two g with amax / (6 g) <= 448, so that no
+ * block scale saturates and the largest ones use the top of the E4M3 range; 1.0
+ * for amax = 0; 0.0 when amax is negative, not finite, or g would fall outside
+ * [2^-64, 2^64]. One pool has one g: pass max(amax[0], amax[1]).
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_HIP.
+ */
+size_t nvfp4_kv_amax_workspace_bytes(void);
+int32_t nvfp4_kv_amax(const void* k_src, const void* v_src, int32_t src_dtype, int64_t token_stride,
+                      int64_t head_stride, int64_t num_tokens, int32_t num_kv_heads, float* amax_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+float nvfp4kv_global_scale_for_amax(float amax);
+
+/*
  * ---- FP8 E4M3 baseline ------------------------------------------------------
  * The cache the pages compare NVFP4 against ([LMSYS] "Synopsis", "Perspective";
  * [EUROK] "Bytes pro Token": one byte per value), built with the same decode

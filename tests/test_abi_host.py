@@ -191,3 +191,35 @@ def test_fp8_baseline_validation(L):
     assert d(fp8_pool(), odt=2) == ERR_DTYPE
     assert d(fp8_pool(hkv=3), hq=8) == ERR_SHAPE
     assert d(fp8_pool(), B=0) == OK
+
+
+def test_global_scale_rule_matches_oracle(L):
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(81)
+    for a in list(np.exp(rng.uniform(np.log(1e-8), np.log(1e12), 400)).astype(np.float32)) + [0.0, 2688.0, 1344.0]:
+        g = B.nvfp4kv_global_scale_for_amax(float(a))
+        assert g == oracle.global_scale_for_amax(float(a)), a
+    assert B.nvfp4kv_global_scale_for_amax(float("nan")) == 0.0
+    assert B.nvfp4kv_global_scale_for_amax(-1.0) == 0.0
+    assert B.nvfp4kv_global_scale_for_amax(3e38) == 0.0  # g beyond 2^64
+
+
+def test_amax_validation(L):
+    ws_need = L.nvfp4_kv_amax_workspace_bytes()
+    assert ws_need == 256 * 2 * 4
+    a = lambda **kw: L.nvfp4_kv_amax(kw.get("k", FAKE), FAKE, kw.get("dt", 0), kw.get("ts", 1024), 128,
+                                     kw.get("T", 16), kw.get("hkv", 8), kw.get("out", FAKE), kw.get("ws", FAKE),
+                                     kw.get("wsb", ws_need), None)
+    assert a(dt=2) == ERR_DTYPE
+    assert a(T=-1) == ERR_SHAPE
+    assert a(hkv=0) == ERR_SHAPE
+    assert a(out=None) == ERR_NULL
+    assert a(ws=None) == ERR_NULL
+    assert a(k=None) == ERR_NULL
+    assert a(wsb=ws_need - 1) == ERR_WORKSPACE
+    assert a(k=FAKE + 4) == ERR_ALIGN
+    assert a(ts=1026) == ERR_ALIGN
+    assert a(out=FAKE + 2) == ERR_ALIGN
