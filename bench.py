@@ -224,7 +224,7 @@ def extend_step(w, pool, B, W, torch, steps, warmup):
         B.nvfp4_kv_quantize(kc, vc, cslots, pool, stream=stream)
         B.nvfp4_kv_dequant_workspace(pool, pts[i % 2], sl, ro, P, k_ws, v_ws, stream=stream)
         B.nvfp4_extend_attn(qc, k_ws, v_ws, kc, vc, w.sm_scale, out=att_out, stream=stream)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
         # the bf16 step: quantize the chunk, dequantize the prefix, attend; then
@@ -240,12 +240,20 @@ def extend_step(w, pool, B, W, torch, steps, warmup):
         ev[i][4].record(stream)
         B.nvfp4_extend_attn(qc, k_w8, v_w8, kc, vc, w.sm_scale, out=att_out, stream=stream)
         ev[i][5].record(stream)
+        # the fused prefill path: dequant, then attention that also quantize-writes the chunk
+        B.nvfp4_kv_dequant_workspace(pool, pts[i % 2], sl, ro, P, k_ws, v_ws, stream=stream)
+        ev[i][6].record(stream)
+        B.nvfp4_extend_attn(qc, k_ws, v_ws, kc, vc, w.sm_scale, out=att_out, chunk_pool=pool, chunk_slots=cslots,
+                            stream=stream)
+        ev[i][7].record(stream)
     torch.cuda.synchronize()
     q_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     d_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     a_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
     d8_ms = sum(e[3].elapsed_time(e[4]) for e in ev) / steps
     a8_ms = sum(e[4].elapsed_time(e[5]) for e in ev) / steps
+    df_ms = sum(e[5].elapsed_time(e[6]) for e in ev) / steps
+    af_ms = sum(e[6].elapsed_time(e[7]) for e in ev) / steps
     # attention flops: QK^T and PV, 2 x 128 multiply-adds per (query row, visible key)
     a_flops = 4 * w.num_q_heads * 128 * (C * P + C * (C + 1) // 2)
     q_bytes = C * w.num_kv_heads * 128 * 2 * 2 + C * w.num_kv_heads * 2 * 8 * 9  # bf16 in + NVFP4 out
@@ -262,7 +270,9 @@ def extend_step(w, pool, B, W, torch, steps, warmup):
             "attn_roofline": {"bound": "mfma", "achieved": round(a_flops / (a_ms * 1e-3) / 1e12, 1),
                               "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(a_flops / (a_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "attn_fused_write_ms": round(af_ms, 4),
             "step_ms": round(q_ms + d_ms + a_ms, 4), "step_fp8_ms": round(q_ms + d8_ms + a8_ms, 4),
+            "step_fused_ms": round(df_ms + af_ms, 4),
             "chunk_tokens": C, "prefix_tokens": P,
             "note": "two different prefixes alternate, so no repeat reads the previous one's bytes from the last-level cache"}
 

@@ -92,7 +92,7 @@ def lib() -> ctypes.CDLL:
                                                  P, P, c.c_int32, P]
         L.nvfp4_kv_dequant_workspace.restype = c.c_int32
         L.nvfp4_extend_attn.argtypes = [P, P, P, c.c_int32, c.c_int64, P, P, c.c_int64, c.c_int32, c.c_int32,
-                                        c.c_float, P, P, P]
+                                        c.c_float, P, P, c.POINTER(PoolDesc), P, P]
         L.nvfp4_extend_attn.restype = c.c_int32
         L.nvfp4_kv_amax_workspace_bytes.argtypes = []
         L.nvfp4_kv_amax_workspace_bytes.restype = c.c_size_t
@@ -295,11 +295,17 @@ def nvfp4_kv_dequant_workspace(pool: Pool, page_table: torch.Tensor, seq_lens: t
 
 def nvfp4_extend_attn(q: torch.Tensor, k_prefix: torch.Tensor, v_prefix: torch.Tensor, k_chunk: torch.Tensor,
                       v_chunk: torch.Tensor, sm_scale: float, out: torch.Tensor | None = None,
-                      lse: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                      lse: torch.Tensor | None = None, chunk_pool: "Pool | None" = None,
+                      chunk_slots: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Chunk queries q [C, Hq, 128] (bf16) over the prefix workspace k/v_prefix
     [P, Hkv, 128] (bfloat16 or float8_e4m3fn) and the chunk's own k/v_chunk
     [C, Hkv, 128] (bf16), causal over the chunk. Returns out [C, Hq, 128] bf16;
-    fills lse [C, Hq] (float32, natural log) when given."""
+    fills lse [C, Hq] (float32, natural log) when given. With chunk_pool and
+    chunk_slots (int32 [C]) the same launch quantize-writes the chunk into the pool."""
+    if (chunk_pool is None) != (chunk_slots is None):
+        raise ValueError("chunk_pool and chunk_slots go together")
+    if chunk_slots is not None and (chunk_slots.dtype != torch.int32 or chunk_slots.numel() != q.shape[0]):
+        raise ValueError("chunk_slots must be int32 [C]")
     for name, t in (("q", q), ("k_chunk", k_chunk), ("v_chunk", v_chunk)):
         if t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous bfloat16")
@@ -317,7 +323,8 @@ def nvfp4_extend_attn(q: torch.Tensor, k_prefix: torch.Tensor, v_prefix: torch.T
     _check("nvfp4_extend_attn",
            lib().nvfp4_extend_attn(_ptr(q), _ptr(k_prefix) if P else None, _ptr(v_prefix) if P else None, pdt, P,
                                    _ptr(k_chunk), _ptr(v_chunk), C, hq, hkv, float(sm_scale), _ptr(out), _ptr(lse),
-                                   _stream(stream)))
+                                   ctypes.byref(chunk_pool.desc()) if chunk_pool is not None else None,
+                                   _ptr(chunk_slots), _stream(stream)))
     return out
 
 

@@ -417,7 +417,11 @@ int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page
 int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_prefix, int32_t prefix_dtype,
                           int64_t prefix_len, const void* k_chunk, const void* v_chunk, int64_t chunk_len,
                           int32_t num_q_heads, int32_t num_kv_heads, float sm_scale, void* out, float* lse,
-                          void* stream) {
+                          const nvfp4kv_pool* chunk_pool, const int32_t* chunk_slots, void* stream) {
+  if (chunk_pool) {
+    if (int32_t e = check_pool(chunk_pool)) return e;
+    if (chunk_pool->num_kv_heads != num_kv_heads) return NVFP4KV_ERR_SHAPE;
+  }
   if (prefix_dtype != NVFP4KV_BF16 && prefix_dtype != NVFP4KV_FP8_E4M3) return NVFP4KV_ERR_DTYPE;
   if (prefix_len < 0 || chunk_len < 0 || num_q_heads < 1 || num_kv_heads < 1) return NVFP4KV_ERR_SHAPE;
   if (num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > NVFP4KV_MAX_GROUP) return NVFP4KV_ERR_SHAPE;
@@ -428,6 +432,8 @@ int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_pre
   if (!isfinite(sm_scale)) return NVFP4KV_ERR_VALUE;
   if (chunk_len == 0) return NVFP4KV_OK;
   if (!q || !k_chunk || !v_chunk || !out || (prefix_len > 0 && (!k_prefix || !v_prefix))) return NVFP4KV_ERR_NULL;
+  if (chunk_pool && !chunk_slots) return NVFP4KV_ERR_NULL;
+  if (chunk_slots && (reinterpret_cast<uintptr_t>(chunk_slots) & 3u)) return NVFP4KV_ERR_ALIGN;
   if (!aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(out) ||
       (prefix_len > 0 && (!aligned16(k_prefix) || !aligned16(v_prefix))) || (reinterpret_cast<uintptr_t>(lse) & 3u))
     return NVFP4KV_ERR_ALIGN;
@@ -451,6 +457,22 @@ int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_pre
   const int64_t blocks = (chunk_len + a.tokens_per_block - 1) / a.tokens_per_block;
   if (blocks * num_kv_heads > ((int64_t)1 << 31) - 1) return NVFP4KV_ERR_SHAPE;
   a.num_token_blocks = (int32_t)blocks;
+  a.write_chunk = chunk_pool != nullptr;
+  if (chunk_pool) {
+    nvfp4kv::QuantizeArgs& w = a.qw;
+    w.k = k_chunk;
+    w.v = v_chunk;
+    w.bf16 = 1;
+    w.token_stride = (int64_t)num_kv_heads * NVFP4KV_HEAD_DIM;
+    w.head_stride = NVFP4KV_HEAD_DIM;
+    w.slots = chunk_slots;
+    w.num_tokens = chunk_len;
+    w.pool = static_cast<uint8_t*>(chunk_pool->data);
+    w.num_kv_heads = num_kv_heads;
+    w.g = chunk_pool->global_scale;
+    w.fp8 = 0;
+    w.inv_k_scale = w.inv_v_scale = 1.0f;
+  }
   return hip_status(nvfp4kv::launch_extend(a, static_cast<hipStream_t>(stream)));
 }
 

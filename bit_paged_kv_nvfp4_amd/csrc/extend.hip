@@ -32,6 +32,9 @@
 // K enters the first product as bf16, V the second as f16: exact for every
 // value of magnitude below 65504, which covers every NVFP4- or FP8-derived
 // workspace value (at g = 1) and every chunk value a model produces.
+// With a pool given, the kernel also quantize-writes the chunk's K/V into it
+// (the prefill path's quantize fused into the attention), each workgroup the
+// blocks of its own tokens and KV head.
 // Online softmax in fp32, base 2, with a lazy rescale (the running max moves
 // only when a tile's max exceeds it by more than 2^8, so P <= 256); P enters
 // the second product as f16 (11 significant bits, where bf16 would keep 8 and
@@ -39,6 +42,7 @@
 // the same rounded values, on the matrix cores (an all-ones operand).
 #include "nvfp4kv.h"
 #include "nvfp4kv_device.h"
+#include "quantize_block.h"
 
 namespace nvfp4kv {
 namespace {
@@ -209,6 +213,15 @@ __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   const int64_t t_last = min(t_first + a.tokens_per_block, C) - 1;
   const int n_pre = (int)((P + kTile - 1) / kTile);
   const int n_tiles = n_pre + (int)((t_last + kTile) / kTile);  // chunk keys 0 .. t_last
+
+  // Fused quantize-on-write of the chunk (the prefill path): this workgroup
+  // encodes its own tokens' K/V blocks for its KV head into the NVFP4 pool; the
+  // attention below reads the bf16 chunk, so the two do not depend on each other.
+  if (a.write_chunk) {
+    const int64_t n_blk = (t_last - t_first + 1) * 16;
+    for (int64_t idx = t; idx < n_blk; idx += kXThreads)
+      qenc::quantize_one(a.qw, t_first + idx / 16, h, (int)((idx >> 3) & 1), (int)(idx & 7));
+  }
 
   __shared__ __attribute__((aligned(16))) uint8_t k_ring[kStages][kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t v_ring[kStages][kStageBytes];

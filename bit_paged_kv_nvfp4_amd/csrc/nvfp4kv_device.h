@@ -188,6 +188,8 @@ struct ExtendArgs {
   float* lse;              // [C][Hq] natural log, or null
   int32_t tokens_per_block;
   int32_t num_token_blocks;
+  int32_t write_chunk;     // 1: also quantize-write the chunk's K/V into an NVFP4 pool
+  QuantizeArgs qw;         // that write (chunk K/V, its slots, the pool)
 };
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);

@@ -7,87 +7,13 @@
 // "Bytes pro Token"): E2M1 values, one E4M3 scale per 16 values, one FP32 scale
 // per tensor.
 //
-// One thread encodes one 16-value block (token, KV head, K|V, block). Every
-// rounding decision is taken by exact comparisons in fp32: the thresholds are
-// products of numbers with few significant bits and a power-of-two global scale,
-// so no quotient is ever rounded. This realizes "nearest, ties to even" on the
-// exact real quotients amax/(6g) and x/(E4M3(s) g).
+// One thread encodes one 16-value block (token, KV head, K|V, block); the encode
+// and write rules are in quantize_block.h.
 #include "nvfp4kv_device.h"
+#include "quantize_block.h"
 
 namespace nvfp4kv {
 namespace {
-
-// E4M3 value of a non-negative finite byte k (0..126), exact in fp32.
-__device__ __forceinline__ float e4m3_value(int k) {
-  return k < 8 ? (float)k * 0x1p-9f : __builtin_ldexpf((float)(8 + (k & 7)), (k >> 3) - 10);
-}
-
-// Byte of the E4M3 value nearest to amax / six_g (six_g = 6 g), ties to the even
-// byte, clamped to 448 (0x7E). Binary search for the first midpoint between
-// consecutive E4M3 values that amax does not pass; a tie passes the midpoint
-// only when its lower neighbour is odd.
-__device__ __forceinline__ int scale_byte(float amax, float six_g) {
-  int lo = 0, hi = 126;
-#pragma unroll
-  for (int it = 0; it < 7; ++it) {
-    if (lo < hi) {
-      const int k = (lo + hi) >> 1;
-      const float thr = (0.5f * (e4m3_value(k) + e4m3_value(k + 1))) * six_g;
-      const bool pass = amax > thr || (amax == thr && (k & 1));
-      lo = pass ? k + 1 : lo;
-      hi = pass ? hi : k;
-    }
-  }
-  return lo;
-}
-
-// E2M1 code of x for block divisor D = E4M3(s) g: count of the magnitude
-// midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 (times D) that |x| passes, where
-// a tie passes only midpoints whose lower code is odd; sign bit from x.
-__device__ __forceinline__ uint32_t e2m1_code(float x, float D, bool zero_scale) {
-  const uint32_t sign = (__float_as_uint(x) >> 28) & 8u;
-  const float ax = __builtin_fabsf(x);
-  uint32_t c = (uint32_t)(ax > 0.25f * D) + (uint32_t)(ax >= 0.75f * D) + (uint32_t)(ax > 1.25f * D) +
-               (uint32_t)(ax >= 1.75f * D) + (uint32_t)(ax > 2.5f * D) + (uint32_t)(ax >= 3.5f * D) +
-               (uint32_t)(ax > 5.0f * D);
-  c = zero_scale ? 0u : c;
-  return sign | c;
-}
-
-// Codes and scale byte of block j (16 values) of token t, head h, kind (0 K, 1 V).
-__device__ __forceinline__ void encode_block(const QuantizeArgs& a, int64_t t, int h, int kind, int j,
-                                             uint32_t (&code)[16], int& s) {
-  const int64_t off = t * a.token_stride + (int64_t)h * a.head_stride + j * 16;
-  float x[16];
-  if (a.bf16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(kind ? a.v : a.k) + off);
-    const uint4 u0 = p[0], u1 = p[1];
-    const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(kind ? a.v : a.k) + off);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 f = p[i];
-      x[4 * i] = f.x;
-      x[4 * i + 1] = f.y;
-      x[4 * i + 2] = f.z;
-      x[4 * i + 3] = f.w;
-    }
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
-  s = scale_byte(amax, 6.0f * a.g);
-  const float D = e4m3_value(s) * a.g;
-  const bool zs = (s == 0);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) code[i] = e2m1_code(x[i], D, zs);
-}
 
 __global__ __launch_bounds__(256) void k_quantize(QuantizeArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -95,88 +21,7 @@ __global__ __launch_bounds__(256) void k_quantize(QuantizeArgs a) {
   if (idx >= a.num_tokens * per_token) return;
   const int64_t t = idx / per_token;
   const int rem = (int)(idx - t * per_token);
-  const int h = rem >> 4;
-  const int kind = (rem >> 3) & 1;
-  const int j = rem & 7;
-  const int32_t slot = a.slots[t];
-  if (slot < 0) return;
-  const int64_t page = slot >> 4;
-  const int row = slot & 15;
-  uint8_t* slab = a.pool + ((page * a.num_kv_heads + h) * 2 + kind) * (int64_t)kSlab;
-
-  if (kind == 1) {
-    // V: a code byte holds rows r and r ^ 2 and a 32-bit word rows 4g .. 4g+3 of
-    // one page. When this call writes those four rows as four consecutive tokens,
-    // the thread of the first one encodes all four and writes whole words.
-    const int r4 = row & 3;
-    const int64_t tl = t - r4;
-    bool full = tl >= 0 && tl + 3 < a.num_tokens;
-    const int32_t s0 = full ? a.slots[tl] : -1;
-    full = full && s0 >= 0 && (s0 & 3) == 0;
-#pragma unroll
-    for (int i = 1; i < 4; ++i) full = full && a.slots[tl + i] == s0 + i;
-    if (full) {
-      if (r4 != 0) return;  // written by the group's first token
-      uint32_t c4[4][16];
-      int s4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) encode_block(a, t + i, h, 1, j, c4[i], s4[i]);
-      // chunk (row/4)*16 + 2j + c holds channels 16j + 8c .. +7; its word wi holds
-      // channel q = 8c + 2wi (bytes 0, 1) and q + 1 (bytes 2, 3), rows 0|2 in the
-      // even byte and rows 1|3 in the odd one
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        uint32_t w[4];
-#pragma unroll
-        for (int wi = 0; wi < 4; ++wi) {
-          const int q = 8 * c + 2 * wi;
-          w[wi] = (c4[0][q] | (c4[2][q] << 4)) | ((c4[1][q] | (c4[3][q] << 4)) << 8) |
-                  ((c4[0][q + 1] | (c4[2][q + 1] << 4)) << 16) | ((c4[1][q + 1] | (c4[3][q + 1] << 4)) << 24);
-        }
-        *reinterpret_cast<uint4*>(slab + ((row >> 2) * 16 + 2 * j + c) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-      *reinterpret_cast<uint32_t*>(slab + kCodeBytes + j * 16 + row) =
-          (uint32_t)s4[0] | ((uint32_t)s4[1] << 8) | ((uint32_t)s4[2] << 16) | ((uint32_t)s4[3] << 24);
-      return;
-    }
-  }
-
-  uint32_t code[16];
-  int s;
-  encode_block(a, t, h, kind, j, code, s);
-  if (kind == 0) {
-    // K: the token's 8 code bytes of block j are contiguous, channel 2i in the low
-    // nibble of byte i
-    uint32_t w[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      w[half] = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[half] |= code[8 * half + i] << (4 * i);
-    }
-    *reinterpret_cast<uint2*>(slab + row * 64 + j * 8) = make_uint2(w[0], w[1]);
-    slab[kCodeBytes + row * 8 + j] = (uint8_t)s;
-  } else {
-    // V, a token alone in its four-row group: channel 16j + e sits in 16-byte
-    // chunk (row/4)*16 + 2j + e/8, byte 2*(e%8) + row%2, high nibble for rows with
-    // row%4 >= 2; the other nibble of each byte is row r ^ 2 of the same page,
-    // which another thread (or another call) may be writing, so the block's
-    // nibbles are cleared and set with 32-bit atomics that leave every other bit
-    // alone.
-    const int sh = 8 * (row & 1) + 4 * ((row >> 1) & 1);
-    const uint32_t mask = (0xFu << sh) | (0xFu << (sh + 16));
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      uint32_t* chunk = reinterpret_cast<uint32_t*>(slab + ((row >> 2) * 16 + 2 * j + c) * 16);
-#pragma unroll
-      for (int wi = 0; wi < 4; ++wi) {
-        const uint32_t val = (code[8 * c + 2 * wi] << sh) | (code[8 * c + 2 * wi + 1] << (sh + 16));
-        __hip_atomic_fetch_and(chunk + wi, ~mask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_or(chunk + wi, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    slab[kCodeBytes + j * 16 + row] = (uint8_t)s;
-  }
+  qenc::quantize_one(a, t, rem >> 4, (rem >> 3) & 1, rem & 7);
 }
 
 // FP8 baseline quantize-on-write: one thread per (token, KV head, K|V, 16-value

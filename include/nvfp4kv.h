@@ -344,13 +344,22 @@ int32_t fp8_paged_decode_attn_partial(const void* q, const int32_t* page_table, 
  * softmax weights enter the second product rounded to bf16 (the row sums use
  * the same rounded weights). All device pointers 16-byte aligned; nothing is
  * allocated; the call is asynchronous on `stream`.
- * Errors: ERR_NULL, ERR_SHAPE (counts out of range, group > 16), ERR_ALIGN,
- * ERR_DTYPE (prefix_dtype), ERR_VALUE (sm_scale not finite), ERR_HIP.
+ * Fused quantize-on-write ([LMSYS] "Interpretation": the prefill path writes
+ * the prompt's keys and values into the NVFP4 cache): when chunk_pool is not
+ * NULL, the same launch also writes chunk token i's K/V to slot chunk_slots[i]
+ * of chunk_pool, with exactly the bytes nvfp4_kv_quantize would write (same
+ * rules, negative slots skipped; chunk_pool->num_kv_heads must equal
+ * num_kv_heads). The attention reads the bf16 chunk, not those bytes.
+ *   chunk_pool      NVFP4 pool or NULL (no write)
+ *   chunk_slots     device int32 [C] when chunk_pool is given
+ * Errors: ERR_NULL, ERR_SHAPE (counts out of range, group > 16, pool heads),
+ * ERR_ALIGN, ERR_DTYPE (prefix_dtype), ERR_VALUE (sm_scale not finite, pool
+ * global scale), ERR_HIP.
  */
 int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_prefix, int32_t prefix_dtype,
                           int64_t prefix_len, const void* k_chunk, const void* v_chunk, int64_t chunk_len,
                           int32_t num_q_heads, int32_t num_kv_heads, float sm_scale, void* out, float* lse,
-                          void* stream);
+                          const nvfp4kv_pool* chunk_pool, const int32_t* chunk_slots, void* stream);
 
 #ifdef __cplusplus
 }

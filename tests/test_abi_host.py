@@ -137,7 +137,7 @@ def test_dequant_validation(L):
 
 def e_call(L, q=FAKE, kp=FAKE, vp=FAKE, pdt=1, P=100, kc=FAKE, vc=FAKE, C=10, hq=8, hkv=1, sm=0.088, out=FAKE,
            lse=None):
-    return L.nvfp4_extend_attn(q, kp, vp, pdt, P, kc, vc, C, hq, hkv, sm, out, lse, None)
+    return L.nvfp4_extend_attn(q, kp, vp, pdt, P, kc, vc, C, hq, hkv, sm, out, lse, None, None, None)
 
 
 def test_extend_validation(L):
@@ -223,3 +223,13 @@ def test_amax_validation(L):
     assert a(k=FAKE + 4) == ERR_ALIGN
     assert a(ts=1026) == ERR_ALIGN
     assert a(out=FAKE + 2) == ERR_ALIGN
+
+
+def test_extend_fused_write_validation(L):
+    p = pool(hkv=1)
+    call = lambda pl, slots: L.nvfp4_extend_attn(FAKE, FAKE, FAKE, 1, 100, FAKE, FAKE, 10, 8, 1, 0.088, FAKE, None,
+                                                 ctypes.byref(pl) if pl is not None else None, slots, None)
+    assert call(pool(hkv=2), FAKE) == ERR_SHAPE  # pool heads differ
+    assert call(pool(g=3.0, hkv=1), FAKE) == ERR_VALUE
+    assert call(p, None) == ERR_NULL
+    assert call(p, FAKE + 2) == ERR_ALIGN

@@ -112,3 +112,51 @@ def test_extend_full_size_sampled_rows(dt):
     err = assert_close(out[ti, hi], ref[ti, hi], what="sampled rows (unit order as listed)")
     assert_close(lse[ti, hi], ref_lse[ti, hi], atol=1e-3, rtol=1e-4, what="sampled lse")
     print(f"  max abs err {err:.3e} over {len(units)} rows")
+
+
+@pytest.mark.parametrize("P,C,hq,hkv", [(50, 70, 16, 2), (64, 33, 8, 1)])
+def test_extend_fused_chunk_write_bytes_and_output(P, C, hq, hkv):
+    """With a pool, the extend launch also quantize-writes the chunk: its bytes
+    equal the oracle's quantize of the same chunk (over the same stale bytes;
+    P = 50 leaves the first four-row V group incomplete, so both the grouped and
+    the single-row V writes run), and the attention output is the same as
+    without the write."""
+    print(f"fused write P={P} C={C} Hq={hq} Hkv={hkv}", flush=True)
+    q, kp, vp, kc, vc = W.extend_inputs(500 + P, P, C, hq, hkv)
+    w = W.small_workload(501 + P, 1, hq, hkv, [P + C])
+    slots = W.slots(w, 0, P, P + C)
+    stale = np.full(oracle.pool_bytes(w.num_pages, hkv), 0xA5, dtype=np.uint8)
+    gpool = B.Pool(w.num_pages, hkv, device="cuda", data=torch.as_tensor(stale.copy(), device="cuda"))
+    sm = 128 ** -0.5
+    plain, _ = _run(q, kp, vp, kc, vc, sm)
+    out = B.nvfp4_extend_attn(q.cuda(), kp.cuda(), vp.cuda(), kc.cuda(), vc.cuda(), sm, chunk_pool=gpool,
+                              chunk_slots=torch.as_tensor(slots, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy(), plain)
+    opool = stale.copy()
+    oracle.quantize_to_pool(bf16_bits(kc), bf16_bits(vc), slots, w.num_pages, pool=opool)
+    got = gpool.data.cpu().numpy()
+    assert np.array_equal(got, opool), f"pool bytes differ at {np.flatnonzero(got != opool)[:8]}"
+
+
+def test_extend_fused_chunk_write_full_size():
+    """Workload 5's 8192-token bf16 chunk written by the extend launch into the
+    extend request's pages, checked byte for byte against the oracle."""
+    w = W.config(5)
+    P, C, hq, hkv = w.extend_prefix, w.extend_chunk, w.num_q_heads, w.num_kv_heads
+    print(f"fused write full size P={P} C={C}", flush=True)
+    _, kp, vp, _, _ = W.extend_inputs(w.seed, 64, 1, hq, hkv, device="cuda")  # the write does not read the prefix
+    kc, vc = W.extend_chunk_kv(w, device="cuda")
+    qc = W.extend_query(w, device="cuda")
+    slots = W.slots(w, w.extend_row, P, P + C)
+    pages = np.unique(slots // 16)
+    gpool = B.Pool(w.num_pages, hkv, device="cuda")
+    B.nvfp4_extend_attn(qc, kp, vp, kc, vc, w.sm_scale, chunk_pool=gpool,
+                        chunk_slots=torch.as_tensor(slots, device="cuda"))
+    torch.cuda.synchronize()
+    opool = np.zeros(oracle.pool_bytes(w.num_pages, hkv), dtype=np.uint8)
+    oracle.quantize_to_pool(bf16_bits(kc), bf16_bits(vc), slots, w.num_pages, pool=opool, n_threads=8)
+    slab_pages = torch.as_tensor(pages, device="cuda", dtype=torch.long)
+    got = gpool.data.view(w.num_pages, -1)[slab_pages].cpu().numpy()
+    ref = opool.reshape(w.num_pages, -1)[pages]
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} bytes differ"
