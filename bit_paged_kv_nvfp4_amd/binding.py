@@ -32,6 +32,7 @@ EXPORTED = [
     "nvfp4_paged_decode_attn",
     "nvfp4_paged_decode_attn_partial",
     "nvfp4_decode_combine",
+    "nvfp4_paged_decode_attn_append",
     "nvfp4_kv_dequant_workspace",
     "nvfp4_extend_attn",
     "nvfp4_kv_amax_workspace_bytes",
@@ -42,6 +43,7 @@ EXPORTED = [
     "fp8_paged_decode_attn_default_splits",
     "fp8_paged_decode_attn",
     "fp8_paged_decode_attn_partial",
+    "fp8_paged_decode_attn_append",
 ]
 
 
@@ -86,6 +88,12 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_paged_decode_attn_partial.argtypes = [P, P, c.c_int64, P, c.c_int32, c.c_int32, c.c_int32,
                                                       c.POINTER(PoolDesc), c.c_float, c.c_int32, P, c.c_size_t, P]
         L.nvfp4_paged_decode_attn_partial.restype = c.c_int32
+        append_args = [P, P, P, c.c_int32, c.c_int64, c.c_int64, P, c.c_int64, P, c.c_int32, c.c_int32, c.c_int32]
+        tail_args = [c.c_float, c.c_int32, P, c.c_size_t, P, c.c_int32, P, P]
+        L.nvfp4_paged_decode_attn_append.argtypes = append_args + [c.POINTER(PoolDesc)] + tail_args
+        L.nvfp4_paged_decode_attn_append.restype = c.c_int32
+        L.fp8_paged_decode_attn_append.argtypes = append_args + [c.POINTER(Fp8PoolDesc)] + tail_args
+        L.fp8_paged_decode_attn_append.restype = c.c_int32
         L.nvfp4_decode_combine.argtypes = [P, c.c_size_t, c.c_int32, c.c_int32, c.c_int32, P, c.c_int32, P, P]
         L.nvfp4_decode_combine.restype = c.c_int32
         L.nvfp4_kv_dequant_workspace.argtypes = [c.POINTER(PoolDesc), P, c.c_int64, P, P, c.c_int32, c.c_int32,
@@ -248,6 +256,58 @@ def nvfp4_paged_decode_attn(q: torch.Tensor, page_table: torch.Tensor, seq_lens:
     return out
 
 
+def _decode_append(name: str, default_splits, q, k_new, v_new, page_table, seq_lens, pool, sm_scale, max_seq_len,
+                   num_splits, workspace, out, out_dtype, lse, stream, combine):
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [B, Hq, 128] tensor")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_contiguous():
+        raise ValueError("page_table must be contiguous int32 [B, stride]")
+    B, hq, _ = q.shape
+    for nm, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.dim() != 3 or tuple(t.shape) != (B, pool.num_kv_heads, HEAD_DIM) or t.stride(2) != 1:
+            raise ValueError(f"{nm} must be [B, Hkv, 128] with unit channel stride")
+    if k_new.dtype != v_new.dtype or k_new.stride() != v_new.stride():
+        raise ValueError("k_new and v_new must share dtype and strides")
+    ndt = {torch.float32: F32, torch.bfloat16: BF16}.get(k_new.dtype)
+    if ndt is None:
+        raise ValueError("k_new/v_new must be float32 or bfloat16")
+    if num_splits == 0:
+        num_splits = default_splits(B, pool.num_kv_heads, max_seq_len)
+    if workspace is None:
+        nbytes = nvfp4_paged_decode_attn_workspace_bytes(B, hq, num_splits)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if not combine:
+        if workspace is None or out is not None or lse is not None:
+            raise ValueError("phase 1 alone needs a workspace and takes no out/lse")
+        odt = F32
+    else:
+        if out is None:
+            out = torch.empty((B, hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+        odt = {torch.float32: F32, torch.bfloat16: BF16}.get(out.dtype)
+        if odt is None or not out.is_contiguous():
+            raise ValueError("out must be contiguous float32 or bfloat16")
+    d = pool.desc()
+    _check(name, getattr(lib(), name)(_ptr(q), _ptr(k_new), _ptr(v_new), ndt, k_new.stride(0), k_new.stride(1),
+                                      _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, hq, int(max_seq_len),
+                                      ctypes.byref(d), float(sm_scale), int(num_splits), _ptr(workspace),
+                                      workspace.numel(), _ptr(out), odt, _ptr(lse), _stream(stream)))
+    return out
+
+
+def nvfp4_paged_decode_attn_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                   page_table: torch.Tensor, seq_lens: torch.Tensor, pool: Pool, sm_scale: float,
+                                   max_seq_len: int, num_splits: int = 0, workspace: torch.Tensor | None = None,
+                                   out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.bfloat16,
+                                   lse: torch.Tensor | None = None, stream=None, combine: bool = True):
+    """One decode step in one split launch: writes k_new/v_new [B, Hkv, 128]
+    (float32 or bfloat16) as token seq_lens[b] - 1 of each sequence into the pool,
+    then attends as nvfp4_paged_decode_attn over the updated cache. With
+    combine=False only phase 1 runs (states left in ``workspace``; returns None)."""
+    return _decode_append("nvfp4_paged_decode_attn_append", nvfp4_paged_decode_attn_default_splits, q, k_new, v_new,
+                          page_table, seq_lens, pool, sm_scale, max_seq_len, num_splits, workspace, out, out_dtype,
+                          lse, stream, combine)
+
+
 def nvfp4_paged_decode_attn_partial(q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor, pool: Pool,
                                     sm_scale: float, max_seq_len: int, num_splits: int, workspace: torch.Tensor,
                                     stream=None):
@@ -373,6 +433,17 @@ def fp8_paged_decode_attn_partial(q: torch.Tensor, page_table: torch.Tensor, seq
            lib().fp8_paged_decode_attn_partial(_ptr(q), _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B,
                                                hq, int(max_seq_len), ctypes.byref(d), float(sm_scale),
                                                int(num_splits), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def fp8_paged_decode_attn_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                 page_table: torch.Tensor, seq_lens: torch.Tensor, pool: Fp8Pool, sm_scale: float,
+                                 max_seq_len: int, num_splits: int = 0, workspace: torch.Tensor | None = None,
+                                 out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.bfloat16,
+                                 lse: torch.Tensor | None = None, stream=None, combine: bool = True):
+    """As nvfp4_paged_decode_attn_append, over an FP8 baseline pool."""
+    return _decode_append("fp8_paged_decode_attn_append", fp8_paged_decode_attn_default_splits, q, k_new, v_new,
+                          page_table, seq_lens, pool, sm_scale, max_seq_len, num_splits, workspace, out, out_dtype,
+                          lse, stream, combine)
 
 
 def nvfp4_kv_amax(k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

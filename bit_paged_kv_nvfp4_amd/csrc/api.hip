@@ -273,6 +273,8 @@ int32_t prepare_decode(const void* q, const int32_t* page_table, int64_t page_ta
   a.num_workgroups = cus > 0 ? nvfp4kv::decode_resident_workgroups(cus, pool.fp8) : 0;  // 0: finish_decode sets it
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = a.part_o + (size_t)batch * num_q_heads * *num_splits * NVFP4KV_HEAD_DIM;
+  a.write_new = 0;
+  a.nw = nvfp4kv::QuantizeArgs{};
   a.out = nullptr;
   a.out_bf16 = 0;
   a.lse = nullptr;
@@ -315,16 +317,61 @@ int32_t decode_partial(const void* q, const int32_t* page_table, int64_t page_ta
   return hip_status(nvfp4kv::launch_decode_partial(a, static_cast<hipStream_t>(stream)));
 }
 
+// The newest token's K/V rows of each sequence, for the decode launches that
+// write them into the pool themselves.
+struct NewRows {
+  const void* k;
+  const void* v;
+  int32_t dtype;
+  int64_t token_stride;
+  int64_t head_stride;
+};
+
+// Validates the new rows (as quantize_into does its sources) and points a.nw at
+// them; batch rows, one per sequence.
+int32_t prepare_new_rows(const NewRows& n, int32_t batch, const PoolInfo& pool, nvfp4kv::DecodeArgs& a) {
+  if (n.dtype != NVFP4KV_F32 && n.dtype != NVFP4KV_BF16) return NVFP4KV_ERR_DTYPE;
+  if (n.token_stride < 0 || n.head_stride < 0) return NVFP4KV_ERR_SHAPE;
+  if (batch == 0) return NVFP4KV_OK;
+  if (!n.k || !n.v) return NVFP4KV_ERR_NULL;
+  const int64_t vec = n.dtype == NVFP4KV_F32 ? 4 : 8;
+  if (!aligned16(n.k) || !aligned16(n.v) || n.token_stride % vec || n.head_stride % vec) return NVFP4KV_ERR_ALIGN;
+  a.write_new = 1;
+  a.nw.k = n.k;
+  a.nw.v = n.v;
+  a.nw.bf16 = n.dtype == NVFP4KV_BF16;
+  a.nw.token_stride = n.token_stride;
+  a.nw.head_stride = n.head_stride;
+  a.nw.slots = nullptr;
+  a.nw.num_tokens = batch;
+  a.nw.pool = static_cast<uint8_t*>(pool.data);
+  a.nw.num_kv_heads = pool.num_kv_heads;
+  a.nw.g = pool.k_mul;
+  a.nw.fp8 = pool.fp8;
+  a.nw.inv_k_scale = 1.0f / pool.k_mul;  // powers of two: exact
+  a.nw.inv_v_scale = 1.0f / pool.v_mul;
+  return NVFP4KV_OK;
+}
+
 int32_t decode_full(const void* q, const int32_t* page_table, int64_t page_table_stride, const int32_t* seq_lens,
                     int32_t batch, int32_t num_q_heads, int32_t max_seq_len, const PoolInfo& pool, float sm_scale,
                     int32_t num_splits, void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
-                    float* lse, void* stream) {
+                    float* lse, void* stream, const NewRows* new_rows = nullptr) {
   nvfp4kv::DecodeArgs a;
   if (out_dtype != NVFP4KV_F32 && out_dtype != NVFP4KV_BF16) return NVFP4KV_ERR_DTYPE;
   if (int32_t e = prepare_decode(q, page_table, page_table_stride, seq_lens, batch, num_q_heads, max_seq_len, pool,
                                  sm_scale, &num_splits, workspace, workspace_bytes, a))
     return e;
+  if (new_rows)
+    if (int32_t e = prepare_new_rows(*new_rows, batch, pool, a)) return e;
+  // the fused step without `out` stops after phase 1 (states in the workspace)
+  const bool phase1_only = new_rows && !out;
+  if (phase1_only && lse) return NVFP4KV_ERR_NULL;
   if (batch == 0) return NVFP4KV_OK;
+  if (phase1_only) {
+    if (int32_t e = finish_decode(a)) return e;
+    return hip_status(nvfp4kv::launch_decode_partial(a, static_cast<hipStream_t>(stream)));
+  }
   nvfp4kv::DecodeArgs c;
   if (int32_t e = prepare_combine(workspace, workspace_bytes, batch, num_q_heads, num_splits, out, out_dtype, lse, c))
     return e;
@@ -372,6 +419,30 @@ int32_t fp8_paged_decode_attn(const void* q, const int32_t* page_table, int64_t 
   if (int32_t e = check_fp8_pool(pool)) return e;
   return decode_full(q, page_table, page_table_stride, seq_lens, batch, num_q_heads, max_seq_len, info_of(pool),
                      sm_scale, num_splits, workspace, workspace_bytes, out, out_dtype, lse, stream);
+}
+
+int32_t nvfp4_paged_decode_attn_append(const void* q, const void* k_new, const void* v_new, int32_t new_dtype,
+                                       int64_t new_token_stride, int64_t new_head_stride, const int32_t* page_table,
+                                       int64_t page_table_stride, const int32_t* seq_lens, int32_t batch,
+                                       int32_t num_q_heads, int32_t max_seq_len, const nvfp4kv_pool* pool,
+                                       float sm_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                       void* out, int32_t out_dtype, float* lse, void* stream) {
+  if (int32_t e = check_pool(pool)) return e;
+  const NewRows n{k_new, v_new, new_dtype, new_token_stride, new_head_stride};
+  return decode_full(q, page_table, page_table_stride, seq_lens, batch, num_q_heads, max_seq_len, info_of(pool),
+                     sm_scale, num_splits, workspace, workspace_bytes, out, out_dtype, lse, stream, &n);
+}
+
+int32_t fp8_paged_decode_attn_append(const void* q, const void* k_new, const void* v_new, int32_t new_dtype,
+                                     int64_t new_token_stride, int64_t new_head_stride, const int32_t* page_table,
+                                     int64_t page_table_stride, const int32_t* seq_lens, int32_t batch,
+                                     int32_t num_q_heads, int32_t max_seq_len, const fp8kv_pool* pool, float sm_scale,
+                                     int32_t num_splits, void* workspace, size_t workspace_bytes, void* out,
+                                     int32_t out_dtype, float* lse, void* stream) {
+  if (int32_t e = check_fp8_pool(pool)) return e;
+  const NewRows n{k_new, v_new, new_dtype, new_token_stride, new_head_stride};
+  return decode_full(q, page_table, page_table_stride, seq_lens, batch, num_q_heads, max_seq_len, info_of(pool),
+                     sm_scale, num_splits, workspace, workspace_bytes, out, out_dtype, lse, stream, &n);
 }
 
 int32_t nvfp4_decode_combine(const void* workspace, size_t workspace_bytes, int32_t batch, int32_t num_q_heads,

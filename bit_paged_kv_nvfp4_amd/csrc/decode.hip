@@ -34,6 +34,7 @@
 // max exceeds it by more than 2^8, which keeps P <= 256 (exact enough in f16) and
 // skips most accumulator rescales.
 #include "nvfp4kv_device.h"
+#include "quantize_block.h"
 
 namespace nvfp4kv {
 namespace {
@@ -171,6 +172,13 @@ struct Nvfp4Page {
     return r;
   }
 
+  // Encode block j of K (kind 0) or V (kind 1) of token t of the new rows into
+  // `slot`. The token is alone in this launch, so V nibbles go in with atomics.
+  __device__ static __forceinline__ void write_new(const QuantizeArgs& a, int64_t t, int64_t slot, int h, int kind,
+                                                   int j) {
+    qenc::write_block(a, t, slot, h, kind, j, false);
+  }
+
   // S^T = K^ Q^T for each page (two independent MFMA chains).
   __device__ static __forceinline__ void scores(const Regs& ra, const Regs& rb, const f16x8 (&qf)[4], f32x4& sa,
                                                 f32x4& sb) {
@@ -257,6 +265,11 @@ struct Fp8Page {
     r.v0 = *reinterpret_cast<const uint4*>(slot + 2048 + 16 * lane);
     r.v1 = *reinterpret_cast<const uint4*>(slot + 3072 + 16 * lane);
     return r;
+  }
+
+  __device__ static __forceinline__ void write_new(const QuantizeArgs& a, int64_t t, int64_t slot, int h, int kind,
+                                                   int j) {
+    qenc::write_block_fp8(a, t, slot, h, kind, j);
   }
 
   // Four E4M3 bytes of w as exact f16 (the converter's scale operand stays 1.0).
@@ -414,7 +427,21 @@ __device__ __forceinline__ void wave_share(const DecodeArgs& a, int b, int h, in
   for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (pg0 >= pg1) return;
 
-  const int L = load_uniform(a.seq_lens, b);
+  const int L = load_uniform(a.seq_lens, b);  // >= 1: the share is not empty
+  if (a.write_new) {
+    // The sequence's newest token (position L - 1) goes into the pool first,
+    // written by the wave whose share holds its page and finished before any
+    // copy of that page: 16 lanes, one block (K or V, 16 channels) each.
+    const int last = (L - 1) / kPage;
+    if (last >= pg0 && last < pg1) {
+      if (lane < 16) {
+        const int64_t slot =
+            (int64_t)load_uniform(a.page_table, (int64_t)b * a.pt_stride + last) * kPage + (L - 1) % kPage;
+        F::write_new(a.nw, b, slot, h, lane >> 3, lane & 7);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the row has reached the cache hierarchy
+    }
+  }
   const bool head_ok = n < a.group;
   const uint8_t* pool_h = a.pool + (int64_t)h * F::kHeadBytes;
   const int64_t page_bytes = (int64_t)a.num_kv_heads * F::kHeadBytes;

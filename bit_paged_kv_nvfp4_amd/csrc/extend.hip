@@ -29,9 +29,10 @@
 // then converted by the whole workgroup: V into a transposed f16 tile, FP8 K
 // into bf16 (both exact). 16-byte and 8-byte pieces are XOR-swizzled by row so
 // that the rows a quarter-wave reads fall in distinct banks.
-// K enters the first product as bf16, V the second as f16: exact for every
-// value of magnitude below 65504, which covers every NVFP4- or FP8-derived
-// workspace value (at g = 1) and every chunk value a model produces.
+// K enters the first product as bf16, V the second as f16: exact for
+// magnitudes in [2^-14, 65504] (every NVFP4- or FP8-derived workspace value at
+// g = 1 and the usual range of chunk values); below 2^-14 the absolute error
+// stays under 2^-25, and values must stay below 65504.
 // With a pool given, the kernel also quantize-writes the chunk's K/V into it
 // (the prefill path's quantize fused into the attention), each workgroup the
 // blocks of its own tokens and KV head.

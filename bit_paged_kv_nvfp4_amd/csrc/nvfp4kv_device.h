@@ -150,6 +150,9 @@ struct DecodeArgs {
                            // qk_scale_log2 and v_scale)
   float* part_o;           // [B][Hq][S][128]
   float* part_ml;          // [B][Hq][S][2]: running max (log2 units), sum
+  int32_t write_new;       // 1: the launch first writes token seq_lens[b] - 1 of
+                           // every sequence b from nw (token index b) into the pool
+  QuantizeArgs nw;         // its sources, pool and scales (nw.slots unused)
   void* out;
   int32_t out_bf16;
   float* lse;

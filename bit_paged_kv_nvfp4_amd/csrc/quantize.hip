@@ -25,66 +25,16 @@ __global__ __launch_bounds__(256) void k_quantize(QuantizeArgs a) {
 }
 
 // FP8 baseline quantize-on-write: one thread per (token, KV head, K|V, 16-value
-// block) writes the E4M3 code of x / s for each value (nearest, ties to even,
-// satfinite; s a power of two, so x / s is exact in fp32). K: the block's 16
-// bytes are contiguous in the token's row (one 16-byte store). V: value (row r,
-// channel d) sits at byte ((r/4)*16 + d/8)*32 + (d%8)*4 + r%4 of the slab, so
-// the block's bytes are scattered; every byte belongs to one value, so plain
-// byte stores never touch a neighbour's.
-constexpr int kFp8Slab = 2048;
-
+// block); the encode and byte layout are in quantize_block.h.
 __global__ __launch_bounds__(256) void k_quantize_fp8(QuantizeArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per_token = (int64_t)a.num_kv_heads * 16;
   if (idx >= a.num_tokens * per_token) return;
   const int64_t t = idx / per_token;
   const int rem = (int)(idx - t * per_token);
-  const int h = rem >> 4;
-  const int kind = (rem >> 3) & 1;
-  const int j = rem & 7;
   const int32_t slot = a.slots[t];
   if (slot < 0) return;
-  const int64_t page = slot >> 4;
-  const int row = slot & 15;
-  uint8_t* slab = a.pool + ((page * a.num_kv_heads + h) * 2 + kind) * (int64_t)kFp8Slab;
-  const int64_t off = t * a.token_stride + (int64_t)h * a.head_stride + j * 16;
-  float x[16];
-  if (a.bf16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(kind ? a.v : a.k) + off);
-    const uint4 u0 = p[0], u1 = p[1];
-    const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(kind ? a.v : a.k) + off);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 f = p[i];
-      x[4 * i] = f.x;
-      x[4 * i + 1] = f.y;
-      x[4 * i + 2] = f.z;
-      x[4 * i + 3] = f.w;
-    }
-  }
-  const float inv = kind ? a.inv_v_scale : a.inv_k_scale;
-  uint32_t c[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) c[i] = f32_to_e4m3(x[i] * inv);
-  if (kind == 0) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = c[4 * i] | (c[4 * i + 1] << 8) | (c[4 * i + 2] << 16) | (c[4 * i + 3] << 24);
-    *reinterpret_cast<uint4*>(slab + row * 128 + j * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int d = 16 * j + i;
-      slab[((row >> 2) * 16 + (d >> 3)) * 32 + (d & 7) * 4 + (row & 3)] = (uint8_t)c[i];
-    }
-  }
+  qenc::write_block_fp8(a, t, slot, rem >> 4, (rem >> 3) & 1, rem & 7);
 }
 
 // ---- per-tensor amax (global-scale calibration) -----------------------------

@@ -1,6 +1,7 @@
-// NVFP4 encode and write of one 16-value block (token, KV head, K|V, block) into
-// the page pool, shared by the quantize-on-write kernel and the extend kernel's
-// fused chunk write (gfx950).
+// Encode and write of one 16-value block (token, KV head, K|V, block) into the
+// page pool, NVFP4 and the FP8 baseline, shared by the quantize-on-write
+// kernels, the extend kernel's fused chunk write and the decode kernel's fused
+// write of each sequence's newest token (gfx950).
 //
 // Page "SGLang stores KV cache in 4 bits ..." (section Interpretation): prefill
 // quantizes the prompt's keys and values into the NVFP4 cache; each block of 16
@@ -56,11 +57,10 @@ __device__ inline __attribute__((always_inline)) uint32_t e2m1_code(float x, flo
   return sign | c;
 }
 
-// Codes and scale byte of block j (16 values) of token t, head h, kind (0 K, 1 V).
-__device__ inline __attribute__((always_inline)) void encode_block(const QuantizeArgs& a, int64_t t, int h, int kind, int j,
-                                             uint32_t (&code)[16], int& s) {
+// The 16 values of block j of token t, head h, kind (0 K, 1 V) as f32.
+__device__ inline __attribute__((always_inline)) void load_block(const QuantizeArgs& a, int64_t t, int h, int kind,
+                                                                 int j, float (&x)[16]) {
   const int64_t off = t * a.token_stride + (int64_t)h * a.head_stride + j * 16;
-  float x[16];
   if (a.bf16) {
     const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(kind ? a.v : a.k) + off);
     const uint4 u0 = p[0], u1 = p[1];
@@ -81,6 +81,13 @@ __device__ inline __attribute__((always_inline)) void encode_block(const Quantiz
       x[4 * i + 3] = f.w;
     }
   }
+}
+
+// Codes and scale byte of block j (16 values) of token t, head h, kind (0 K, 1 V).
+__device__ inline __attribute__((always_inline)) void encode_block(const QuantizeArgs& a, int64_t t, int h, int kind, int j,
+                                             uint32_t (&code)[16], int& s) {
+  float x[16];
+  load_block(a, t, h, kind, j, x);
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
@@ -91,17 +98,18 @@ __device__ inline __attribute__((always_inline)) void encode_block(const Quantiz
   for (int i = 0; i < 16; ++i) code[i] = e2m1_code(x[i], D, zs);
 }
 
-// Encode block j of token t (of a.num_tokens), KV head h, kind (0 K, 1 V) and
-// write its codes and scale to slot a.slots[t] (negative: skipped).
-__device__ inline __attribute__((always_inline)) void quantize_one(const QuantizeArgs& a, int64_t t, int h,
-                                                                   int kind, int j) {
-  const int32_t slot = a.slots[t];
-  if (slot < 0) return;
+// Encode block j of token t, KV head h, kind (0 K, 1 V) and write its codes and
+// scale to `slot` (>= 0). With `grouped`, a V block whose four-row group is
+// written by this call as four consecutive tokens of a.slots (of a.num_tokens)
+// is left to the thread of the group's first token, which writes whole words;
+// otherwise the block's nibbles are set with atomics.
+__device__ inline __attribute__((always_inline)) void write_block(const QuantizeArgs& a, int64_t t, int64_t slot,
+                                                                  int h, int kind, int j, bool grouped) {
   const int64_t page = slot >> 4;
-  const int row = slot & 15;
+  const int row = (int)(slot & 15);
   uint8_t* slab = a.pool + ((page * a.num_kv_heads + h) * 2 + kind) * (int64_t)kSlab;
 
-  if (kind == 1) {
+  if (kind == 1 && grouped) {
     // V: a code byte holds rows r and r ^ 2 and a 32-bit word rows 4g .. 4g+3 of
     // one page. When this call writes those four rows as four consecutive tokens,
     // the thread of the first one encodes all four and writes whole words.
@@ -173,6 +181,49 @@ __device__ inline __attribute__((always_inline)) void quantize_one(const Quantiz
       }
     }
     slab[kCodeBytes + j * 16 + row] = (uint8_t)s;
+  }
+}
+
+// Block j of token t (of a.num_tokens), KV head h, kind into slot a.slots[t]
+// (negative: skipped).
+__device__ inline __attribute__((always_inline)) void quantize_one(const QuantizeArgs& a, int64_t t, int h,
+                                                                   int kind, int j) {
+  const int32_t slot = a.slots[t];
+  if (slot < 0) return;
+  write_block(a, t, slot, h, kind, j, true);
+}
+
+// FP8 baseline pool: block j of token t, head h, kind into `slot` (>= 0), the
+// E4M3 code of x / s for each value (nearest, ties to even, satfinite; s a
+// power of two, so x / s is exact in fp32). K: the block's 16 bytes are
+// contiguous in the token's row (one 16-byte store). V: value (row r, channel d)
+// sits at byte ((r/4)*16 + d/8)*32 + (d%8)*4 + r%4 of the slab, so the block's
+// bytes are scattered; every byte belongs to one value, so plain byte stores
+// never touch a neighbour's.
+constexpr int kFp8Slab = 2048;
+
+__device__ inline __attribute__((always_inline)) void write_block_fp8(const QuantizeArgs& a, int64_t t, int64_t slot,
+                                                                      int h, int kind, int j) {
+  const int64_t page = slot >> 4;
+  const int row = (int)(slot & 15);
+  uint8_t* slab = a.pool + ((page * a.num_kv_heads + h) * 2 + kind) * (int64_t)kFp8Slab;
+  float x[16];
+  load_block(a, t, h, kind, j, x);
+  const float inv = kind ? a.inv_v_scale : a.inv_k_scale;
+  uint32_t c[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[i] = f32_to_e4m3(x[i] * inv);
+  if (kind == 0) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = c[4 * i] | (c[4 * i + 1] << 8) | (c[4 * i + 2] << 16) | (c[4 * i + 3] << 24);
+    *reinterpret_cast<uint4*>(slab + row * 128 + j * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int d = 16 * j + i;
+      slab[((row >> 2) * 16 + (d >> 3)) * 32 + (d & 7) * 4 + (row & 3)] = (uint8_t)c[i];
+    }
   }
 }
 

@@ -224,6 +224,39 @@ int32_t nvfp4_decode_combine(const void* workspace, size_t workspace_bytes, int3
                              int32_t num_splits, void* out, int32_t out_dtype, float* lse, void* stream);
 
 /*
+ * One decode step with its quantize-on-write in the same launch ([LMSYS]
+ * "Interpretation": each step writes the new token's K/V into the NVFP4 cache
+ * and the decode kernel reads the cache dequantizing in registers). For each
+ * sequence b with seq_lens[b] >= 1, token L-1 (L = seq_lens[b]) is the newest:
+ * its K/V rows k_new[b], v_new[b] are encoded exactly as nvfp4_kv_quantize
+ * encodes them and written to slot page_table[b][(L-1)/16]*16 + (L-1)%16 of the
+ * pool; then the attention of nvfp4_paged_decode_attn runs over tokens 0..L-1,
+ * the new one included. Result: the pool bytes and out/lse of
+ * nvfp4_kv_quantize(k_new, v_new, those slots) followed by
+ * nvfp4_paged_decode_attn, with one launch fewer.
+ *   k_new, v_new    device [batch][num_kv_heads][128] at b*new_token_stride +
+ *                   h*new_head_stride + d (elements), float32 or bfloat16 per
+ *                   new_dtype (NVFP4KV_F32 / NVFP4KV_BF16); strides multiples
+ *                   of 4 (F32) or 8 (BF16)
+ *   out             as nvfp4_paged_decode_attn, or NULL (then lse must be NULL):
+ *                   the call stops after phase 1 and leaves the partial states
+ *                   in the workspace, as nvfp4_paged_decode_attn_partial does,
+ *                   for nvfp4_decode_combine
+ *   all other arguments as nvfp4_paged_decode_attn.
+ * The page holding a sequence's newest token must not be among the first
+ * ceil(seq_lens/16) pages of another sequence of the batch (it is written while
+ * the others are read). Errors: as nvfp4_paged_decode_attn, plus ERR_NULL,
+ * ERR_DTYPE, ERR_SHAPE (negative strides) and ERR_ALIGN for the new rows, and
+ * ERR_NULL for an lse without out.
+ */
+int32_t nvfp4_paged_decode_attn_append(const void* q, const void* k_new, const void* v_new, int32_t new_dtype,
+                                       int64_t new_token_stride, int64_t new_head_stride, const int32_t* page_table,
+                                       int64_t page_table_stride, const int32_t* seq_lens, int32_t batch,
+                                       int32_t num_q_heads, int32_t max_seq_len, const nvfp4kv_pool* pool,
+                                       float sm_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                       void* out, int32_t out_dtype, float* lse, void* stream);
+
+/*
  * Extend-path dequantization ([LMSYS] "Interpretation": the cached prefix is
  * dequantized into one workspace shared across layers and attended alongside the
  * current chunk). For each listed sequence s and t < seq_lens[s], writes the
@@ -318,6 +351,15 @@ int32_t fp8_paged_decode_attn_partial(const void* q, const int32_t* page_table, 
                                       const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
                                       int32_t max_seq_len, const fp8kv_pool* pool, float sm_scale,
                                       int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+/* One FP8 decode step with its quantize-on-write in the same launch: arguments,
+ * result and errors as nvfp4_paged_decode_attn_append, with the FP8 encode of
+ * fp8_kv_quantize. */
+int32_t fp8_paged_decode_attn_append(const void* q, const void* k_new, const void* v_new, int32_t new_dtype,
+                                     int64_t new_token_stride, int64_t new_head_stride, const int32_t* page_table,
+                                     int64_t page_table_stride, const int32_t* seq_lens, int32_t batch,
+                                     int32_t num_q_heads, int32_t max_seq_len, const fp8kv_pool* pool, float sm_scale,
+                                     int32_t num_splits, void* workspace, size_t workspace_bytes, void* out,
+                                     int32_t out_dtype, float* lse, void* stream);
 
 /*
  * Extend-path attention ([LMSYS] "Interpretation": after the cached prefix is
@@ -340,9 +382,12 @@ int32_t fp8_paged_decode_attn_partial(const void* q, const int32_t* page_table, 
  *   out             device bf16 [C][num_q_heads][128]
  *   lse             device f32 [C][num_q_heads] or NULL
  * num_q_heads must be a multiple of num_kv_heads with a quotient of at most 16.
- * Arithmetic: bf16 products with fp32 accumulation on the matrix cores; the
- * softmax weights enter the second product rounded to bf16 (the row sums use
- * the same rounded weights). All device pointers 16-byte aligned; nothing is
+ * Arithmetic: fp32 accumulation on the matrix cores; Q and K enter the first
+ * product as bf16; V and the softmax weights enter the second as f16 (the row
+ * sums use the same rounded weights). V converts exactly for magnitudes in
+ * [2^-14, 65504], which holds every NVFP4- or FP8-derived workspace value at
+ * g = 1; smaller values carry an absolute error below 2^-25; V values must stay
+ * below 65504 in magnitude. All device pointers 16-byte aligned; nothing is
  * allocated; the call is asynchronous on `stream`.
  * Fused quantize-on-write ([LMSYS] "Interpretation": the prefill path writes
  * the prompt's keys and values into the NVFP4 cache): when chunk_pool is not

@@ -233,3 +233,29 @@ def test_extend_fused_write_validation(L):
     assert call(pool(g=3.0, hkv=1), FAKE) == ERR_VALUE
     assert call(p, None) == ERR_NULL
     assert call(p, FAKE + 2) == ERR_ALIGN
+
+
+def test_decode_append_validation(L):
+    """The fused decode step checks its new rows (as the quantize call checks its
+    sources) after the decode arguments, all before any HIP call."""
+    def a(fn, p, **kw):
+        return fn(FAKE, kw.get("k", FAKE), kw.get("v", FAKE), kw.get("dt", 1), kw.get("ts", 1024), kw.get("hs", 128),
+                  FAKE, 8, FAKE, kw.get("B", 2), kw.get("hq", 8), 100, ctypes.byref(p) if p is not None else None,
+                  0.088, 2, FAKE, 1 << 30, kw.get("out", FAKE), kw.get("odt", 1), kw.get("lse"), None)
+
+    for fn, good, bad_scale in ((L.nvfp4_paged_decode_attn_append, pool(hkv=2), pool(hkv=2, g=0.3)),
+                                (L.fp8_paged_decode_attn_append, fp8_pool(hkv=2), fp8_pool(hkv=2, ks=3.0))):
+        assert a(fn, None) == ERR_NULL
+        assert a(fn, bad_scale) == ERR_VALUE
+        assert a(fn, good, odt=2) == ERR_DTYPE
+        assert a(fn, good, hq=7) == ERR_SHAPE
+        assert a(fn, good, k=None) == ERR_NULL
+        assert a(fn, good, v=None) == ERR_NULL
+        assert a(fn, good, dt=2) == ERR_DTYPE
+        assert a(fn, good, ts=-8) == ERR_SHAPE
+        assert a(fn, good, k=FAKE + 4) == ERR_ALIGN
+        assert a(fn, good, hs=4) == ERR_ALIGN  # bf16 rows need multiples of 8 elements
+        assert a(fn, good, B=0) == OK  # no-op, no HIP call
+        assert a(fn, good, B=0, k=None) == OK
+        assert a(fn, good, out=None, lse=FAKE) == ERR_NULL  # lse needs the combine
+        assert a(fn, good, out=None, B=0) == OK  # phase 1 only, nothing to do
