@@ -564,16 +564,156 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
 // that start in [g T / W, (g + 1) T / W), T = total pages, W = workgroups (the
 // last one owns everything after its start). Its units form at most a few runs
 // of consecutive splits of one (b, h); a run is processed as one range of pages,
-// its four waves taking a quarter each, and writes one state (in its first
-// split's slot; the run's other splits get empty states).
+// its waves taking equal shares, and writes one state (in its first split's
+// slot; the run's other splits get empty states).
 struct Cursor {
-  int b;        // current sequence (a.batch = done)
+  int b;        // sequence (a.batch: past the end)
   int64_t seg;  // flattened start of segment (b, 0)
   int np;       // pages of sequence b
 };
 
-// Four waves per SIMD (at most 128 VGPRs): the persistent grid assumes four
-// resident workgroups per CU.
+// The first unit in index order that starts at or after flattened page pos: its
+// sequence's cursor and (h, s), where s may be S (then the unit is the first of
+// (b, h + 1), or of the next sequence). Every lane computes the same.
+struct UnitPos {
+  Cursor cu;
+  int h;
+  int s;
+};
+
+__device__ __forceinline__ UnitPos locate(const DecodeArgs& a, int64_t pos, int lane) {
+  const int S = a.num_splits;
+  const int Hkv = a.num_kv_heads;
+  // the first b whose segments end at or after pos
+  Cursor cu{a.batch, 0, 0};
+  int64_t base = 0;
+  for (int c0 = 0; c0 < a.batch; c0 += 64) {
+    const int bb = c0 + lane;
+    const int np = bb < a.batch ? seq_pages_lane(a, bb) : 0;
+    const int64_t incl = wave_incl_scan((int64_t)Hkv * np, lane);  // segments of b <= bb end at base + incl
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(bb < a.batch && base + incl >= pos);
+    if (hit) {
+      const int k = __builtin_ctzll(hit);
+      const int64_t incl_k = uniform((int64_t)__shfl(incl, k));
+      const int np_k = uniform(__shfl(np, k));
+      cu = Cursor{uniform(c0 + k), base + incl_k - (int64_t)Hkv * np_k, np_k};
+      break;
+    }
+    base += uniform((int64_t)__shfl(incl, 63));
+  }
+  UnitPos u{cu, 0, 0};
+  if (cu.b < a.batch && pos > cu.seg) {
+    // Here cu.seg < pos <= cu.seg + Hkv np, so np > 0. With rel = pos - cu.seg in
+    // [1, Hkv np], segment h = (rel - 1) / np holds offset r = rel - h np in
+    // [1, np], and its unit s = ceil(r / P) is the first to start at or after pos
+    // (s = S: none does; r = np: the segment's empty trailing splits start
+    // exactly at pos).
+    const int P = (cu.np + S - 1) / S;
+    const int64_t rel = pos - cu.seg;
+    u.h = (int)((rel - 1) / cu.np);
+    const int64_t r = rel - (int64_t)u.h * cu.np;
+    u.s = (int)((r + P - 1) / P);
+  }
+  return u;
+}
+
+// One run: splits s .. s1 of (b, h), np = pages of sequence b. The waves take
+// equal shares of its pages, then the last wave to finish merges the shares and
+// writes the run's state; the closing barrier frees every ring for the next run.
+template <class F>
+__device__ __forceinline__ void run(const DecodeArgs& a, int b, int h, int s, int s1, int np, int wave, int lane,
+                                    uint8_t* ring_base, int32_t* ids_base, int* waves_done, int& left, int quota) {
+  constexpr int kWaves = F::kWaves;
+  constexpr int kRingBytes = kRing * F::kSlotBytes;
+  const int S = a.num_splits;
+  const int P = (np + S - 1) / S;
+  const int rp0 = min(s * P, np);
+  const int rp1 = min((s1 + 1) * P, np);
+  // this wave's share: an even number of pages, so that only the last pair of
+  // the share can hold masked rows
+  const int share = (((rp1 - rp0 + kWaves - 1) / kWaves) + 1) & ~1;
+  const int pg0 = min(rp0 + wave * share, rp1);
+  const int pg1 = min(pg0 + share, rp1);
+
+  // The lane index is re-read each run so that the many values derived from it
+  // (copy offsets, LDS addresses) are rebuilt here rather than hoisted and kept
+  // live across the page loop, where registers are scarce.
+  int ln;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+  const int n = ln & 15;
+  const int G = ln >> 4;
+  uint8_t* const ring = ring_base + wave * kRingBytes;
+  f32x4 acc[8];
+  float m_ref, lsum;
+  wave_share<F>(a, b, h, pg0, pg1, ln, ring, ids_base + wave * (2 * kIdChunk), acc, m_ref, lsum, left, quota);
+
+  // ---- merge the waves' states; the last wave to finish writes the run's ----
+  lsum = xor16_sum(lsum);
+  lsum = xor32_sum(lsum);  // per head n, on every lane of head n
+  {
+    // own state into own ring region (its copies have all landed): acc as
+    // [q][lane] float4s, then (m, l) per head
+    float4* acc_lds = reinterpret_cast<float4*>(ring);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc_lds[q * 64 + ln] = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+    if (G == 0) reinterpret_cast<float2*>(ring + 8 * 64 * 16)[n] = make_float2(m_ref, lsum);
+  }
+  int prior = 0;
+  if (ln == 0) prior = __hip_atomic_fetch_add(waves_done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+  prior = __builtin_amdgcn_readfirstlane(prior);
+  if (prior == kWaves - 1) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    float mw[kWaves], lw[kWaves];
+    float m_all = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float2 ml = reinterpret_cast<const float2*>(ring_base + w * kRingBytes + 8 * 64 * 16)[n];
+      mw[w] = ml.x;
+      lw[w] = ml.y;
+      m_all = __builtin_fmaxf(m_all, ml.x);
+    }
+    float l_all = 0.0f;
+    f32x4 o_all[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) o_all[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      // an empty share has m = -inf and weight 0; so does everything when all are
+      const float f = (mw[w] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - m_all);
+      l_all += f * lw[w];
+      const float4* src = reinterpret_cast<const float4*>(ring_base + w * kRingBytes);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = src[q * 64 + ln];
+        o_all[q][0] += f * v.x;
+        o_all[q][1] += f * v.y;
+        o_all[q][2] += f * v.z;
+        o_all[q][3] += f * v.w;
+      }
+    }
+    if (n < a.group) {
+      const int qh = h * a.group + n;
+      const size_t unit = ((size_t)b * a.num_q_heads + qh) * S + s;
+      float* po = a.part_o + unit * kHeadDim;
+      // o_all[q][r] is O^T[channel 8 (4G + r) + q][head n], in units of
+      // 2^-kScaleLog2 of the value scale (NVFP4 V scales travel as E4M3/256)
+      const float vs = __builtin_ldexpf(a.v_scale, F::kScaleLog2);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float4 v0 = make_float4(o_all[0][r] * vs, o_all[1][r] * vs, o_all[2][r] * vs, o_all[3][r] * vs);
+        const float4 v1 = make_float4(o_all[4][r] * vs, o_all[5][r] * vs, o_all[6][r] * vs, o_all[7][r] * vs);
+        *reinterpret_cast<float4*>(po + 32 * G + 8 * r) = v0;
+        *reinterpret_cast<float4*>(po + 32 * G + 8 * r + 4) = v1;
+      }
+      // the run's state, then empty states for its other splits
+      float2* pml = reinterpret_cast<float2*>(a.part_ml) + unit;
+      for (int k = G; k <= s1 - s; k += 4) pml[k] = k == 0 ? make_float2(m_all, l_all) : make_float2(-__builtin_inff(), 0.0f);
+    }
+    *waves_done = 0;  // for the next run; the barrier below orders it
+  }
+  __syncthreads();  // every wave's state has been merged: rings may be reused
+}
+
 template <class F>
 __device__ __forceinline__ void decode_split(const DecodeArgs& a) {
   constexpr int kWaves = F::kWaves;
@@ -605,48 +745,16 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a) {
   const int64_t lo = total * g / W;
   const int64_t hi = g == W - 1 ? INT64_MAX : total * (g + 1) / W;
 
-  // ---- first segment that can hold a unit starting at or after lo: the first b
-  // whose segments end at or after lo ----
-  Cursor cu{a.batch, 0, 0};
-  {
-    int64_t base = 0;
-    for (int c0 = 0; c0 < a.batch; c0 += 64) {
-      const int bb = c0 + lane;
-      const int np = bb < a.batch ? seq_pages_lane(a, bb) : 0;
-      const int64_t incl = wave_incl_scan((int64_t)Hkv * np, lane);  // segments of b <= bb end at base + incl
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(bb < a.batch && base + incl >= lo);
-      if (hit) {
-        const int k = __builtin_ctzll(hit);
-        const int64_t incl_k = uniform((int64_t)__shfl(incl, k));
-        const int np_k = uniform(__shfl(np, k));
-        cu = Cursor{uniform(c0 + k), base + incl_k - (int64_t)Hkv * np_k, np_k};
-        break;
-      }
-      base += uniform((int64_t)__shfl(incl, 63));
-    }
-  }
-  int h = 0;
-  int s = 0;
-  if (cu.b < a.batch && lo > cu.seg) {
-    // First (h, s) of sequence cu.b whose unit starts at or after lo. Here
-    // cu.seg < lo <= cu.seg + Hkv np, so np > 0. With rel = lo - cu.seg in
-    // [1, Hkv np], segment h = (rel - 1) / np holds offset r = rel - h np in
-    // [1, np], and its unit s = ceil(r / P) is the first to start at or after lo
-    // (s = S: none does, the loop moves on; r = np: the segment's empty trailing
-    // splits start exactly at lo).
-    const int P = (cu.np + S - 1) / S;
-    const int64_t rel = lo - cu.seg;
-    h = (int)((rel - 1) / cu.np);
-    const int64_t r = rel - (int64_t)h * cu.np;
-    s = (int)((r + P - 1) / P);
-  }
-
   // ---- runs ----
-  // pages this wave is expected to process (a quarter of the window), and left
-  const int quota = (int)min<int64_t>((g == W - 1 ? total - lo : hi - lo) / kWaves + 1, 1 << 30);
+  // pages this wave is expected to process (its share of the window), and left
+  const int quota = (int)min<int64_t>((min(hi, total) - lo) / kWaves + 1, 1 << 26);  // left * 12 fits int
   int left = quota;
-  uint8_t* const ring = ring_all[wave];
-  int32_t* const ids = ids_all[wave];
+  uint8_t* const ring_base = &ring_all[0][0];
+  int32_t* const ids_base = &ids_all[0][0];
+  const UnitPos at = locate(a, lo, lane);
+  Cursor cu = at.cu;
+  int h = at.h;
+  int s = at.s;
   while (cu.b < a.batch) {
     if (s >= S) {  // (b, h) exhausted: next head, or next sequence
       s = 0;
@@ -670,90 +778,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a) {
       const int64_t last = (hi - 1 - seg) / P;  // split index of page hi - 1 relative to seg
       s1 = (int)min<int64_t>(last, S - 1);
     }
-    const int rp0 = min(s * P, np);
-    const int rp1 = min((s1 + 1) * P, np);
-    // this wave's share: an even number of pages, so that only the last pair of
-    // the share can hold masked rows
-    const int share = (((rp1 - rp0 + kWaves - 1) / kWaves) + 1) & ~1;
-    const int pg0 = min(rp0 + wave * share, rp1);
-    const int pg1 = min(pg0 + share, rp1);
-
-    // The lane index is re-read each run so that the many values derived from it
-    // (copy offsets, LDS addresses) are rebuilt here rather than hoisted and kept
-    // live across the page loop, where registers are scarce.
-    int ln;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
-    const int n = ln & 15;
-    const int G = ln >> 4;
-    f32x4 acc[8];
-    float m_ref, lsum;
-    wave_share<F>(a, cu.b, h, pg0, pg1, ln, ring, ids, acc, m_ref, lsum, left, quota);
-
-    // ---- merge the waves' states; the last wave to finish writes the run's ----
-    lsum = xor16_sum(lsum);
-    lsum = xor32_sum(lsum);  // per head n, on every lane of head n
-    {
-      // own state into own ring region (its copies have all landed): acc as
-      // [q][lane] float4s, then (m, l) per head
-      float4* acc_lds = reinterpret_cast<float4*>(ring);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc_lds[q * 64 + ln] = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
-      if (G == 0) reinterpret_cast<float2*>(ring + 8 * 64 * 16)[n] = make_float2(m_ref, lsum);
-    }
-    int prior = 0;
-    if (ln == 0) prior = __hip_atomic_fetch_add(&waves_done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-    prior = __builtin_amdgcn_readfirstlane(prior);
-    if (prior == kWaves - 1) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      float mw[kWaves], lw[kWaves];
-      float m_all = -__builtin_inff();
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float2 ml = reinterpret_cast<const float2*>(&ring_all[w][0] + 8 * 64 * 16)[n];
-        mw[w] = ml.x;
-        lw[w] = ml.y;
-        m_all = __builtin_fmaxf(m_all, ml.x);
-      }
-      float l_all = 0.0f;
-      f32x4 o_all[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) o_all[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        // an empty share has m = -inf and weight 0; so does everything when all are
-        const float f = (mw[w] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - m_all);
-        l_all += f * lw[w];
-        const float4* src = reinterpret_cast<const float4*>(&ring_all[w][0]);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float4 v = src[q * 64 + ln];
-          o_all[q][0] += f * v.x;
-          o_all[q][1] += f * v.y;
-          o_all[q][2] += f * v.z;
-          o_all[q][3] += f * v.w;
-        }
-      }
-      if (n < a.group) {
-        const int qh = h * a.group + n;
-        const size_t unit = ((size_t)cu.b * a.num_q_heads + qh) * S + s;
-        float* po = a.part_o + unit * kHeadDim;
-        // o_all[q][r] is O^T[channel 8 (4G + r) + q][head n], in units of
-        // 2^-kScaleLog2 of the value scale (NVFP4 V scales travel as E4M3/256)
-        const float vs = __builtin_ldexpf(a.v_scale, F::kScaleLog2);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float4 v0 = make_float4(o_all[0][r] * vs, o_all[1][r] * vs, o_all[2][r] * vs, o_all[3][r] * vs);
-          const float4 v1 = make_float4(o_all[4][r] * vs, o_all[5][r] * vs, o_all[6][r] * vs, o_all[7][r] * vs);
-          *reinterpret_cast<float4*>(po + 32 * G + 8 * r) = v0;
-          *reinterpret_cast<float4*>(po + 32 * G + 8 * r + 4) = v1;
-        }
-        // the run's state, then empty states for its other splits
-        float2* pml = reinterpret_cast<float2*>(a.part_ml) + unit;
-        for (int k = G; k <= s1 - s; k += 4) pml[k] = k == 0 ? make_float2(m_all, l_all) : make_float2(-__builtin_inff(), 0.0f);
-      }
-      waves_done = 0;  // for the next run; the barrier below orders it
-    }
-    __syncthreads();  // every wave's state has been merged: rings may be reused
+    run<F>(a, cu.b, h, s, s1, np, wave, lane, ring_base, ids_base, &waves_done, left, quota);
     s = s1 + 1;
   }
 }

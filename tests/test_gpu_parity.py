@@ -401,3 +401,56 @@ def test_quantize_write_orders_give_the_oracle_bytes():
         o = oracle.slab_offset(p, 0, 0, w.num_kv_heads)
         span = w.num_kv_heads * 2 * 1152
         assert np.array_equal(g[o:o + span], opool[o:o + span]), f"page {p}"
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["nvfp4", "fp8"])
+@pytest.mark.parametrize("splits", [0, 1, 7])
+def test_wide_page_table_parity(fp8, splits):
+    """A page table far wider than the sequences (max_seq_len 32768 for sequences
+    of 0 to 3000 tokens, so the default split count gives splits of one page and
+    many empty ones), checked against the oracle on every output; a second call
+    gives bit-identical results."""
+    lens = [3000, 1, 0, 517, 1600, 33]
+    hq, hkv = 64, 8
+    w = W.small_workload(611, len(lens), hq, hkv, lens, num_splits=splits, name="wide_table")
+    stride = 2048
+    pt_wide = np.full((w.batch, stride), 0, dtype=np.int32)
+    pt_wide[:, :w.page_table.shape[1]] = w.page_table
+    max_len = stride * 16
+    kv = _kv(w)
+    q = W.query(w)
+    if fp8:
+        gpool = B.Fp8Pool(w.num_pages, hkv, device="cuda")
+        opool = np.zeros(oracle.fp8_pool_bytes(w.num_pages, hkv), dtype=np.uint8)
+        for b, (k, v) in enumerate(kv):
+            if k.shape[0]:
+                sl_b = W.slots(w, b, 0, k.shape[0])
+                B.fp8_kv_quantize(k.cuda().contiguous(), v.cuda().contiguous(), torch.as_tensor(sl_b, device="cuda"),
+                                  gpool)
+                oracle.fp8_quantize_to_pool(k.numpy(), v.numpy(), sl_b, w.num_pages, pool=opool)
+        torch.cuda.synchronize()
+        fn, default = B.fp8_paged_decode_attn, B.fp8_paged_decode_attn_default_splits
+        ref, ref_lse = oracle.fp8_decode_attn(bf16_bits(q), w.page_table, w.seq_lens, opool, hkv, w.sm_scale,
+                                              n_threads=8)
+    else:
+        gpool = gpu_pool_from_kv(w, kv)
+        opool = oracle_pool_from_kv(w, kv)
+        fn, default = B.nvfp4_paged_decode_attn, B.nvfp4_paged_decode_attn_default_splits
+        ref, ref_lse = oracle.decode_attn(bf16_bits(q), w.page_table, w.seq_lens, opool, hkv, w.sm_scale, n_threads=8)
+    S = splits or default(w.batch, hkv, max_len)
+    ws = torch.empty(B.nvfp4_paged_decode_attn_workspace_bytes(w.batch, hq, S), dtype=torch.uint8, device="cuda")
+    pt = torch.as_tensor(pt_wide, device="cuda").contiguous()
+    sl = torch.as_tensor(w.seq_lens, device="cuda")
+    results = []
+    for _ in range(2):
+        lse = torch.empty((w.batch, hq), dtype=torch.float32, device="cuda")
+        out = fn(q.cuda().contiguous(), pt, sl, gpool, w.sm_scale, max_len, num_splits=S, workspace=ws,
+                 out_dtype=torch.float32, lse=lse)
+        torch.cuda.synchronize()
+        results.append((out.cpu().numpy(), lse.cpu().numpy()))
+    assert np.array_equal(results[0][0], results[1][0]) and np.array_equal(results[0][1], results[1][1])
+    out, lse = results[0]
+    live = np.asarray(w.seq_lens) > 0
+    assert_close(out[live], ref[live], what=f"wide page table splits={S}")
+    assert_close(lse[live], ref_lse[live], atol=1e-3, rtol=1e-4, what="lse")
+    assert np.all(out[~live] == 0) and np.all(np.isneginf(lse[~live]))
