@@ -144,9 +144,17 @@ __device__ __forceinline__ void issue_tile(const Tile& x, int hkv, uint32_t k_ld
   }
 }
 
-// V^T tile (f16): channel d, keys 4q .. 4q+3 (one 8-byte piece of the 128-byte
-// row) at byte d * 128 + 8 (q ^ (d & 15)).
-__device__ __forceinline__ uint32_t vt_piece(int d, int q) { return d * 128 + 8 * (q ^ (d & 15)); }
+// V^T tile (f16), one 128-byte row per channel d. A PV operand of key half ks
+// and lane group G holds keys 32 ks + 4 G .. +3 and 32 ks + 16 + 4 G .. +3 of
+// its channel, so 16-byte unit u = 4 ks + G of the row holds exactly those 8
+// keys (the second four in its upper 8 bytes), at byte d * 128 + 16 (u ^ (d & 7)):
+// one ds_read_b128 per operand, and the 8 rows a group of 8 lanes reads fall in
+// 8 different 16-byte bank groups. Keys 4q .. 4q+3 (q < 16) are unit
+// 4 (q / 8) + q % 4, half (q / 4) % 2.
+__device__ __forceinline__ uint32_t vt_unit(int d, int u) { return d * 128 + 16 * (u ^ (d & 7)); }
+__device__ __forceinline__ uint32_t vt_piece(int d, int q) {
+  return vt_unit(d, 4 * (q >> 3) + (q & 3)) + 8 * ((q >> 2) & 1);
+}
 
 // Workgroup pass over a landed stage: raw V -> V^T (f16); FP8 K -> bf16 K in the
 // K-operand layout. Thread t: channels 8c .. 8c+7 (c = t / 32) of keys 2m, 2m+1
@@ -385,9 +393,7 @@ __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         const int dim = 16 * d + n;
-        const uint2 v0 = *reinterpret_cast<const uint2*>(vt + vt_piece(dim, 8 * ks + G));
-        const uint2 v1 = *reinterpret_cast<const uint2*>(vt + vt_piece(dim, 8 * ks + 4 + G));
-        const f16x8 vf = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+        const f16x8 vf = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(vt + vt_unit(dim, 4 * ks + G)));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
           oacc[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[ks][rb], oacc[d][rb], 0, 0, 0);
