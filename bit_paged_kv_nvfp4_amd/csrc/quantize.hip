@@ -15,13 +15,66 @@
 namespace nvfp4kv {
 namespace {
 
+// One workgroup per (16 consecutive tokens, KV head); thread (kind, row, block)
+// = (threadIdx / 128, threadIdx / 8 % 16, threadIdx % 8) encodes block j of token
+// t0 + row. When the 16 tokens fill one page in order (slots s0 .. s0 + 15, s0 a
+// multiple of 16), the workgroup owns that page's K and V slabs of this head and
+// writes them whole: K codes and all scales with plain stores, V code words
+// after the four rows of each word have traded codes across lanes. Otherwise
+// each thread writes its block alone, as the shared block writer does.
 __global__ __launch_bounds__(256) void k_quantize(QuantizeArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_token = (int64_t)a.num_kv_heads * 16;
-  if (idx >= a.num_tokens * per_token) return;
-  const int64_t t = idx / per_token;
-  const int rem = (int)(idx - t * per_token);
-  qenc::quantize_one(a, t, rem >> 4, (rem >> 3) & 1, rem & 7);
+  const int h = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * kPage;
+  const int kind = threadIdx.x >> 7;
+  const int row = (threadIdx.x >> 3) & 15;
+  const int j = threadIdx.x & 7;
+  const int64_t t = t0 + row;
+  const bool live = t < a.num_tokens;
+  const int32_t slot = live ? a.slots[t] : -1;
+  const int32_t s0 = a.slots[t0];
+  const bool whole = __syncthreads_and(live && s0 >= 0 && (s0 & (kPage - 1)) == 0 && slot == s0 + row);
+  if (!whole) {
+    if (slot >= 0) qenc::write_block(a, t, slot, h, kind, j, true);
+    return;
+  }
+  uint8_t* slab = a.pool + (((int64_t)(s0 / kPage) * a.num_kv_heads + h) * 2 + kind) * (int64_t)kSlab;
+  uint32_t w[2];
+  int s;
+  qenc::encode_block(a, t, h, kind, j, w, s);
+  if (kind == 0) {
+    // K: row r holds its 64 code bytes at 64 r (block j at 8 j), scales at 1024 + 8 r + j
+    *reinterpret_cast<uint2*>(slab + row * 64 + j * 8) = make_uint2(w[0], w[1]);
+    slab[kCodeBytes + row * 8 + j] = (uint8_t)s;
+    return;
+  }
+  // V: the 32 code bytes of block j for rows 4G .. 4G+3 sit in 16-byte chunks
+  // 16 G + 2 j + c (c = 0, 1: channels 8c .. 8c+7 of the block); word wi of a
+  // chunk holds channels q = 8c + 2 wi and q + 1, each as a byte of rows 0|2 (low
+  // nibble row 0) and a byte of rows 1|3. The lane of row 4G + r4 writes the 8
+  // bytes of words 2 (r4 & 1), +1 of chunk c = r4 >> 1, i.e. channels 4 r4 .. 4 r4 + 3
+  // of the four rows: 16-bit field r4 of each row's packed codes.
+  const int r4 = row & 3;
+  const int lane = threadIdx.x & 63;  // = (row % 8) * 8 + j
+  uint32_t f[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int src = lane + 8 * (i - r4);
+    const uint32_t lo = (uint32_t)__shfl((int)w[0], src, 64);
+    const uint32_t hi = (uint32_t)__shfl((int)w[1], src, 64);
+    f[i] = ((r4 >> 1) ? hi : lo) >> (16 * (r4 & 1));
+  }
+  uint32_t out[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    uint32_t b[4];  // channels 4 r4 + 2k (low nibble) and + 1 (high nibble) of row i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = (f[i] >> (8 * k)) & 0xFFu;
+    out[k] = (b[0] & 15u) | ((b[2] & 15u) << 4) | ((b[1] & 15u) << 8) | ((b[3] & 15u) << 12) |
+             ((b[0] >> 4) << 16) | ((b[2] >> 4) << 20) | ((b[1] >> 4) << 24) | ((b[3] >> 4) << 28);
+  }
+  *reinterpret_cast<uint2*>(slab + ((row >> 2) * 16 + 2 * j + (r4 >> 1)) * 16 + 8 * (r4 & 1)) =
+      make_uint2(out[0], out[1]);
+  slab[kCodeBytes + j * 16 + row] = (uint8_t)s;
 }
 
 // FP8 baseline quantize-on-write: one thread per (token, KV head, K|V, 16-value
@@ -129,11 +182,13 @@ hipError_t launch_amax(const AmaxArgs& a, hipStream_t stream) {
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
   const int64_t threads = a.num_tokens * a.num_kv_heads * 16;
   if (threads == 0) return hipSuccess;
-  const int64_t blocks = (threads + 255) / 256;
-  if (a.fp8)
+  if (a.fp8) {
+    const int64_t blocks = (threads + 255) / 256;
     hipLaunchKernelGGL(k_quantize_fp8, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_quantize, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  } else {
+    const int64_t groups = (a.num_tokens + kPage - 1) / kPage;
+    hipLaunchKernelGGL(k_quantize, dim3((unsigned)groups, (unsigned)a.num_kv_heads), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -83,19 +83,81 @@ __device__ inline __attribute__((always_inline)) void load_block(const QuantizeA
   }
 }
 
-// Codes and scale byte of block j (16 values) of token t, head h, kind (0 K, 1 V).
+// x / D from r = 1/D correctly rounded: the product x r, its exact remainder
+// x - (x r) D (one fma), and one correction step. The result is the correctly
+// rounded quotient whenever D carries at most 4 significant bits (every E4M3
+// value, and 6, times a power of two), so its nearest-even E2M1 or E4M3
+// decision is the decision on the exact real quotient; a CPU test checks this
+// for every binary32 x in the binades that can change a code. Written as
+// -fma(-rem, r, -q0) so that a zero quotient keeps the sign of x.
+__device__ inline __attribute__((always_inline)) float quotient(float x, float D, float r) {
+#pragma clang fp contract(off)
+  const float q0 = x * r;
+  const float rem = __builtin_fmaf(-q0, D, x);
+  return -__builtin_fmaf(-rem, r, -q0);
+}
+
+// Codes (packed: value i in nibble i % 8 of word i / 8, i.e. the K byte order)
+// and scale byte of the 16 values x, for global scale g.
+//
+// Blocks whose values are all finite, whose scale is not saturated and not zero
+// take the fast path: the scale byte is the nearest-even E4M3 of the quotient
+// amax / (6 g), and every code the nearest-even E2M1 of x / D, D = E4M3(s) g,
+// rounded by the hardware f32 -> fp4 conversion (scale operand 1.0), which
+// saturates at 6 and keeps the sign. Other blocks (NaN or infinite values,
+// amax / (6 g) above 448, a zero scale) take the threshold path: a binary search
+// over exact midpoint products for the scale and seven exact threshold compares
+// per value, where NaN values are ignored by amax and get magnitude 0.
+__device__ inline __attribute__((always_inline)) void encode_values(const float (&x)[16], float g, uint32_t (&w)[2],
+                                                                    int& s) {
+  float ap = __builtin_fabsf(x[0]);  // NaN-propagating max of |x|
+#pragma unroll
+  for (int i = 1; i < 16; ++i) ap = __builtin_elementwise_maximum(ap, __builtin_fabsf(x[i]));
+  const float six_g = 6.0f * g;
+  bool fast = ap <= 2688.0f * g;  // 6 * 448 g: false for NaN and infinities
+  if (fast) {
+    s = (int)f32_to_e4m3(quotient(ap, six_g, 1.0f / six_g));
+    fast = s != 0;
+  }
+  if (fast) {
+    const float D = e4m3_to_f32((uint32_t)s) * g;
+    const float r = 1.0f / D;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* y = x + 8 * h;
+      uint32_t v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quotient(y[0], D, r), quotient(y[1], D, r), 1.0f, 0);
+      v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, quotient(y[2], D, r), quotient(y[3], D, r), 1.0f, 1);
+      v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, quotient(y[4], D, r), quotient(y[5], D, r), 1.0f, 2);
+      w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, quotient(y[6], D, r), quotient(y[7], D, r), 1.0f, 3);
+    }
+  } else {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+    s = scale_byte(amax, six_g);
+    const float D = e4m3_value(s) * g;
+    const bool zs = (s == 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v |= e2m1_code(x[8 * h + i], D, zs) << (4 * i);
+      w[h] = v;
+    }
+  }
+}
+
+// Code of value q (0..15) of a block from its packed words.
+__device__ inline __attribute__((always_inline)) uint32_t nibble(const uint32_t (&w)[2], int q) {
+  return (w[q >> 3] >> (4 * (q & 7))) & 15u;
+}
+
+// Codes and scale byte of block j of token t, head h, kind (0 K, 1 V).
 __device__ inline __attribute__((always_inline)) void encode_block(const QuantizeArgs& a, int64_t t, int h, int kind, int j,
-                                             uint32_t (&code)[16], int& s) {
+                                             uint32_t (&w)[2], int& s) {
   float x[16];
   load_block(a, t, h, kind, j, x);
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
-  s = scale_byte(amax, 6.0f * a.g);
-  const float D = e4m3_value(s) * a.g;
-  const bool zs = (s == 0);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) code[i] = e2m1_code(x[i], D, zs);
+  encode_values(x, a.g, w, s);
 }
 
 // Encode block j of token t, KV head h, kind (0 K, 1 V) and write its codes and
@@ -122,7 +184,7 @@ __device__ inline __attribute__((always_inline)) void write_block(const Quantize
     for (int i = 1; i < 4; ++i) full = full && a.slots[tl + i] == s0 + i;
     if (full) {
       if (r4 != 0) return;  // written by the group's first token
-      uint32_t c4[4][16];
+      uint32_t c4[4][2];
       int s4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) encode_block(a, t + i, h, 1, j, c4[i], s4[i]);
@@ -135,8 +197,9 @@ __device__ inline __attribute__((always_inline)) void write_block(const Quantize
 #pragma unroll
         for (int wi = 0; wi < 4; ++wi) {
           const int q = 8 * c + 2 * wi;
-          w[wi] = (c4[0][q] | (c4[2][q] << 4)) | ((c4[1][q] | (c4[3][q] << 4)) << 8) |
-                  ((c4[0][q + 1] | (c4[2][q + 1] << 4)) << 16) | ((c4[1][q + 1] | (c4[3][q + 1] << 4)) << 24);
+          w[wi] = (nibble(c4[0], q) | (nibble(c4[2], q) << 4)) | ((nibble(c4[1], q) | (nibble(c4[3], q) << 4)) << 8) |
+                  ((nibble(c4[0], q + 1) | (nibble(c4[2], q + 1) << 4)) << 16) |
+                  ((nibble(c4[1], q + 1) | (nibble(c4[3], q + 1) << 4)) << 24);
         }
         *reinterpret_cast<uint4*>(slab + ((row >> 2) * 16 + 2 * j + c) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
       }
@@ -146,20 +209,13 @@ __device__ inline __attribute__((always_inline)) void write_block(const Quantize
     }
   }
 
-  uint32_t code[16];
+  uint32_t code[2];
   int s;
   encode_block(a, t, h, kind, j, code, s);
   if (kind == 0) {
     // K: the token's 8 code bytes of block j are contiguous, channel 2i in the low
     // nibble of byte i
-    uint32_t w[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      w[half] = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[half] |= code[8 * half + i] << (4 * i);
-    }
-    *reinterpret_cast<uint2*>(slab + row * 64 + j * 8) = make_uint2(w[0], w[1]);
+    *reinterpret_cast<uint2*>(slab + row * 64 + j * 8) = make_uint2(code[0], code[1]);
     slab[kCodeBytes + row * 8 + j] = (uint8_t)s;
   } else {
     // V, a token alone in its four-row group: channel 16j + e sits in 16-byte
@@ -175,7 +231,7 @@ __device__ inline __attribute__((always_inline)) void write_block(const Quantize
       uint32_t* chunk = reinterpret_cast<uint32_t*>(slab + ((row >> 2) * 16 + 2 * j + c) * 16);
 #pragma unroll
       for (int wi = 0; wi < 4; ++wi) {
-        const uint32_t val = (code[8 * c + 2 * wi] << sh) | (code[8 * c + 2 * wi + 1] << (sh + 16));
+        const uint32_t val = (nibble(code, 8 * c + 2 * wi) << sh) | (nibble(code, 8 * c + 2 * wi + 1) << (sh + 16));
         __hip_atomic_fetch_and(chunk + wi, ~mask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_fetch_or(chunk + wi, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }

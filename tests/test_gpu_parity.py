@@ -122,6 +122,49 @@ def test_quantize_rounding_edges_bitexact():
     assert np.array_equal(g, opool), f"{int((g != opool).sum())} bytes differ"
 
 
+def _special_rows(T, seed):
+    """[T, 2, 128] fp32 rows: seeded N(0,1) values with blocks that hold NaN (both
+    signs), infinities, values whose block scale saturates, blocks whose scale
+    rounds to zero, and a NaN among finite values (ignored by amax)."""
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((T, 2, 128)).astype(np.float32)
+    nan = np.float32(np.nan)
+    x[0, 0, 3] = nan
+    x[1, 1, 17] = -nan
+    x[2, 0, 40] = np.inf
+    x[3, 1, 64] = -np.inf
+    x[4, 0, 80:96] = np.float32(3e38) * np.sign(x[4, 0, 80:96])
+    x[5, 1, 0:16] = np.float32(1e-30) * x[5, 1, 0:16]
+    x[6, 0, 96:112] = np.float32(5000.0) * x[6, 0, 96:112]
+    x[7, 1, 112:128] = nan
+    x[8, 0, 16:32] = -0.0
+    for t in range(9, T, 7):  # more of the same further on, in whole pages and tails
+        x[t, t % 2, (t * 5) % 128] = nan if t % 3 else -np.inf
+    return x
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_special_values_bitexact(dtype):
+    """NaN, infinities, saturated and zero block scales through the whole-page
+    writer (tokens filling pages in order), the per-block writer (a call that
+    starts mid-page, and the partial last page) and the four-row V groups: the
+    pool bytes equal the oracle's."""
+    w = W.small_workload(500, 2, 4, 2, [48, 37], name="specials")
+    rows = [torch.from_numpy(_special_rows(int(L), 77 + b)) for b, L in enumerate(w.seq_lens)]
+    kv = [(r.to(dtype), r.flip(0).contiguous().to(dtype)) for r in rows]
+    pool = B.Pool(w.num_pages, w.num_kv_heads, device="cuda")
+    # sequence 0 in one call; sequence 1 as tokens [0, 5) and [5, 37) (not page-aligned)
+    for b, cuts in ((0, [(0, 48)]), (1, [(0, 5), (5, 37)])):
+        for t0, t1 in cuts:
+            k, v = kv[b]
+            slots = torch.as_tensor(W.slots(w, b, t0, t1), device="cuda")
+            B.nvfp4_kv_quantize(k[t0:t1].cuda().contiguous(), v[t0:t1].cuda().contiguous(), slots, pool)
+    torch.cuda.synchronize()
+    opool = oracle_pool_from_kv(w, kv)
+    gp = pool.data.cpu().numpy()
+    assert np.array_equal(gp, opool), f"{int((gp != opool).sum())} bytes differ"
+
+
 @pytest.mark.parametrize("g", [0.5, 4.0])
 def test_power_of_two_global_scale(g):
     w = W.small_workload(400, 2, 8, 1, [70, 33], name="gscale")
