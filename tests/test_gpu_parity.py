@@ -210,7 +210,13 @@ def test_dequant_workspace_bitexact():
     gbig = gpu_pool_from_kv(w, big)
     obig = oracle_pool_from_kv(w, big)
     assert np.array_equal(gbig.data.cpu().numpy(), obig)
-    for pool_g, pool_o in ((gpool, opool), (gbig, obig)):
+    # values scaled by 2^-8: block scales near 2^-9, so dequantized values land on
+    # E4M3 subnormals (multiples of 2^-9), with ties between them
+    tiny = [(k * 2.0 ** -8, v * 2.0 ** -8) for k, v in kv]
+    gtiny = gpu_pool_from_kv(w, tiny)
+    otiny = oracle_pool_from_kv(w, tiny)
+    assert np.array_equal(gtiny.data.cpu().numpy(), otiny)
+    for pool_g, pool_o in ((gpool, opool), (gbig, obig), (gtiny, otiny)):
         kr, vr = oracle.dequant_workspace(pool_o, 2, w.page_table, w.seq_lens)
         k8 = torch.full((rows, 2, 128), 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
         v8 = torch.full_like(k8.view(torch.uint8), 0x7F).view(torch.float8_e4m3fn)
@@ -220,7 +226,12 @@ def test_dequant_workspace_bitexact():
             want = oracle.e4m3_codes_of(ref)
             gotb = got.view(torch.uint8).cpu().numpy()
             assert np.array_equal(gotb, want), f"{int((gotb != want).sum())} FP8 codes differ"
-    assert np.abs(kr).max() > 448  # saturation was exercised
+        if pool_g is gbig:
+            assert np.abs(kr).max() > 448  # saturation was exercised
+        if pool_g is gtiny:  # subnormal E4M3 results, some of them ties, were exercised
+            a = np.abs(kr[kr != 0])
+            assert (a < 2.0 ** -6).mean() > 0.2
+            assert np.any((a * 2.0 ** 9) % 1 == 0.5)
 
 
 def test_split_count_and_page_permutation_invariance_and_reproducibility():
