@@ -3,11 +3,16 @@
 // For every (sequence, query head) the S split states (M_s, Z_s, O_s) written by
 // the split kernel are merged: M* = max M_s, w_s = 2^(M_s - M*) (0 for an empty
 // split), out = sum w_s O_s / sum w_s Z_s, lse = (M* + log2 sum w_s Z_s) ln 2.
-// One wave per (sequence, query head); lane i owns output channels 2i and 2i+1.
-// The (M, Z) pairs are read first (lanes stride over the splits); O is read
-// only for splits of nonzero weight: an empty split's O is never written (its
-// pages were merged into another split's state), and at most 16 O rows are in
-// flight at once.
+// One workgroup per (sequence, query head), one wave per 64 splits (at most 16
+// waves, taking every 16th chunk of 64 beyond that); lane i owns output channels
+// 2i and 2i+1. Each wave reads its (M, Z) pairs first; O is read only for splits
+// of nonzero weight: an empty split's O is never written (its pages were merged
+// into another split's state), and at most 16 O rows are in flight per wave.
+// With several waves, wave 0 merges their states through LDS the same way.
+// Measured with 1024 splits (2 sequences x 64 heads): one wave per (sequence,
+// head) took 22-28 us, bounded by its chain of dependent loads.
+#include <algorithm>
+
 #include "nvfp4kv_device.h"
 
 namespace nvfp4kv {
@@ -26,19 +31,25 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
+// Waves per (sequence, query head): one per 64 splits, at most kMaxWaves.
+constexpr int kMaxWaves = 16;
+
+__global__ __launch_bounds__(64 * kMaxWaves) void k_decode_combine(DecodeArgs a) {
   const int unit = blockIdx.x;  // b * Hq + qh
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
   const int S = a.num_splits;
   const float2* __restrict__ ml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)unit * S;
   const float* __restrict__ po = a.part_o + (size_t)unit * S * kHeadDim + 2 * lane;
 
+  // this wave's splits: chunks of 64 starting at 64 (wave + k nw)
   float M = -__builtin_inff();
-  for (int i = lane; i < S; i += 64) M = __builtin_fmaxf(M, ml[i].x);
+  for (int i = 64 * wave + lane; i < S; i += 64 * nw) M = __builtin_fmaxf(M, ml[i].x);
   M = wave_max(M);
   float o0 = 0.0f, o1 = 0.0f, Ls = 0.0f;
   if (M != -__builtin_inff()) {
-    for (int c0 = 0; c0 < S; c0 += 64) {
+    for (int c0 = 64 * wave; c0 < S; c0 += 64 * nw) {
       const float2 st = c0 + lane < S ? ml[c0 + lane] : make_float2(-__builtin_inff(), 0.0f);
       const float wl = st.x == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(st.x - M);
       Ls += wl * st.y;
@@ -70,6 +81,35 @@ __global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
       }
     }
     Ls = wave_sum(Ls);
+  }
+
+  if (nw > 1) {
+    // merge the waves' states (M_w, Ls_w, O_w relative to 2^M_w) in wave 0
+    __shared__ float sM[kMaxWaves], sL[kMaxWaves];
+    __shared__ float2 sO[kMaxWaves][64];
+    sO[wave][lane] = make_float2(o0, o1);
+    if (lane == 0) {
+      sM[wave] = M;
+      sL[wave] = Ls;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float Mt = -__builtin_inff();
+    for (int w = 0; w < nw; ++w) Mt = __builtin_fmaxf(Mt, sM[w]);
+    o0 = o1 = Ls = 0.0f;
+    if (Mt != -__builtin_inff()) {
+      for (int w = 0; w < nw; ++w) {
+        if (sM[w] == -__builtin_inff()) continue;
+        const float f = __builtin_amdgcn_exp2f(sM[w] - Mt);
+        const float2 ow = sO[w][lane];
+        o0 += f * ow.x;
+        o1 += f * ow.y;
+        Ls += f * sL[w];
+      }
+    }
+    M = Mt;
+  }
+  if (M != -__builtin_inff()) {
     const float inv = 1.0f / Ls;
     o0 *= inv;
     o1 *= inv;
@@ -90,7 +130,8 @@ __global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
 
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_decode_combine, dim3(a.batch * a.num_q_heads), dim3(64), 0, stream, a);
+  const int nw = std::min(kMaxWaves, std::max(1, (a.num_splits + 63) / 64));
+  hipLaunchKernelGGL(k_decode_combine, dim3(a.batch * a.num_q_heads), dim3(64 * nw), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -39,6 +39,9 @@ CASES = [
     ("group3", 12, 4, [65, 2], 0),
     ("many_splits", 8, 1, [4096], 64),
     ("one_split", 16, 2, [513], 1),
+    # the combine spreads more than 64 splits over several waves of a workgroup
+    ("splits_200", 8, 1, [4096, 3000, 17], 200),
+    ("splits_1100", 8, 2, [20000, 900], 1100),
 ]
 
 
