@@ -87,10 +87,14 @@ def committed_traffic(workload, splits):
                 fields[k.strip()] = v.strip()
         if fields.get("workload") != workload or fields.get("num_splits") != str(splits):
             continue
-        src = os.path.join(here, fields.get("kernel_source", ""))
-        if not os.path.isfile(src):
+        # every source file the kernel is compiled from, hashed in the listed order
+        srcs = [os.path.join(here, f.strip()) for f in fields.get("kernel_source", "").split(",") if f.strip()]
+        if not srcs or not all(os.path.isfile(f) for f in srcs):
             continue
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields.get("kernel_source_sha256"):
+        h = hashlib.sha256()
+        for f in srcs:
+            h.update(open(f, "rb").read())
+        if h.hexdigest() != fields.get("kernel_source_sha256"):
             return None
         return int(fields["traffic_bytes_per_launch"])
     return None
