@@ -49,9 +49,11 @@
  *   (r/4)*16 + d/8 holds channels 8(d/8)..+7 of tokens 4(r/4)..+3, and each of
  *   its bytes holds one channel of two tokens (r and r+2), the pairs the decode
  *   kernel's matrix-core operands take along the token axis. A V byte is
- *   therefore shared by two tokens: nvfp4_kv_quantize updates only the written
- *   token's nibbles (atomically), so tokens of one page may be written by
- *   different calls or by one call in any order.
+ *   therefore shared by two tokens. nvfp4_kv_quantize writes whole V bytes only
+ *   where the same call writes every token they hold (a whole page, or a group
+ *   of four rows 4G..4G+3). Otherwise it updates only the written token's
+ *   nibbles, with atomics. Tokens of one page may therefore be written by
+ *   different calls, or by one call in any order.
  *   Token t of a sequence lives at page page_table[t/16], row t%16.
  *
  * Conventions for every entry point:
@@ -122,7 +124,7 @@ int32_t nvfp4kv_version(void);
  * head h, encodes K[t][h][0..127] and V[t][h][0..127] as 8 NVFP4 blocks each and
  * writes codes and scales to page slot/16, row slot%16 of `pool` (layout above).
  * Tokens with a negative slot are skipped. Output bytes are a deterministic
- * function of the inputs (no atomics); distinct tokens must map to distinct slots.
+ * function of the inputs; distinct tokens must map to distinct slots.
  *   k_src, v_src    device; element (t, h, d) at t*token_stride + h*head_stride + d
  *                   (elements), float32 or bfloat16 per src_dtype
  *   src_dtype       NVFP4KV_F32 or NVFP4KV_BF16
