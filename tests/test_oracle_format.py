@@ -229,6 +229,34 @@ def test_zero_scale_reading(oracle_lib):
     assert list(codes) == [0x80] * 8  # magnitude 0, sign of x kept
 
 
+def test_non_finite_reading(oracle_lib):
+    """Reading for non-finite inputs (the pages are silent): a NaN element is left
+    out of the block's amax and encodes as magnitude 0 with its sign bit; an
+    infinity saturates the block scale at 448 and encodes as magnitude 6. The
+    finite elements are encoded against the scale that results, per the brute
+    force of every candidate code."""
+    rng = np.random.default_rng(5)
+    for sign in (1.0, -1.0):
+        x = rng.standard_normal(16).astype(np.float32)
+        x[3] = np.float32(math.copysign(math.nan, sign))
+        codes, s = oracle_lib.quantize_block16(x)
+        finite = np.delete(x, 3)
+        assert s == brute_scale(float(np.abs(finite).max()))
+        D = E4M3_FINITE[s]
+        nib = [(codes[i // 2] >> (4 * (i % 2))) & 15 for i in range(16)]
+        assert nib[3] == (8 if sign < 0 else 0)
+        assert all(nib[i] == brute_code(float(x[i]), D) for i in range(16) if i != 3)
+        x[3] = np.float32(sign * math.inf)
+        codes, s = oracle_lib.quantize_block16(x)
+        assert s == 0x7E
+        nib = [(codes[i // 2] >> (4 * (i % 2))) & 15 for i in range(16)]
+        assert nib[3] == (15 if sign < 0 else 7)
+        assert all(nib[i] == brute_code(float(x[i]), E4M3_FINITE[0x7E]) for i in range(16) if i != 3)
+    # an all-NaN block: amax 0, scale 0, every code magnitude 0 with its sign
+    codes, s = oracle_lib.quantize_block16(np.array([math.nan, -math.nan] * 8, dtype=np.float32))
+    assert s == 0 and list(codes) == [0x80] * 8
+
+
 def test_global_scale_power_of_two(oracle_lib):
     rng = np.random.default_rng(16)
     for _ in range(200):
