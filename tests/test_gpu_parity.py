@@ -168,6 +168,48 @@ def test_quantize_special_values_bitexact(dtype):
     assert np.array_equal(gp, opool), f"{int((gp != opool).sum())} bytes differ"
 
 
+@pytest.mark.parametrize("pattern", ["in_order", "reversed", "gap", "mid_page", "mixed_seqs"])
+def test_quantize_slot_patterns_bitexact(pattern):
+    """The quantize kernel writes a (page, head) slab whole when one 16-token group
+    of the call fills a page in order, and block by block otherwise. Every way a
+    group can miss the whole-page case must still give the oracle's bytes:
+    tokens in reverse order, a skipped slot (-1) inside a page group, a call that
+    starts mid-page, and one call holding tokens of several sequences."""
+    w = W.small_workload(700, 3, 8, 2, [64, 40, 23], name="slots")
+    kv = _kv(w, torch.bfloat16)
+    calls = []  # (k, v, slots) per call
+    if pattern == "in_order":
+        calls = [(k, v, W.slots(w, b, 0, int(L))) for b, ((k, v), L) in enumerate(zip(kv, w.seq_lens))]
+    elif pattern == "reversed":
+        for b, ((k, v), L) in enumerate(zip(kv, w.seq_lens)):
+            calls.append((k.flip(0), v.flip(0), W.slots(w, b, 0, int(L))[::-1].copy()))
+    elif pattern == "gap":
+        for b, ((k, v), L) in enumerate(zip(kv, w.seq_lens)):
+            sl = W.slots(w, b, 0, int(L)).copy()
+            sl[5] = -1  # token 5 of every sequence is not written by this call
+            calls.append((k, v, sl))
+        # the skipped tokens in a second call (each alone in its V group)
+        for b, ((k, v), L) in enumerate(zip(kv, w.seq_lens)):
+            calls.append((k[5:6], v[5:6], W.slots(w, b, 5, 6)))
+    elif pattern == "mid_page":
+        for b, ((k, v), L) in enumerate(zip(kv, w.seq_lens)):
+            cut = min(7, int(L))
+            calls.append((k[:cut], v[:cut], W.slots(w, b, 0, cut)))
+            calls.append((k[cut:], v[cut:], W.slots(w, b, cut, int(L))))
+    else:  # mixed_seqs: all sequences in one call, so groups straddle sequences
+        calls = [(torch.cat([k for k, _ in kv]), torch.cat([v for _, v in kv]),
+                  np.concatenate([W.slots(w, b, 0, int(L)) for b, L in enumerate(w.seq_lens)]))]
+    pool = B.Pool(w.num_pages, w.num_kv_heads, device="cuda")
+    opool = np.zeros(oracle.pool_bytes(w.num_pages, w.num_kv_heads), dtype=np.uint8)
+    for k, v, sl in calls:
+        B.nvfp4_kv_quantize(k.cuda().contiguous(), v.cuda().contiguous(),
+                            torch.as_tensor(np.ascontiguousarray(sl), device="cuda"), pool)
+        oracle.quantize_to_pool(bf16_bits(k), bf16_bits(v), np.ascontiguousarray(sl), w.num_pages, pool=opool)
+    torch.cuda.synchronize()
+    gp = pool.data.cpu().numpy()
+    assert np.array_equal(gp, opool), f"{pattern}: {int((gp != opool).sum())} bytes differ"
+
+
 @pytest.mark.parametrize("g", [0.5, 4.0])
 def test_power_of_two_global_scale(g):
     w = W.small_workload(400, 2, 8, 1, [70, 33], name="gscale")
