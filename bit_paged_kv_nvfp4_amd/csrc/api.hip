@@ -84,6 +84,18 @@ int32_t quantize_into(const void* k_src, const void* v_src, int32_t src_dtype, i
   return hip_status(nvfp4kv::launch_quantize(a, static_cast<hipStream_t>(stream)));
 }
 
+// Workgroups of the persistent decode grid: the resident count, but at most one
+// per kMinGridPages pages of the largest cache the call can hold (batch x KV heads
+// x pages of max_seq_len), so that a small batch does not launch a thousand
+// workgroups with nothing to read. The kernel's result does not depend on it.
+constexpr int64_t kMinGridPages = 8;
+int32_t decode_grid(int num_cus, bool fp8, int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
+  const int64_t resident = nvfp4kv::decode_resident_workgroups(num_cus, fp8);
+  const int64_t pages = (int64_t)batch * num_kv_heads * ((max_seq_len + NVFP4KV_PAGE_SIZE - 1) / NVFP4KV_PAGE_SIZE);
+  const int64_t want = (pages + kMinGridPages - 1) / kMinGridPages;
+  return (int32_t)(want < 1 ? 1 : (want < resident ? want : resident));
+}
+
 int32_t default_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len, int32_t num_cus, bool fp8) {
   if (batch < 1 || num_kv_heads < 1 || max_seq_len < 1) return 1;
   if (num_cus <= 0) {
@@ -99,7 +111,7 @@ int32_t default_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
   // cut: about 16 splits per window keeps the windows within about 6% of each
   // other. Consecutive splits in one window share one state, so more splits do
   // not mean more partial-state writes. At least 4 pages per split.
-  const int64_t windows = nvfp4kv::decode_resident_workgroups(num_cus, fp8);
+  const int64_t windows = decode_grid(num_cus, fp8, batch, num_kv_heads, max_seq_len);
   int64_t s = (16 * windows + segments - 1) / segments;
   const int64_t max_by_pages = pages / 4 > 1 ? pages / 4 : 1;
   if (s > max_by_pages) s = max_by_pages;
@@ -225,7 +237,7 @@ int32_t finish_decode(nvfp4kv::DecodeArgs& a) {
   if (a.num_workgroups > 0) return NVFP4KV_OK;
   int cus = 0;
   if (!query_cus(&cus)) return NVFP4KV_ERR_HIP;
-  a.num_workgroups = nvfp4kv::decode_resident_workgroups(cus, a.fp8 != 0);
+  a.num_workgroups = decode_grid(cus, a.fp8 != 0, a.batch, a.num_kv_heads, a.max_seq_len);
   return NVFP4KV_OK;
 }
 
@@ -270,7 +282,7 @@ int32_t prepare_decode(const void* q, const int32_t* page_table, int64_t page_ta
   a.v_scale = pool.v_mul;
   a.fp8 = pool.fp8;
   a.num_splits = *num_splits;
-  a.num_workgroups = cus > 0 ? nvfp4kv::decode_resident_workgroups(cus, pool.fp8) : 0;  // 0: finish_decode sets it
+  a.num_workgroups = cus > 0 ? decode_grid(cus, pool.fp8, batch, hkv, max_seq_len) : 0;  // 0: finish_decode sets it
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = a.part_o + (size_t)batch * num_q_heads * *num_splits * NVFP4KV_HEAD_DIM;
   a.write_new = 0;

@@ -142,10 +142,12 @@ int32_t nvfp4_kv_quantize(const void* k_src, const void* v_src, int32_t src_dtyp
 
 /*
  * Split count the decode call uses when passed num_splits = 0. The decode
- * kernel keeps 4 workgroups of 4 waves resident per compute unit for the whole
- * launch and gives each a window of about equal page count, cut at split
- * boundaries; the default makes about 16 splits per window (windows within about
- * 6% of each other), at least 4 pages per split, at most NVFP4KV_MAX_SPLITS.
+ * kernel keeps up to 4 workgroups of 4 waves resident per compute unit for the
+ * whole launch (fewer when the cache is small: at most one workgroup per 8
+ * pages of batch x num_kv_heads x ceil(max_seq_len / 16)) and gives each a
+ * window of about equal page count, cut at split boundaries. The default makes
+ * about 16 splits per window (windows within about 6% of each other), at least
+ * 4 pages per split, at most NVFP4KV_MAX_SPLITS.
  * num_cus <= 0 asks the current
  * HIP device for its compute-unit count (the only HIP call of this function).
  * Returns >= 1.
