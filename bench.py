@@ -201,6 +201,41 @@ def cpu_baseline(w, n_seqs, W, torch):
             "decode_steps_per_s_per_layer_equiv": round((kv_bytes / w.kv_bytes_per_step()) / dt, 6)}
 
 
+def cpu_extend_baseline(w, W, torch, prefix_sample=16384):
+    """The oracle on the extend path of the chunked-prefill workload: quantize of
+    the whole 8192-token bf16 chunk, and dequantization (fp64) of the first
+    prefix_sample tokens of the cached prefix, with all host cores. Bytes are the
+    GPU kernels' algorithmic bytes for the same tokens."""
+    import numpy as np
+
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    row, P, C, H = w.extend_row, w.extend_prefix, w.extend_chunk, w.num_kv_heads
+    kc, vc = W.extend_chunk_kv(w)
+    kb = kc.contiguous().view(torch.int16).numpy().view(np.uint16)
+    vb = vc.contiguous().view(torch.int16).numpy().view(np.uint16)
+    pool = np.zeros(oracle.pool_bytes(w.num_pages, H), dtype=np.uint8)
+    t0 = time.perf_counter()
+    oracle.quantize_to_pool(kb, vb, W.slots(w, row, P, P + C), w.num_pages, pool=pool, n_threads=cores)
+    dq = time.perf_counter() - t0
+    q_bytes = C * H * 128 * 2 * 2 + C * H * 2 * 8 * 9
+    n = min(prefix_sample, P)
+    k, v = W.kv(w, row, 0, n)
+    oracle.quantize_to_pool(k.numpy(), v.numpy(), W.slots(w, row, 0, n), w.num_pages, pool=pool, n_threads=cores)
+    pt = np.ascontiguousarray(w.page_table[row:row + 1, :-(-n // 16)])
+    t0 = time.perf_counter()
+    oracle.dequant_workspace(pool, H, pt, np.array([n], dtype=np.int32))
+    dd = time.perf_counter() - t0
+    d_bytes = n * H * 2 * 8 * 9 + n * H * 128 * 2 * 2
+    return {"quantize_chunk": {"value": round(q_bytes / dq / 1e9, 4), "unit": "GB/s", "seconds": round(dq, 3),
+                               "sample": f"the whole {C}-token bf16 chunk, {H} KV heads"},
+            "dequant_prefix": {"value": round(d_bytes / dd / 1e9, 4), "unit": "GB/s", "seconds": round(dd, 3),
+                               "sample": f"the first {n} of {P} prefix tokens, {H} KV heads, fp64 output "
+                                         "(bytes counted as the GPU's bf16 workspace)"},
+            "cores": cores, "kind": "oracle"}
+
+
 def extend_step(w, pool, B, W, torch, steps, warmup):
     """Config 5's chunked-prefill step: quantize-write the 8192-token bf16 chunk
     into the extend request's pages, dequantize its 163840-token prefix into a
@@ -431,6 +466,8 @@ def main():
         res["extend"] = extend_step(w, pool, B, W, torch, max(3, args.steps // 5), 2)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, W, torch)
+        if w.extend_prefix:
+            res["cpu_baseline_extend"] = cpu_extend_baseline(w, W, torch)
     print(json.dumps(res), flush=True)
 
 
