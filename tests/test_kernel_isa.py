@@ -125,3 +125,30 @@ def test_no_cache_wide_fences(decode_asm, kernel):
     per launch)."""
     body = _function(decode_asm, kernel)
     assert not re.search(r"^\s*buffer_(wbl2|inv)\b", body, flags=re.M)
+
+
+# ---- every source of the library ---------------------------------------------
+@pytest.fixture(scope="module")
+def all_asm(tmp_path_factory):
+    if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
+        pytest.skip("hipcc not available")
+    d = tmp_path_factory.mktemp("isa_all")
+    return {src: _asm(d, os.path.join(B.CSRC, src)) for src in B.SOURCES}
+
+
+def test_no_packed_fp32_and_no_scratch_anywhere(all_asm):
+    """No packed-FP32 VALU instruction in any kernel of the library (the build
+    turns the feature off), and no kernel spills to scratch."""
+    for src, asm in all_asm.items():
+        assert not re.search(r"v_pk_(add|mul|fma)_f32", asm), src
+        for m in re.finditer(r"ScratchSize:\s*(\d+)", asm):
+            assert int(m.group(1)) == 0, src
+
+
+def test_quantize_encodes_with_the_fp4_conversion(all_asm):
+    """The quantize kernel's fast encode: a NaN-propagating max for amax and the
+    hardware f32 -> fp4 conversion of the corrected quotients (eight conversions
+    per 16-value block, on each of its code paths)."""
+    body = _function(all_asm["quantize.hip"], "10k_quantize")
+    assert re.search(r"v_maximum3_f32", body)
+    assert len(re.findall(r"v_cvt_scalef32_pk_fp4_f32", body)) >= 8
