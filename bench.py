@@ -85,6 +85,8 @@ def committed_traffic(workload, splits):
             if ":" in line and line.startswith("    "):
                 k, v = line.strip().split(":", 1)
                 fields[k.strip()] = v.strip()
+        if fields.get("kernel") != "k_decode_split":
+            continue  # e.g. the FP8 baseline's summary
         if fields.get("workload") != workload or fields.get("num_splits") != str(splits):
             continue
         # every source file the kernel is compiled from, hashed in the listed order
