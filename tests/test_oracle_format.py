@@ -237,21 +237,23 @@ def test_non_finite_reading(oracle_lib):
     force of every candidate code."""
     rng = np.random.default_rng(5)
     for sign in (1.0, -1.0):
-        x = rng.standard_normal(16).astype(np.float32)
-        x[3] = np.float32(math.copysign(math.nan, sign))
-        codes, s = oracle_lib.quantize_block16(x)
-        finite = np.delete(x, 3)
-        assert s == brute_scale(float(np.abs(finite).max()))
-        D = E4M3_FINITE[s]
-        nib = [(codes[i // 2] >> (4 * (i % 2))) & 15 for i in range(16)]
-        assert nib[3] == (8 if sign < 0 else 0)
-        assert all(nib[i] == brute_code(float(x[i]), D) for i in range(16) if i != 3)
-        x[3] = np.float32(sign * math.inf)
-        codes, s = oracle_lib.quantize_block16(x)
-        assert s == 0x7E
-        nib = [(codes[i // 2] >> (4 * (i % 2))) & 15 for i in range(16)]
-        assert nib[3] == (15 if sign < 0 else 7)
-        assert all(nib[i] == brute_code(float(x[i]), E4M3_FINITE[0x7E]) for i in range(16) if i != 3)
+        for pos in (3, 15):  # the NaN after the largest value, and last
+            x = rng.standard_normal(16).astype(np.float32)
+            x[0] = np.float32(4.0)  # the block's largest magnitude comes first
+            x[pos] = np.float32(math.copysign(math.nan, sign))
+            codes, s = oracle_lib.quantize_block16(x)
+            finite = np.delete(x, pos)
+            assert s == brute_scale(float(np.abs(finite).max()))
+            D = E4M3_FINITE[s]
+            nib = [(codes[i // 2] >> (4 * (i % 2))) & 15 for i in range(16)]
+            assert nib[pos] == (8 if sign < 0 else 0)
+            assert all(nib[i] == brute_code(float(x[i]), D) for i in range(16) if i != pos)
+            x[pos] = np.float32(sign * math.inf)
+            codes, s = oracle_lib.quantize_block16(x)
+            assert s == 0x7E
+            nib = [(codes[i // 2] >> (4 * (i % 2))) & 15 for i in range(16)]
+            assert nib[pos] == (15 if sign < 0 else 7)
+            assert all(nib[i] == brute_code(float(x[i]), E4M3_FINITE[0x7E]) for i in range(16) if i != pos)
     # an all-NaN block: amax 0, scale 0, every code magnitude 0 with its sign
     codes, s = oracle_lib.quantize_block16(np.array([math.nan, -math.nan] * 8, dtype=np.float32))
     assert s == 0 and list(codes) == [0x80] * 8

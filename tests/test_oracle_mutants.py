@@ -76,6 +76,9 @@ MUTANTS = [
      "while (amax / (6.0 * (g / 2.0)) <= 224.0) g /= 2.0;"),
     ("slab_kind_ignored", "return ((page * num_kv_heads + head) * 2 + kind) * (int64_t)ORC_SLAB;",
      "return ((page * num_kv_heads + head) * 2) * (int64_t)ORC_SLAB;"),
+    # non-finite inputs (reading: NaN left out of amax and coded as magnitude 0)
+    ("amax_takes_nan", "if (a > amax) amax = a;", "if (!(a <= amax)) amax = a;"),
+    ("nan_code_saturates", "double ax = fabs((double)x);", "double ax = isnan(x) ? INFINITY : fabs((double)x);"),
 ]
 
 
@@ -88,6 +91,7 @@ def _pins(o):
     yield lambda: TF.test_e2m1_code_threshold_edges(o)
     yield lambda: TF.test_round_trip_of_representable_blocks(o)
     yield lambda: TF.test_zero_scale_reading(o)
+    yield lambda: TF.test_non_finite_reading(o)
     yield lambda: TF.test_fp8_workspace_rounding_vs_library(o)
     yield lambda: TA.test_attention_vs_library_sdpa_on_representable_kv(o, 8, 2, [16, 50, 1])
     yield lambda: TA.test_dequant_workspace_returns_representable_values_exactly(o)
