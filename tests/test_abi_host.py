@@ -55,6 +55,13 @@ def test_default_splits_and_workspace_size(L):
     # over 44 x 8 (sequence, KV head) segments: ceil(16 * 1024 / 352) = 47
     assert L.nvfp4_paged_decode_attn_default_splits(44, 8, 32768, 256) == 47
     assert L.nvfp4_paged_decode_attn_default_splits(1, 1, 16, 256) == 1
+    # a small cache gets at most one workgroup per 8 pages: 1 x 1 x 128 pages -> 16
+    # workgroups, 16 * 16 = 256 splits, capped at 4 pages per split -> 32
+    assert L.nvfp4_paged_decode_attn_default_splits(1, 1, 2048, 256) == 32
+    # 2 x 8 segments of 300 pages -> 600 workgroups (below 1024), 600 splits, capped at 300 / 4 = 75
+    assert L.nvfp4_paged_decode_attn_default_splits(2, 8, 4800, 256) == 75
+    # 8 x 8 segments of 64 pages -> 512 workgroups, ceil(16 * 512 / 64) = 128, capped at 64 / 4 = 16
+    assert L.nvfp4_paged_decode_attn_default_splits(8, 8, 1024, 256) == 16
     assert L.nvfp4_paged_decode_attn_default_splits(2, 8, 1048576, 256) <= 4096
     s = L.nvfp4_paged_decode_attn_default_splits(15, 8, 163840, 256)
     assert 1 <= s <= 163840 // 16 // 4
