@@ -144,6 +144,58 @@ def _stream(stream) -> int | None:
     return getattr(stream, "cuda_stream", stream)
 
 
+def _same_device(ref: torch.Tensor, **tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, q on {ref.device}: every tensor must be on one device")
+
+
+def _decode_inputs(q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor, pool, max_seq_len: int):
+    """Checks the decode inputs against the header's contract and returns (B, Hq).
+    The kernels read seq_lens as int32 [B] and q as bf16 [B, Hq, 128]; a tensor of
+    another dtype or size would be read as wrong values or past its end."""
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [B, Hq, 128] tensor")
+    B, hq, _ = q.shape
+    if hq % pool.num_kv_heads != 0:
+        raise ValueError(f"num_q_heads {hq} is not a multiple of the pool's {pool.num_kv_heads} KV heads")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_contiguous():
+        raise ValueError("page_table must be contiguous int32 [B, stride]")
+    if page_table.shape[0] < B:
+        raise ValueError(f"page_table has {page_table.shape[0]} rows for a batch of {B}")
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError(f"seq_lens must be a contiguous int32 tensor of {B} entries (got {seq_lens.dtype} "
+                         f"{tuple(seq_lens.shape)})")
+    if int(max_seq_len) > page_table.shape[1] * PAGE_SIZE:
+        raise ValueError(f"max_seq_len {max_seq_len} exceeds the page table row ({page_table.shape[1]} pages)")
+    _same_device(q, page_table=page_table, seq_lens=seq_lens, pool=pool.data)
+    return B, hq
+
+
+def _outputs(q: torch.Tensor, B: int, hq: int, out: torch.Tensor | None, out_dtype, lse: torch.Tensor | None):
+    """The combine writes out [B, Hq, 128] (f32 or bf16) and lse f32 [B, Hq]: any
+    other shape would be written past its end. Returns (out, dtype code)."""
+    if out is None:
+        out = torch.empty((B, hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    odt = {torch.float32: F32, torch.bfloat16: BF16}.get(out.dtype)
+    if odt is None or not out.is_contiguous() or tuple(out.shape) != (B, hq, HEAD_DIM):
+        raise ValueError(f"out must be a contiguous float32 or bfloat16 [{B}, {hq}, 128] tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, hq)):
+        raise ValueError(f"lse must be a contiguous float32 [{B}, {hq}] tensor")
+    _same_device(q, out=out, lse=lse)
+    return out, odt
+
+
+def _workspace(q: torch.Tensor, workspace: torch.Tensor | None, B: int, hq: int, num_splits: int) -> torch.Tensor:
+    nbytes = nvfp4_paged_decode_attn_workspace_bytes(B, hq, num_splits)
+    if workspace is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    _same_device(q, workspace=workspace)
+    return workspace
+
+
 class Pool:
     """NVFP4 KV pool of one layer: a device uint8 buffer of num_pages pages with
     num_kv_heads K and V slabs each (layout in include/nvfp4kv.h)."""
@@ -230,23 +282,13 @@ def nvfp4_paged_decode_attn(q: torch.Tensor, page_table: torch.Tensor, seq_lens:
                             sm_scale: float, max_seq_len: int, num_splits: int = 0,
                             workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
                             out_dtype: torch.dtype = torch.bfloat16, lse: torch.Tensor | None = None, stream=None):
-    """q: bf16 [B, Hq, 128]; page_table: int32 [B, stride]; seq_lens: int32 [B].
+    """q: bf16 [B, Hq, 128]; page_table: int32 [>= B, stride]; seq_lens: int32 [B].
     Returns out [B, Hq, 128] (and fills ``lse`` [B, Hq] float32 when given)."""
-    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous bf16 [B, Hq, 128] tensor")
-    if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_contiguous():
-        raise ValueError("page_table must be contiguous int32 [B, stride]")
-    B, hq, _ = q.shape
+    B, hq = _decode_inputs(q, page_table, seq_lens, pool, max_seq_len)
     if num_splits == 0:
         num_splits = nvfp4_paged_decode_attn_default_splits(B, pool.num_kv_heads, max_seq_len)
-    if workspace is None:
-        nbytes = nvfp4_paged_decode_attn_workspace_bytes(B, hq, num_splits)
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((B, hq, HEAD_DIM), dtype=out_dtype, device=q.device)
-    odt = {torch.float32: F32, torch.bfloat16: BF16}.get(out.dtype)
-    if odt is None or not out.is_contiguous():
-        raise ValueError("out must be contiguous float32 or bfloat16")
+    workspace = _workspace(q, workspace, B, hq, num_splits)
+    out, odt = _outputs(q, B, hq, out, out_dtype, lse)
     d = pool.desc()
     _check("nvfp4_paged_decode_attn",
            lib().nvfp4_paged_decode_attn(_ptr(q), _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, hq,
@@ -258,11 +300,7 @@ def nvfp4_paged_decode_attn(q: torch.Tensor, page_table: torch.Tensor, seq_lens:
 
 def _decode_append(name: str, default_splits, q, k_new, v_new, page_table, seq_lens, pool, sm_scale, max_seq_len,
                    num_splits, workspace, out, out_dtype, lse, stream, combine):
-    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous bf16 [B, Hq, 128] tensor")
-    if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_contiguous():
-        raise ValueError("page_table must be contiguous int32 [B, stride]")
-    B, hq, _ = q.shape
+    B, hq = _decode_inputs(q, page_table, seq_lens, pool, max_seq_len)
     for nm, t in (("k_new", k_new), ("v_new", v_new)):
         if t.dim() != 3 or tuple(t.shape) != (B, pool.num_kv_heads, HEAD_DIM) or t.stride(2) != 1:
             raise ValueError(f"{nm} must be [B, Hkv, 128] with unit channel stride")
@@ -271,21 +309,16 @@ def _decode_append(name: str, default_splits, q, k_new, v_new, page_table, seq_l
     ndt = {torch.float32: F32, torch.bfloat16: BF16}.get(k_new.dtype)
     if ndt is None:
         raise ValueError("k_new/v_new must be float32 or bfloat16")
+    _same_device(q, k_new=k_new, v_new=v_new)
     if num_splits == 0:
         num_splits = default_splits(B, pool.num_kv_heads, max_seq_len)
-    if workspace is None:
-        nbytes = nvfp4_paged_decode_attn_workspace_bytes(B, hq, num_splits)
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     if not combine:
         if workspace is None or out is not None or lse is not None:
             raise ValueError("phase 1 alone needs a workspace and takes no out/lse")
         odt = F32
     else:
-        if out is None:
-            out = torch.empty((B, hq, HEAD_DIM), dtype=out_dtype, device=q.device)
-        odt = {torch.float32: F32, torch.bfloat16: BF16}.get(out.dtype)
-        if odt is None or not out.is_contiguous():
-            raise ValueError("out must be contiguous float32 or bfloat16")
+        out, odt = _outputs(q, B, hq, out, out_dtype, lse)
+    workspace = _workspace(q, workspace, B, hq, num_splits)
     d = pool.desc()
     _check(name, getattr(lib(), name)(_ptr(q), _ptr(k_new), _ptr(v_new), ndt, k_new.stride(0), k_new.stride(1),
                                       _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, hq, int(max_seq_len),
@@ -312,9 +345,8 @@ def nvfp4_paged_decode_attn_partial(q: torch.Tensor, page_table: torch.Tensor, s
                                     sm_scale: float, max_seq_len: int, num_splits: int, workspace: torch.Tensor,
                                     stream=None):
     """Phase 1: per-split online-softmax states into ``workspace`` (layout in the C header)."""
-    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous bf16 [B, Hq, 128] tensor")
-    B, hq, _ = q.shape
+    B, hq = _decode_inputs(q, page_table, seq_lens, pool, max_seq_len)
+    workspace = _workspace(q, workspace, B, hq, int(num_splits))
     d = pool.desc()
     _check("nvfp4_paged_decode_attn_partial",
            lib().nvfp4_paged_decode_attn_partial(_ptr(q), _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, hq,
@@ -325,9 +357,9 @@ def nvfp4_paged_decode_attn_partial(q: torch.Tensor, page_table: torch.Tensor, s
 def nvfp4_decode_combine(workspace: torch.Tensor, batch: int, num_q_heads: int, num_splits: int, out: torch.Tensor,
                          lse: torch.Tensor | None = None, stream=None):
     """Phase 2: merge the split states into ``out`` (float32 or bfloat16 [B, Hq, 128])."""
-    odt = {torch.float32: F32, torch.bfloat16: BF16}.get(out.dtype)
-    if odt is None or not out.is_contiguous():
-        raise ValueError("out must be contiguous float32 or bfloat16")
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    out, odt = _outputs(workspace, int(batch), int(num_q_heads), out, None, lse)
     _check("nvfp4_decode_combine",
            lib().nvfp4_decode_combine(_ptr(workspace), workspace.numel(), int(batch), int(num_q_heads), int(num_splits),
                                       _ptr(out), odt, _ptr(lse), _stream(stream)))
@@ -339,10 +371,22 @@ def nvfp4_kv_dequant_workspace(pool: Pool, page_table: torch.Tensor, seq_lens: t
                                v_out: torch.Tensor, stream=None):
     """Writes K^, V^ rows [row_offsets[s] + t] of k_out / v_out ([rows, Hkv, 128],
     float32, bfloat16 or float8_e4m3fn) for t < seq_lens[s]."""
-    if row_offsets.dtype != torch.int64:
-        raise ValueError("row_offsets must be int64")
+    n = seq_lens.numel()
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [n_seqs] tensor")
+    if row_offsets.dtype != torch.int64 or tuple(row_offsets.shape) != (n,) or not row_offsets.is_contiguous():
+        raise ValueError(f"row_offsets must be a contiguous int64 tensor of {n} entries")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_contiguous() or \
+            page_table.shape[0] < n:
+        raise ValueError(f"page_table must be contiguous int32 [>= {n}, stride]")
+    if int(max_seq_len) > page_table.shape[1] * PAGE_SIZE:
+        raise ValueError(f"max_seq_len {max_seq_len} exceeds the page table row ({page_table.shape[1]} pages)")
     if k_out.dtype != v_out.dtype or not k_out.is_contiguous() or not v_out.is_contiguous():
         raise ValueError("k_out and v_out must be contiguous and share a dtype")
+    if k_out.shape != v_out.shape or k_out.dim() != 3 or k_out.shape[1:] != (pool.num_kv_heads, HEAD_DIM):
+        raise ValueError(f"k_out and v_out must be [rows, {pool.num_kv_heads}, 128]")
+    _same_device(k_out, v_out=v_out, page_table=page_table, seq_lens=seq_lens, row_offsets=row_offsets,
+                 pool=pool.data)
     odt = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}.get(k_out.dtype)
     if odt is None:
         raise ValueError("workspace dtype must be float32, bfloat16 or float8_e4m3fn")
@@ -374,12 +418,22 @@ def nvfp4_extend_attn(q: torch.Tensor, k_prefix: torch.Tensor, v_prefix: torch.T
     pdt = {torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}.get(k_prefix.dtype)
     if pdt is None:
         raise ValueError("prefix workspace dtype must be bfloat16 or float8_e4m3fn")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or k_prefix.dim() != 3 or k_chunk.dim() != 3:
+        raise ValueError("q, k/v_prefix and k/v_chunk must be [rows, heads, 128]")
     C, hq, _ = q.shape
     P, hkv, _ = k_prefix.shape
+    if tuple(k_prefix.shape) != (P, hkv, HEAD_DIM) or v_prefix.shape != k_prefix.shape:
+        raise ValueError("k_prefix and v_prefix must both be [P, Hkv, 128]")
+    if tuple(k_chunk.shape) != (C, hkv, HEAD_DIM) or v_chunk.shape != k_chunk.shape:
+        raise ValueError(f"k_chunk and v_chunk must both be [{C}, {hkv}, 128]")
     if out is None:
         out = torch.empty_like(q)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be contiguous float32")
+    if out.dtype != torch.bfloat16 or not out.is_contiguous() or out.shape != q.shape:
+        raise ValueError(f"out must be a contiguous bfloat16 [{C}, {hq}, 128] tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (C, hq)):
+        raise ValueError(f"lse must be a contiguous float32 [{C}, {hq}] tensor")
+    _same_device(q, k_prefix=k_prefix, v_prefix=v_prefix, k_chunk=k_chunk, v_chunk=v_chunk, out=out, lse=lse,
+                 chunk_slots=chunk_slots)
     _check("nvfp4_extend_attn",
            lib().nvfp4_extend_attn(_ptr(q), _ptr(k_prefix) if P else None, _ptr(v_prefix) if P else None, pdt, P,
                                    _ptr(k_chunk), _ptr(v_chunk), C, hq, hkv, float(sm_scale), _ptr(out), _ptr(lse),
@@ -397,21 +451,11 @@ def fp8_paged_decode_attn(q: torch.Tensor, page_table: torch.Tensor, seq_lens: t
                           workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
                           out_dtype: torch.dtype = torch.bfloat16, lse: torch.Tensor | None = None, stream=None):
     """As nvfp4_paged_decode_attn, over an FP8 baseline pool."""
-    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous bf16 [B, Hq, 128] tensor")
-    if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_contiguous():
-        raise ValueError("page_table must be contiguous int32 [B, stride]")
-    B, hq, _ = q.shape
+    B, hq = _decode_inputs(q, page_table, seq_lens, pool, max_seq_len)
     if num_splits == 0:
         num_splits = fp8_paged_decode_attn_default_splits(B, pool.num_kv_heads, max_seq_len)
-    if workspace is None:
-        nbytes = nvfp4_paged_decode_attn_workspace_bytes(B, hq, num_splits)
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((B, hq, HEAD_DIM), dtype=out_dtype, device=q.device)
-    odt = {torch.float32: F32, torch.bfloat16: BF16}.get(out.dtype)
-    if odt is None or not out.is_contiguous():
-        raise ValueError("out must be contiguous float32 or bfloat16")
+    workspace = _workspace(q, workspace, B, hq, num_splits)
+    out, odt = _outputs(q, B, hq, out, out_dtype, lse)
     d = pool.desc()
     _check("fp8_paged_decode_attn",
            lib().fp8_paged_decode_attn(_ptr(q), _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, hq,
@@ -425,9 +469,8 @@ def fp8_paged_decode_attn_partial(q: torch.Tensor, page_table: torch.Tensor, seq
                                   sm_scale: float, max_seq_len: int, num_splits: int, workspace: torch.Tensor,
                                   stream=None):
     """Phase 1 over an FP8 baseline pool (phase 2 is nvfp4_decode_combine)."""
-    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous bf16 [B, Hq, 128] tensor")
-    B, hq, _ = q.shape
+    B, hq = _decode_inputs(q, page_table, seq_lens, pool, max_seq_len)
+    workspace = _workspace(q, workspace, B, hq, int(num_splits))
     d = pool.desc()
     _check("fp8_paged_decode_attn_partial",
            lib().fp8_paged_decode_attn_partial(_ptr(q), _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B,

@@ -182,8 +182,9 @@ struct Nvfp4Page {
   // S^T = K^ Q^T for each page (two independent MFMA chains).
   __device__ static __forceinline__ void scores(const Regs& ra, const Regs& rb, const f16x8 (&qf)[4], f32x4& sa,
                                                 f32x4& sb) {
-    // scale bytes of finite E4M3 values are <= 0x7E; bit 7 is dropped so that even
-    // bytes of never-written (masked) rows decode to finite values
+    // Bit 7 of the scale bytes is kept (k_scale_pair): a never-written row past the
+    // end of the sequence may score NaN, and pair_step's tail mask replaces its
+    // logit by -inf and its weight by an exact 0 before either is used.
     const uint32_t ska0 = k_scale_pair<0>(ra.ks), ska1 = k_scale_pair<1>(ra.ks);
     const uint32_t skb0 = k_scale_pair<0>(rb.ks), skb1 = k_scale_pair<1>(rb.ks);
     const uint32_t kwa[4] = {ra.kc.x, ra.kc.y, ra.kc.z, ra.kc.w};

@@ -266,3 +266,84 @@ def test_decode_append_validation(L):
         assert a(fn, good, B=0, k=None) == OK
         assert a(fn, good, out=None, lse=FAKE) == ERR_NULL  # lse needs the combine
         assert a(fn, good, out=None, B=0) == OK  # phase 1 only, nothing to do
+
+
+# ---- argument checks of the Python binding (raised before any library call) ----
+def _decode_args(batch=3, hq=16, hkv=2, stride=4):
+    import torch
+
+    p = B.Pool(8, hkv, device="cpu")
+    q = torch.zeros((batch, hq, 128), dtype=torch.bfloat16)
+    pt = torch.zeros((batch, stride), dtype=torch.int32)
+    sl = torch.full((batch,), 16, dtype=torch.int32)
+    return q, pt, sl, p
+
+
+def test_binding_rejects_int64_seq_lens(L):
+    import torch
+
+    q, pt, sl, p = _decode_args()
+    # int64 lengths would be read by the kernel as int32 pairs [L0, 0, L1, 0, ...]
+    with pytest.raises(ValueError, match="seq_lens"):
+        B.nvfp4_paged_decode_attn(q, pt, sl.to(torch.int64), p, 0.1, 16)
+    with pytest.raises(ValueError, match="seq_lens"):
+        B.nvfp4_paged_decode_attn(q, pt, sl[:2], p, 0.1, 16)
+    with pytest.raises(ValueError, match="seq_lens"):
+        B.nvfp4_paged_decode_attn_partial(q, pt, sl.to(torch.int64), p, 0.1, 16, 1, torch.zeros(16, dtype=torch.uint8))
+
+
+def test_binding_rejects_short_outputs(L):
+    import torch
+
+    q, pt, sl, p = _decode_args()
+    short = torch.zeros((2, 16, 128), dtype=torch.float32)  # batch 3 needs [3, 16, 128]
+    with pytest.raises(ValueError, match="out must be"):
+        B.nvfp4_paged_decode_attn(q, pt, sl, p, 0.1, 16, out=short)
+    with pytest.raises(ValueError, match="lse must be"):
+        B.nvfp4_paged_decode_attn(q, pt, sl, p, 0.1, 16, lse=torch.zeros((3, 8), dtype=torch.float32))
+    with pytest.raises(ValueError, match="lse must be"):
+        B.nvfp4_paged_decode_attn(q, pt, sl, p, 0.1, 16, lse=torch.zeros((3, 16), dtype=torch.float64))
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="out must be"):
+        B.nvfp4_decode_combine(ws, 3, 16, 1, short)
+
+
+def test_binding_rejects_bad_query_and_table(L):
+    import torch
+
+    q, pt, sl, p = _decode_args()
+    with pytest.raises(ValueError, match="q must be"):
+        B.nvfp4_paged_decode_attn(torch.zeros((3, 16, 64), dtype=torch.bfloat16), pt, sl, p, 0.1, 16)
+    with pytest.raises(ValueError, match="multiple"):
+        B.nvfp4_paged_decode_attn(torch.zeros((3, 15, 128), dtype=torch.bfloat16), pt, sl, p, 0.1, 16)
+    with pytest.raises(ValueError, match="page_table has 2 rows"):
+        B.nvfp4_paged_decode_attn(q, pt[:2], sl, p, 0.1, 16)
+    with pytest.raises(ValueError, match="max_seq_len"):
+        B.nvfp4_paged_decode_attn(q, pt, sl, p, 0.1, 4 * 16 + 1)
+    kn = torch.zeros((3, 2, 128), dtype=torch.float32)
+    with pytest.raises(ValueError, match="seq_lens"):
+        B.nvfp4_paged_decode_attn_append(q, kn, kn, pt, sl.to(torch.int64), p, 0.1, 16)
+
+
+def test_binding_rejects_bad_extend_and_dequant_shapes(L):
+    import torch
+
+    p = B.Pool(8, 2, device="cpu")
+    pt = torch.zeros((2, 4), dtype=torch.int32)
+    sl = torch.full((2,), 16, dtype=torch.int32)
+    ro = torch.zeros(2, dtype=torch.int64)
+    ko = torch.zeros((32, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="row_offsets"):
+        B.nvfp4_kv_dequant_workspace(p, pt, sl, ro[:1], 16, ko, ko.clone())
+    with pytest.raises(ValueError, match="k_out and v_out must be"):
+        B.nvfp4_kv_dequant_workspace(p, pt, sl, ro, 16, torch.zeros((32, 3, 128), dtype=torch.bfloat16),
+                                     torch.zeros((32, 3, 128), dtype=torch.bfloat16))
+    q = torch.zeros((5, 4, 128), dtype=torch.bfloat16)
+    kp = torch.zeros((7, 2, 128), dtype=torch.bfloat16)
+    kc = torch.zeros((5, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="k_chunk and v_chunk"):
+        B.nvfp4_extend_attn(q, kp, kp, kc[:4], kc[:4], 0.1)
+    with pytest.raises(ValueError, match="out must be"):
+        B.nvfp4_extend_attn(q, kp, kp, kc, kc, 0.1, out=torch.zeros((4, 4, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="lse must be"):
+        B.nvfp4_extend_attn(q, kp, kp, kc, kc, 0.1, lse=torch.zeros((5, 2), dtype=torch.float32))
