@@ -19,8 +19,14 @@ Parity status of each function (what pins it is listed in the tests):
   fp8_* (FP8 baseline pool)        pinned (codes vs library float8 cast of x/s;
                                    layout bijection; attention vs fp64 SDPA on
                                    E4M3-representable K/V with scales)
-  amax, global_scale_for_amax      pinned (library max; closed forms and
-                                   minimality over powers of two)
+  amax, global_scale_for_amax,
+  global_scale_tight_for_amax      pinned (library max; closed forms and
+                                   minimality over powers of two / binary32)
+  bf16_bits_of                     pinned (library RNE cast of float32-exact
+                                   values; exact-rational nearest-even)
+  any finite global scale g        pinned (exact-rational brute force of scale
+                                   and codes at non-power-of-two g, threshold
+                                   sweeps +-1 ulp, exact dequantized products)
   extend_attn                      pinned (fp64 library SDPA with an explicit
                                    prefix + causal mask, all three workspace
                                    dtypes; single-row and equal-key closed forms)
@@ -113,6 +119,12 @@ def _load(path: str) -> ctypes.CDLL:
     L.orc_amax.restype = c.c_double
     L.orc_global_scale_for_amax.argtypes = [c.c_double]
     L.orc_global_scale_for_amax.restype = c.c_double
+    L.orc_global_scale_tight_for_amax.argtypes = [c.c_double]
+    L.orc_global_scale_tight_for_amax.restype = c.c_float
+    L.orc_bf16_bits_of.argtypes = [c.c_double]
+    L.orc_bf16_bits_of.restype = c.c_uint16
+    L.orc_bf16_bits_of_array.argtypes = [P, c.c_int64, P]
+    L.orc_bf16_bits_of_array.restype = None
     return L
 
 
@@ -398,3 +410,17 @@ def amax(x: np.ndarray) -> float:
 
 def global_scale_for_amax(a: float) -> float:
     return float(lib().orc_global_scale_for_amax(float(a)))
+
+
+def global_scale_tight_for_amax(a: float) -> float:
+    """Smallest binary32 g with a / (6 g) <= 448 (1.0 for a = 0)."""
+    return float(lib().orc_global_scale_tight_for_amax(float(a)))
+
+
+def bf16_bits_of(x: np.ndarray) -> np.ndarray:
+    """Bit patterns (uint16) of the bf16 values nearest to the float64 values x,
+    ties to even: one rounding of exact values (e.g. a dequantized workspace)."""
+    xa = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.zeros(xa.shape, dtype=np.uint16)
+    lib().orc_bf16_bits_of_array(_ptr(xa), xa.size, _ptr(out))
+    return out

@@ -53,7 +53,15 @@
  *      the accuracy gap). Reading: the calibrated g is the smallest power of
  *      two with amax / (6 g) <= 448, amax = max |x| over the tensor, so that no
  *      block scale saturates and the largest block scales use the top of the
- *      E4M3 range; g = 1 for an all-zero tensor.
+ *      E4M3 range; g = 1 for an all-zero tensor. The tight variant is the
+ *      smallest binary32 g with the same property ([EUROK] "Bytes pro Token"
+ *      names the global scale an FP32 number).
+ *  11. Any finite g > 0 (steps 3, 4 and 6 take g as an FP32 number): every
+ *      threshold of steps 3 and 4 is the product of a few-bit constant, an E4M3
+ *      value and g, at most 31 significant bits, so it is exact in double, and so
+ *      is every dequantized value E2M1 * E4M3 * g. A dense workspace of another
+ *      precision holds the nearest value of that precision to the exact product
+ *      (nearest, ties to even; one rounding).
  *   9. FP8 baseline ([LMSYS] "Perspective" and "Synopsis" compare NVFP4 KV
  *      against an FP8 KV cache; [EUROK] "Bytes pro Token" gives FP8 one byte
  *      per value). Each value is stored as the E4M3 code of x / s, s the
@@ -189,6 +197,30 @@ void orc_quantize_block16(const float* x, float g, uint8_t* codes8, uint8_t* sca
     codes8[i] = (uint8_t)(lo | (hi << 4));
   }
   *scale = (uint8_t)s;
+}
+
+/* ---- 11. one rounding of an exact value to bf16 ------------------------- */
+/* Bit pattern of the bfloat16 value nearest to x (8 significant bits), ties to
+ * the even significand, sign kept. x is finite and either zero or inside the
+ * normal bf16 range, as every dequantized value with g in [2^-64, 2^64] is. The
+ * significand is scaled to [128, 256) exactly, rounded to an integer (the
+ * default rounding mode rounds half to even), and scaled back. */
+uint16_t orc_bf16_bits_of(double x) {
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double a = fabs(x);
+  int e;
+  float f;
+  uint32_t u;
+  if (a == 0.0) return sign;
+  frexp(a, &e); /* a = m 2^e, m in [0.5, 1) */
+  f = (float)ldexp(nearbyint(ldexp(a, 8 - e)), e - 8); /* exact: at most 9 significant bits */
+  memcpy(&u, &f, 4);
+  return (uint16_t)(sign | (u >> 16));
+}
+
+void orc_bf16_bits_of_array(const double* x, int64_t n, uint16_t* out) {
+  int64_t i;
+  for (i = 0; i < n; ++i) out[i] = orc_bf16_bits_of(x[i]);
 }
 
 /* ---- pool addressing (written definition, see header) ------------------- */
@@ -683,6 +715,18 @@ double orc_amax(const void* src, int src_dtype, int64_t token_stride, int64_t he
         if (fabs(x) > m) m = fabs(x);
       }
   return m;
+}
+
+/* Smallest binary32 g with amax / (6 g) <= 448, i.e. amax <= 2688 g (a product
+ * of at most 29 significant bits, exact in double); g = 1 for amax = 0. Starts
+ * from a float near amax / 2688 and steps one binary32 value at a time. */
+float orc_global_scale_tight_for_amax(double amax) {
+  float g;
+  if (amax <= 0.0) return 1.0f;
+  g = (float)(amax / 2688.0);
+  while (!(amax <= 2688.0 * (double)g)) g = nextafterf(g, INFINITY);
+  while (g > 0.0f && amax <= 2688.0 * (double)nextafterf(g, 0.0f)) g = nextafterf(g, 0.0f);
+  return g;
 }
 
 /* Smallest power of two g with amax / (6 g) <= 448 (g = 1 for amax = 0). */

@@ -1,6 +1,9 @@
 """Pins of the oracle's global-scale calibration: amax against numpy's max of
 |x|, and the chosen scale against closed forms and minimality over powers of
-two (no block scale saturates at g, one would at g / 2)."""
+two (no block scale saturates at g, one would at g / 2), and the tight binary32
+variant against exact-rational minimality."""
+from fractions import Fraction
+
 import numpy as np
 import pytest
 import torch
@@ -34,3 +37,27 @@ def test_global_scale_is_the_smallest_power_of_two_without_saturation(oracle_lib
         m, e = np.frexp(g)
         assert m == 0.5  # a power of two
         assert a / (6 * g) <= 448 < a / (6 * (g / 2))
+
+
+def test_tight_global_scale_closed_forms(oracle_lib):
+    assert oracle_lib.global_scale_tight_for_amax(0.0) == 1.0
+    assert oracle_lib.global_scale_tight_for_amax(2688.0) == 1.0
+    assert oracle_lib.global_scale_tight_for_amax(1344.0) == 0.5
+    assert oracle_lib.global_scale_tight_for_amax(2688.0 * 3) == 3.0
+    g = oracle_lib.global_scale_tight_for_amax(1.0)
+    up = np.float32(1 / 2688)  # 1/2688 rounded up to binary32
+    if Fraction(float(up)) < Fraction(1, 2688):
+        up = np.nextafter(up, np.float32(1))
+    assert g == float(up) and Fraction(1) <= 2688 * Fraction(g)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_tight_global_scale_is_the_smallest_binary32_without_saturation(oracle_lib, seed):
+    rng = np.random.default_rng(90 + seed)
+    for a in np.float32(np.exp(rng.uniform(np.log(1e-6), np.log(1e9), 400))):
+        a = float(a)
+        g = oracle_lib.global_scale_tight_for_amax(a)
+        assert np.float32(g) == g and g > 0
+        below = float(np.nextafter(np.float32(g), np.float32(0)))
+        assert Fraction(a) <= 2688 * Fraction(g)  # no block scale saturates at g ...
+        assert Fraction(a) > 2688 * Fraction(below)  # ... and one would at the next smaller binary32

@@ -320,3 +320,129 @@ def test_fp8_workspace_rounding_vs_library(oracle_lib):
     for x, want in [(448.0, 0x7E), (464.0, 0x7E), (2688.0, 0x7E), (-1e30, 0xFE), (-0.0, 0x80), (0.0, 0x00),
                     (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02), (2.0 ** -9 * 7.5, 0x08)]:
         assert oracle_lib.e4m3_code_of(x) == want, (x, want)
+
+
+# ---- any finite global scale g (not only powers of two) -------------------------------
+# g values with many significant bits (0.3, 1/2688 as binary32), few bits but not a
+# power of two (7.5, 0.75: their thresholds are exact in binary32, so exact ties
+# occur), and a random one.
+NON_POW2_G = [float(np.float32(0.3)), float(np.float32(1 / 2688)), 7.5, 0.75, float(np.float32(1.8472671))]
+
+
+def _f32_near(q: Fraction) -> list:
+    """The binary32 nearest to q and its two neighbours (all positive)."""
+    t = np.float32(float(q))
+    return [float(t), float(np.nextafter(t, np.float32(0))), float(np.nextafter(t, np.float32(np.inf)))]
+
+
+def test_scale_byte_non_power_of_two_global_scale(oracle_lib):
+    rng = np.random.default_rng(17)
+    n_ties = 0
+    for g in NON_POW2_G:
+        G = Fraction(g)
+        # every E4M3 midpoint times 6 g, as the nearest binary32 and one ulp either side
+        for k in range(126):
+            mid = (E4M3_FINITE[k] + E4M3_FINITE[k + 1]) / 2
+            for a in _f32_near(mid * 6 * G):
+                n_ties += Fraction(a) == mid * 6 * G
+                assert oracle_lib.scale_byte(a, g) == brute_scale(a, g), (a, g, k)
+        for a in (np.abs(rng.standard_normal(200)) * 6 * g * np.exp(rng.uniform(-8, 6, 200))).astype(np.float32):
+            assert oracle_lib.scale_byte(float(a), g) == brute_scale(float(a), g), (float(a), g)
+    assert n_ties > 200  # the few-bit g produce exact ties, decided to the even byte
+
+
+def test_e2m1_code_non_power_of_two_divisor(oracle_lib):
+    """Codes against D = E4M3(s) g (exact in double: at most 28 significant bits) at
+    every E2M1 midpoint times D, as the nearest binary32 and one ulp either side."""
+    mids = [Fraction(m) for m in ("1/4", "3/4", "5/4", "7/4", "5/2", "7/2", "5")]
+    n = 0
+    for g in NON_POW2_G:
+        for s in range(1, 127, 3):
+            D = E4M3_FINITE[s] * Fraction(g)
+            assert Fraction(float(D)) == D
+            for m in mids:
+                for a in _f32_near(m * D):
+                    for xv in (a, -a):
+                        assert oracle_lib.e2m1_code(xv, float(D)) == brute_code(xv, D), (xv, s, g)
+                        n += 1
+    assert n > 8000
+
+
+def _nibbles(codes):
+    return [(int(codes[i // 2]) >> (4 * (i % 2))) & 15 for i in range(16)]
+
+
+def test_quantize_block_non_power_of_two_global_scale(oracle_lib):
+    rng = np.random.default_rng(18)
+    mids = [Fraction(m) for m in ("1/4", "3/4", "5/4", "7/4", "5/2", "7/2", "5")]
+    for g in NON_POW2_G:
+        # blocks whose values sit on the code thresholds of their own scale (+-1 ulp)
+        for s_want in (9, 40, 77, 110):
+            D = E4M3_FINITE[s_want] * Fraction(g)
+            top = np.float32(float(6 * D))  # amax near 6 D: the scale is s_want or a neighbour
+            s = brute_scale(float(top), g)
+            D = E4M3_FINITE[s] * Fraction(g)
+            vals = [v for m in mids for v in _f32_near(m * D)][:15]
+            x = np.array([float(top)] + [v if i % 2 else -v for i, v in enumerate(vals)], dtype=np.float32)
+            codes, s2 = oracle_lib.quantize_block16(x, g)
+            assert s2 == s
+            assert _nibbles(codes) == [brute_code(float(v), D) for v in x], (g, s)
+        for _ in range(150):
+            x = (rng.standard_normal(16) * g * np.exp(rng.uniform(-4, 6))).astype(np.float32)
+            codes, s = oracle_lib.quantize_block16(x, g)
+            assert s == brute_scale(float(np.abs(x).max()), g)
+            D = E4M3_FINITE[s] * Fraction(g)
+            assert _nibbles(codes) == [brute_code(float(v), D) for v in x]
+
+
+def test_dequant_values_are_exact_products_for_any_g(oracle_lib):
+    """x^ = E2M1(c) E4M3(s) g exactly (at most 30 significant bits, exact in double)."""
+    rng = np.random.default_rng(19)
+    for g in NON_POW2_G:
+        k = (rng.standard_normal((3, 2, 128)) * g * 4).astype(np.float32)
+        pool = oracle_lib.quantize_to_pool(k, -k, np.array([16 * 2 + 5, 3, 16 + 15], dtype=np.int32), 3, g=g)
+        for t, slot in enumerate((37, 3, 31)):
+            for h in range(2):
+                for kind in (0, 1):
+                    row = oracle_lib.dequant_row(pool, slot // 16, slot % 16, h, kind, 2, g)
+                    slab = pool[oracle_lib.slab_offset(slot // 16, h, kind, 2):][:1152]
+                    for d in range(0, 128, 7):
+                        nib = oracle_lib.code_nibble(kind, slot % 16, d)
+                        c = (int(slab[nib // 2]) >> (4 * (nib % 2))) & 15
+                        sb = int(slab[oracle_lib.scale_byte_offset(kind, slot % 16, d // 16)])
+                        want = Fraction(E2M1_MAGNITUDES[c & 7]) * (-1 if c & 8 else 1) * E4M3_FINITE[sb] * Fraction(g)
+                        assert Fraction(row[d]) == want, (g, t, h, kind, d)
+
+
+def _bf16_nearest_even(x: float) -> int:
+    """Exact-rational nearest bf16 (8 significant bits), ties to the even significand."""
+    q = abs(Fraction(x))
+    sign = 0x8000 if math.copysign(1.0, x) < 0 else 0
+    if q == 0:
+        return sign
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    if Fraction(2) ** e > q:
+        e -= 1
+    ulp = Fraction(2) ** (e - 7)
+    lo = (q // ulp)
+    r = q - lo * ulp
+    n = lo + (1 if (r > ulp / 2 or (r == ulp / 2 and lo % 2 == 1)) else 0)
+    v = float(n * ulp)
+    return sign | int(torch.tensor([v], dtype=torch.float32).to(torch.bfloat16).view(torch.int16)[0]) & 0x7FFF
+
+
+def test_bf16_rounding_of_exact_values(oracle_lib):
+    rng = np.random.default_rng(20)
+    # float32-exact inputs: the library's float32 -> bf16 cast rounds once, to nearest even
+    f = np.concatenate([rng.standard_normal(3000).astype(np.float32) * 100,
+                        (1 + np.arange(256, dtype=np.float32) / 256) * np.float32(3.0)])
+    lib = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle_lib.bf16_bits_of(f.astype(np.float64)), lib)
+    # doubles with more bits than binary32 (dequantized products at non-power-of-two g),
+    # and exact ties with a tiny excess either side
+    xs = [float(Fraction(c) * E4M3_FINITE[s] * Fraction(g)) for g in NON_POW2_G for s in range(1, 127, 5)
+          for c in ("1/2", "3/2", "3", "6")]
+    xs += [1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -40, 1 + 2.0 ** -8 - 2.0 ** -40, -(1 + 2.0 ** -8)]
+    got = oracle_lib.bf16_bits_of(np.array(xs))
+    assert [int(v) for v in got] == [_bf16_nearest_even(x) for x in xs]
+    assert [int(v) for v in got[-5:]] == [0x3F80, 0x3F82, 0x3F81, 0x3F80, 0xBF80]

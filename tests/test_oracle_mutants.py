@@ -79,6 +79,21 @@ MUTANTS = [
     # non-finite inputs (reading: NaN left out of amax and coded as magnitude 0)
     ("amax_takes_nan", "if (a > amax) amax = a;", "if (!(a <= amax)) amax = a;"),
     ("nan_code_saturates", "double ax = fabs((double)x);", "double ax = isnan(x) ? INFINITY : fabs((double)x);"),
+    # any finite global scale g: every threshold and dequantized value exact in double
+    ("scale_divisor_rounded_to_float", "orc_e4m3_nearest_of_quotient((double)amax, 6.0 * (double)g)",
+     "orc_e4m3_nearest_of_quotient((double)amax, (double)(6.0f * g))"),
+    ("code_divisor_rounded_to_float", "double D = orc_e4m3_value(s) * (double)g;",
+     "double D = (double)(float)(orc_e4m3_value(s) * (double)g);"),
+    ("dequant_product_rounded_to_float", "out128[d] = orc_e2m1_value(code) * orc_e4m3_value(s) * (double)g;",
+     "out128[d] = (double)(float)(orc_e2m1_value(code) * orc_e4m3_value(s) * (double)g);"),
+    ("bf16_ties_away", "nearbyint(ldexp(a, 8 - e))", "round(ldexp(a, 8 - e))"),
+    ("bf16_truncates", "nearbyint(ldexp(a, 8 - e))", "floor(ldexp(a, 8 - e))"),
+    ("tight_scale_not_raised", "while (!(amax <= 2688.0 * (double)g)) g = nextafterf(g, INFINITY);", ""),
+    ("tight_scale_wrong_limit",
+     "g = (float)(amax / 2688.0);\n  while (!(amax <= 2688.0 * (double)g)) g = nextafterf(g, INFINITY);\n"
+     "  while (g > 0.0f && amax <= 2688.0 * (double)nextafterf(g, 0.0f))",
+     "g = (float)(amax / 2048.0);\n  while (!(amax <= 2048.0 * (double)g)) g = nextafterf(g, INFINITY);\n"
+     "  while (g > 0.0f && amax <= 2048.0 * (double)nextafterf(g, 0.0f))"),
 ]
 
 
@@ -100,6 +115,12 @@ def _pins(o):
     yield lambda: TE.test_constant_keys_give_running_mean_of_values(o)
     yield lambda: TC.test_amax_vs_library(o)
     yield lambda: TC.test_global_scale_closed_forms(o)
+    yield lambda: TC.test_tight_global_scale_closed_forms(o)
+    yield lambda: TC.test_tight_global_scale_is_the_smallest_binary32_without_saturation(o, 0)
+    yield lambda: TF.test_scale_byte_non_power_of_two_global_scale(o)
+    yield lambda: TF.test_quantize_block_non_power_of_two_global_scale(o)
+    yield lambda: TF.test_dequant_values_are_exact_products_for_any_g(o)
+    yield lambda: TF.test_bf16_rounding_of_exact_values(o)
     yield lambda: T8.test_fp8_layout_is_a_bijection(o)
     yield lambda: T8.test_fp8_codes_vs_library_cast(o, 0.5)
     yield lambda: T8.test_fp8_codes_saturate_and_keep_sign(o)
