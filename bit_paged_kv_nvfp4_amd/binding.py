@@ -44,6 +44,7 @@ EXPORTED = [
     "fp8_paged_decode_attn",
     "fp8_paged_decode_attn_partial",
     "fp8_paged_decode_attn_append",
+    "nvfp4_paged_decode_attn_noalloc",
 ]
 
 
@@ -121,6 +122,9 @@ def lib() -> ctypes.CDLL:
         L.fp8_paged_decode_attn_partial.argtypes = [P, P, c.c_int64, P, c.c_int32, c.c_int32, c.c_int32,
                                                     c.POINTER(Fp8PoolDesc), c.c_float, c.c_int32, P, c.c_size_t, P]
         L.fp8_paged_decode_attn_partial.restype = c.c_int32
+        L.nvfp4_paged_decode_attn_noalloc.argtypes = [P, P, c.c_int64, P, c.c_int32, c.c_int32, c.c_int32,
+                                                      c.POINTER(PoolDesc), c.c_float, c.c_int32, P, c.c_int32, P, P]
+        L.nvfp4_paged_decode_attn_noalloc.restype = c.c_int32
         _lib = L
     return _lib
 
@@ -295,6 +299,23 @@ def nvfp4_paged_decode_attn(q: torch.Tensor, page_table: torch.Tensor, seq_lens:
                                          int(max_seq_len), ctypes.byref(d), float(sm_scale), int(num_splits),
                                          _ptr(workspace), workspace.numel(), _ptr(out), odt, _ptr(lse),
                                          _stream(stream)))
+    return out
+
+
+def nvfp4_paged_decode_attn_noalloc(q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor, pool: Pool,
+                                    sm_scale: float, max_seq_len: int, num_splits: int = 0, out: torch.Tensor | None = None,
+                                    out_dtype: torch.dtype = torch.bfloat16, lse: torch.Tensor | None = None,
+                                    stream=None):
+    """As nvfp4_paged_decode_attn, with the split states in the library's fixed
+    per-GPU scratch array instead of a workspace (no device allocation by the
+    library; ``out`` is allocated here only when not given)."""
+    B, hq = _decode_inputs(q, page_table, seq_lens, pool, max_seq_len)
+    out, odt = _outputs(q, B, hq, out, out_dtype, lse)
+    d = pool.desc()
+    _check("nvfp4_paged_decode_attn_noalloc",
+           lib().nvfp4_paged_decode_attn_noalloc(_ptr(q), _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, hq,
+                                                 int(max_seq_len), ctypes.byref(d), float(sm_scale), int(num_splits),
+                                                 _ptr(out), odt, _ptr(lse), _stream(stream)))
     return out
 
 

@@ -4,6 +4,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "nvfp4kv.h"
 #include "nvfp4kv_device.h"
 
@@ -139,6 +142,8 @@ const char* nvfp4kv_status_string(int32_t status) {
     case NVFP4KV_ERR_WORKSPACE: return "workspace too small";
     case NVFP4KV_ERR_VALUE: return "a float argument is out of its allowed set";
     case NVFP4KV_ERR_HIP: return "a HIP runtime call failed";
+    case NVFP4KV_ERR_SCRATCH:
+      return "the call needs more split-state memory than the library's fixed scratch buffer holds";
     default: return "unknown status";
   }
 }
@@ -557,6 +562,88 @@ int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_pre
     w.inv_k_scale = w.inv_v_scale = 1.0f;
   }
   return hip_status(nvfp4kv::launch_extend(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---- decode without a caller workspace ----------------------------------------
+// The split states of nvfp4_paged_decode_attn_noalloc live in one fixed device
+// array per GPU. In host code `scratch` is only a stand-in for the symbol: its
+// device address comes from hipGetSymbolAddress, once per device, and only that
+// address is ever passed to a kernel.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)NVFP4KV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array (NULL on failure).
+void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t nvfp4_paged_decode_attn_noalloc(const void* q, const int32_t* page_table, int64_t page_table_stride,
+                                        const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                        int32_t max_seq_len, const nvfp4kv_pool* pool, float sm_scale,
+                                        int32_t num_splits, void* out, int32_t out_dtype, float* lse, void* stream) {
+  if (int32_t e = check_pool(pool)) return e;
+  if (out_dtype != NVFP4KV_F32 && out_dtype != NVFP4KV_BF16) return NVFP4KV_ERR_DTYPE;
+  if (batch < 0 || num_q_heads < 1 || max_seq_len < 0 || page_table_stride < 1) return NVFP4KV_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > NVFP4KV_MAX_SPLITS) return NVFP4KV_ERR_SHAPE;
+  if (batch == 0) return NVFP4KV_OK;
+  // the most splits whose states fit the scratch array
+  const size_t per_split = nvfp4_paged_decode_attn_workspace_bytes(batch, num_q_heads, 1);
+  if (per_split == 0 || per_split > kScratchBytes) return NVFP4KV_ERR_SCRATCH;
+  int32_t fit = (int32_t)(kScratchBytes / per_split < NVFP4KV_MAX_SPLITS ? kScratchBytes / per_split
+                                                                          : NVFP4KV_MAX_SPLITS);
+  while (fit > 1 && nvfp4_paged_decode_attn_workspace_bytes(batch, num_q_heads, fit) > kScratchBytes) --fit;
+  if (num_splits > 0 && nvfp4_paged_decode_attn_workspace_bytes(batch, num_q_heads, num_splits) > kScratchBytes)
+    return NVFP4KV_ERR_SCRATCH;
+  if (num_splits == 0) {
+    int cus = 0;
+    if (!query_cus(&cus)) return NVFP4KV_ERR_HIP;
+    num_splits = default_splits(batch, pool->num_kv_heads, max_seq_len, cus, false);
+    if (num_splits > fit) num_splits = fit;
+  }
+  // every argument check of the workspace entry point runs before the scratch
+  // address is looked up (the only HIP call here that is not a launch)
+  nvfp4kv::DecodeArgs a, c;
+  const size_t ws_bytes = nvfp4_paged_decode_attn_workspace_bytes(batch, num_q_heads, num_splits);
+  void* const kFakeAligned = reinterpret_cast<void*>((uintptr_t)256);  // stands in for the scratch in checks
+  if (int32_t e = prepare_decode(q, page_table, page_table_stride, seq_lens, batch, num_q_heads, max_seq_len,
+                                 info_of(pool), sm_scale, &num_splits, kFakeAligned, ws_bytes, a))
+    return e;
+  if (int32_t e = prepare_combine(kFakeAligned, ws_bytes, batch, num_q_heads, num_splits, out, out_dtype, lse, c))
+    return e;
+  void* ws = scratch_of_current_device();
+  if (!ws) return NVFP4KV_ERR_HIP;
+  a.part_o = static_cast<float*>(ws);
+  a.part_ml = a.part_o + (size_t)batch * num_q_heads * num_splits * NVFP4KV_HEAD_DIM;
+  c.part_o = a.part_o;
+  c.part_ml = a.part_ml;
+  if (int32_t e = finish_decode(a)) return e;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (int32_t e = hip_status(nvfp4kv::launch_decode_partial(a, st))) return e;
+  return hip_status(nvfp4kv::launch_decode_combine(c, st));
 }
 
 }  // extern "C"

@@ -58,7 +58,9 @@
  *
  * Conventions for every entry point:
  *   - The caller owns all memory; the library allocates nothing, keeps no
- *     global mutable state, and is reentrant.
+ *     global mutable state, and is reentrant. The one exception is
+ *     nvfp4_paged_decode_attn_noalloc, which keeps its split states in a fixed
+ *     device array of the library (see there).
  *   - Arguments named *device* are device pointers; the pool descriptor is a
  *     host pointer to a struct whose data member is a device pointer.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
@@ -93,7 +95,8 @@ enum nvfp4kv_status {
   NVFP4KV_ERR_DTYPE = 4,     /* unsupported dtype code */
   NVFP4KV_ERR_WORKSPACE = 5, /* workspace smaller than required */
   NVFP4KV_ERR_VALUE = 6,     /* a float argument is not allowed (e.g. global scale) */
-  NVFP4KV_ERR_HIP = 7        /* a HIP runtime call failed */
+  NVFP4KV_ERR_HIP = 7,       /* a HIP runtime call failed */
+  NVFP4KV_ERR_SCRATCH = 8    /* nvfp4_paged_decode_attn_noalloc: the states exceed its fixed scratch */
 };
 
 /* Element types. NVFP4KV_FP8_E4M3 (OCP E4M3 "fn": 1 sign, 4 exponent bits with
@@ -226,6 +229,30 @@ int32_t nvfp4_paged_decode_attn_partial(const void* q, const int32_t* page_table
 
 int32_t nvfp4_decode_combine(const void* workspace, size_t workspace_bytes, int32_t batch, int32_t num_q_heads,
                              int32_t num_splits, void* out, int32_t out_dtype, float* lse, void* stream);
+
+/*
+ * Decode attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, kernels and result as nvfp4_paged_decode_attn, without the
+ * workspace argument. The split states go to a device array the library holds,
+ * NVFP4KV_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, kept from the first call on a
+ * GPU until the process ends. That first call also looks up the array's device
+ * address (hipGetSymbolAddress); no call allocates anything.
+ *   num_splits   0: the default split count, lowered until the states fit the
+ *                scratch; otherwise the states of num_splits splits
+ *                (nvfp4_paged_decode_attn_workspace_bytes) must fit, else
+ *                NVFP4KV_ERR_SCRATCH
+ *   all other arguments, results and errors as nvfp4_paged_decode_attn.
+ * Every call on one GPU uses the same array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and give wrong results.
+ * Calls in order on one stream are safe; nothing in the array needs to start
+ * at zero (each call writes every state it reads).
+ */
+#define NVFP4KV_NOALLOC_SCRATCH_BYTES (64 << 20)
+int32_t nvfp4_paged_decode_attn_noalloc(const void* q, const int32_t* page_table, int64_t page_table_stride,
+                                        const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                        int32_t max_seq_len, const nvfp4kv_pool* pool, float sm_scale,
+                                        int32_t num_splits, void* out, int32_t out_dtype, float* lse, void* stream);
 
 /*
  * One decode step with its quantize-on-write in the same launch ([LMSYS]

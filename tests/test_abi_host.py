@@ -12,7 +12,7 @@ from bit_paged_kv_nvfp4_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4kv.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_VALUE, ERR_HIP = range(8)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_VALUE, ERR_HIP, ERR_SCRATCH = range(9)
 FAKE = 0x10000  # 16-byte aligned, never dereferenced by validation
 
 
@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(L):
 def test_constants_and_strings(L):
     assert L.nvfp4kv_version() == 1
     assert L.nvfp4kv_pool_bytes(10, 8) == 10 * 8 * 2 * 1152
-    for s in range(8):
+    for s in range(9):
         assert len(B.status_string(s)) > 0
     assert B.status_string(99) == "unknown status"
 
@@ -347,3 +347,21 @@ def test_binding_rejects_bad_extend_and_dequant_shapes(L):
         B.nvfp4_extend_attn(q, kp, kp, kc, kc, 0.1, out=torch.zeros((4, 4, 128), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="lse must be"):
         B.nvfp4_extend_attn(q, kp, kp, kc, kc, 0.1, lse=torch.zeros((5, 2), dtype=torch.float32))
+
+
+def test_noalloc_decode_rejects_before_any_hip_call(L):
+    P = B.PoolDesc(FAKE, 4096, 8, 1.0)
+    fn = L.nvfp4_paged_decode_attn_noalloc
+    common = (FAKE, FAKE, 4096, FAKE, 44, 64, 32768)
+    # 44 x 64 x 47 splits need 69 MB of states, more than the 64 MiB scratch
+    assert fn(*common, ctypes.byref(P), 0.1, 47, FAKE, 1, None, None) == ERR_SCRATCH
+    # so many (sequence, head) rows that even one split does not fit
+    assert fn(FAKE, FAKE, 4096, FAKE, 1 << 20, 64, 32768, ctypes.byref(P), 0.1, 1, FAKE, 1, None, None) == ERR_SCRATCH
+    assert fn(*common, ctypes.byref(P), 0.1, 8, FAKE, 7, None, None) == ERR_DTYPE
+    assert fn(*common, ctypes.byref(P), 0.1, 5000, FAKE, 1, None, None) == ERR_SHAPE
+    assert fn(FAKE, FAKE, 4096, FAKE, 44, 60, 32768, ctypes.byref(P), 0.1, 8, FAKE, 1, None, None) == ERR_SHAPE
+    assert fn(*common, ctypes.byref(P), float("nan"), 8, FAKE, 1, None, None) == ERR_VALUE
+    assert fn(*common, ctypes.byref(P), 0.1, 8, None, 1, None, None) == ERR_NULL
+    assert fn(*common, ctypes.byref(P), 0.1, 8, FAKE + 4, 1, None, None) == ERR_ALIGN
+    assert fn(FAKE, FAKE, 4096, FAKE, 0, 64, 32768, ctypes.byref(P), 0.1, 8, FAKE, 1, None, None) == OK
+    assert L.nvfp4_paged_decode_attn_workspace_bytes(44, 64, 47) > (64 << 20)
