@@ -36,3 +36,39 @@ def test_cpu_extend_baseline_runs():
     assert r["kind"] == "oracle" and r["cores"] >= 1
     assert r["quantize_chunk"]["value"] > 0 and r["dequant_prefix"]["value"] > 0
     assert "1024 of 163840" in r["dequant_prefix"]["sample"]
+
+
+def test_headline_is_the_largest_decode_workload():
+    a = bench.parse([])
+    assert a.config == 4 and a.gpus == 1
+    kv = {c: W.config(c).kv_bytes_per_step() for c in range(1, 6)}
+    assert max(kv, key=kv.get) == a.config
+    assert sorted(int(x) for x in a.workloads.split(",")) == [1, 2, 3, 5]
+
+
+def test_trace_summary_of_a_kernel_trace(tmp_path, capsys):
+    import json
+
+    rows = ["Kernel_Name,Start_Timestamp,End_Timestamp,Grid_Size_X"]
+    t = 0
+    for i, d in enumerate([900, 500, 400, 410, 420]):
+        rows.append(f'"void nvfp4kv::(anonymous namespace)::k_decode_split(nvfp4kv::DecodeArgs)",{t},{t + d},1024')
+        t += d + 10
+    rows.append(f"__amd_rocclr_copyBuffer,{t},{t + 5},64")
+    (tmp_path / "run").mkdir()
+    (tmp_path / "run" / "x_kernel_trace.csv").write_text("\n".join(rows) + "\n")
+    bench.trace_summary(str(tmp_path), 2)
+    out = json.loads(capsys.readouterr().out)
+    assert list(out) == ["k_decode_split"]
+    k = out["k_decode_split"]
+    assert k["launches"] == 5 and k["steady_launches"] == 3 and k["steady_mean_ns"] == 410 and k["max_ns"] == 900
+
+
+def test_cpu_baseline_sample_is_bounded():
+    # the sample is whole sequences within the token budget, at least one
+    w = W.config(4)
+    n, tok = 0, 0
+    while n < w.batch and (n == 0 or tok + int(w.seq_lens[n]) <= 786432):
+        tok += int(w.seq_lens[n])
+        n += 1
+    assert n == 4 and tok == 4 * 163840
