@@ -38,6 +38,7 @@ EXPORTED = [
     "nvfp4_kv_amax_workspace_bytes",
     "nvfp4_kv_amax",
     "nvfp4kv_global_scale_for_amax",
+    "nvfp4kv_global_scale_tight_for_amax",
     "fp8kv_pool_bytes",
     "fp8_kv_quantize",
     "fp8_paged_decode_attn_default_splits",
@@ -101,7 +102,7 @@ def lib() -> ctypes.CDLL:
                                                  P, P, c.c_int32, P]
         L.nvfp4_kv_dequant_workspace.restype = c.c_int32
         L.nvfp4_extend_attn.argtypes = [P, P, P, c.c_int32, c.c_int64, P, P, c.c_int64, c.c_int32, c.c_int32,
-                                        c.c_float, P, P, c.POINTER(PoolDesc), P, P]
+                                        c.c_float, c.c_float, P, P, c.POINTER(PoolDesc), P, P]
         L.nvfp4_extend_attn.restype = c.c_int32
         L.nvfp4_kv_amax_workspace_bytes.argtypes = []
         L.nvfp4_kv_amax_workspace_bytes.restype = c.c_size_t
@@ -109,6 +110,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_kv_amax.restype = c.c_int32
         L.nvfp4kv_global_scale_for_amax.argtypes = [c.c_float]
         L.nvfp4kv_global_scale_for_amax.restype = c.c_float
+        L.nvfp4kv_global_scale_tight_for_amax.argtypes = [c.c_float]
+        L.nvfp4kv_global_scale_tight_for_amax.restype = c.c_float
         L.fp8kv_pool_bytes.argtypes = [c.c_int64, c.c_int32]
         L.fp8kv_pool_bytes.restype = c.c_int64
         L.fp8_kv_quantize.argtypes = [P, P, c.c_int32, c.c_int64, c.c_int64, P, c.c_int64, c.POINTER(Fp8PoolDesc), P]
@@ -421,12 +424,14 @@ def nvfp4_kv_dequant_workspace(pool: Pool, page_table: torch.Tensor, seq_lens: t
 def nvfp4_extend_attn(q: torch.Tensor, k_prefix: torch.Tensor, v_prefix: torch.Tensor, k_chunk: torch.Tensor,
                       v_chunk: torch.Tensor, sm_scale: float, out: torch.Tensor | None = None,
                       lse: torch.Tensor | None = None, chunk_pool: "Pool | None" = None,
-                      chunk_slots: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                      chunk_slots: torch.Tensor | None = None, v_bound: float = 0.0, stream=None) -> torch.Tensor:
     """Chunk queries q [C, Hq, 128] (bf16) over the prefix workspace k/v_prefix
     [P, Hkv, 128] (bfloat16 or float8_e4m3fn) and the chunk's own k/v_chunk
     [C, Hkv, 128] (bf16), causal over the chunk. Returns out [C, Hq, 128] bf16;
     fills lse [C, Hq] (float32, natural log) when given. With chunk_pool and
-    chunk_slots (int32 [C]) the same launch quantize-writes the chunk into the pool."""
+    chunk_slots (int32 [C]) the same launch quantize-writes the chunk into the pool.
+    ``v_bound``: an upper bound of |V| over the workspace and the chunk (0 when it
+    is below 2^15; a workspace dequantized at global scale g is bounded by 2688 g)."""
     if (chunk_pool is None) != (chunk_slots is None):
         raise ValueError("chunk_pool and chunk_slots go together")
     if chunk_slots is not None and (chunk_slots.dtype != torch.int32 or chunk_slots.numel() != q.shape[0]):
@@ -457,7 +462,8 @@ def nvfp4_extend_attn(q: torch.Tensor, k_prefix: torch.Tensor, v_prefix: torch.T
                  chunk_slots=chunk_slots)
     _check("nvfp4_extend_attn",
            lib().nvfp4_extend_attn(_ptr(q), _ptr(k_prefix) if P else None, _ptr(v_prefix) if P else None, pdt, P,
-                                   _ptr(k_chunk), _ptr(v_chunk), C, hq, hkv, float(sm_scale), _ptr(out), _ptr(lse),
+                                   _ptr(k_chunk), _ptr(v_chunk), C, hq, hkv, float(sm_scale), float(v_bound),
+                                   _ptr(out), _ptr(lse),
                                    ctypes.byref(chunk_pool.desc()) if chunk_pool is not None else None,
                                    _ptr(chunk_slots), _stream(stream)))
     return out
@@ -530,3 +536,7 @@ def nvfp4_kv_amax(k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = N
 
 def nvfp4kv_global_scale_for_amax(amax: float) -> float:
     return float(lib().nvfp4kv_global_scale_for_amax(float(amax)))
+
+
+def nvfp4kv_global_scale_tight_for_amax(amax: float) -> float:
+    return float(lib().nvfp4kv_global_scale_tight_for_amax(float(amax)))

@@ -14,14 +14,20 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// g must be a power of two in [2^-64, 2^64]: then every threshold of the encode
-// rule and every decoded value stays an exact fp32 product.
+// The NVFP4 global scale g: any finite float in [2^-64, 2^64]. Every dequantized
+// value E2M1 * E4M3 * g then lies inside the normal range of fp32 and bf16.
 bool valid_global_scale(float g) {
-  if (!(g > 0.0f) || !isfinite(g)) return false;
-  int e;
-  const float m = frexpf(g, &e);
-  return m == 0.5f && e - 1 >= -64 && e - 1 <= 64;
+  return isfinite(g) && g >= 0x1p-64f && g <= 0x1p64f;
 }
+
+bool is_pow2(float g) {
+  int e;
+  return isfinite(g) && g > 0.0f && frexpf(g, &e) == 0.5f;
+}
+
+// The FP8 baseline's per-tensor scales: powers of two in [2^-64, 2^64], so that
+// x / s is exact and the per-value encode is one rounding.
+bool valid_pow2_scale(float s) { return valid_global_scale(s) && is_pow2(s); }
 
 int32_t check_pool(const nvfp4kv_pool* pool) {
   if (!pool || !pool->data) return NVFP4KV_ERR_NULL;
@@ -41,7 +47,7 @@ int32_t check_fp8_pool(const fp8kv_pool* pool) {
   if (pool->num_pages > ((int64_t)1 << 40) / ((int64_t)pool->num_kv_heads * 2 * FP8KV_SLAB_BYTES))
     return NVFP4KV_ERR_SHAPE;
   if (!aligned16(pool->data)) return NVFP4KV_ERR_ALIGN;
-  if (!valid_global_scale(pool->k_scale) || !valid_global_scale(pool->v_scale)) return NVFP4KV_ERR_VALUE;
+  if (!valid_pow2_scale(pool->k_scale) || !valid_pow2_scale(pool->v_scale)) return NVFP4KV_ERR_VALUE;
   return NVFP4KV_OK;
 }
 
@@ -81,8 +87,9 @@ int32_t quantize_into(const void* k_src, const void* v_src, int32_t src_dtype, i
   a.pool = static_cast<uint8_t*>(pool.data);
   a.num_kv_heads = pool.num_kv_heads;
   a.g = pool.k_mul;
+  a.g_pow2 = is_pow2(pool.k_mul);
   a.fp8 = pool.fp8;
-  a.inv_k_scale = 1.0f / pool.k_mul;  // powers of two: exact
+  a.inv_k_scale = 1.0f / pool.k_mul;  // FP8 scales are powers of two: exact
   a.inv_v_scale = 1.0f / pool.v_mul;
   return hip_status(nvfp4kv::launch_quantize(a, static_cast<hipStream_t>(stream)));
 }
@@ -148,7 +155,7 @@ const char* nvfp4kv_status_string(int32_t status) {
   }
 }
 
-int32_t nvfp4kv_version(void) { return 1; }
+int32_t nvfp4kv_version(void) { return 2; }
 
 int32_t nvfp4_kv_quantize(const void* k_src, const void* v_src, int32_t src_dtype, int64_t token_stride,
                           int64_t head_stride, const int32_t* slot_mapping, int64_t num_tokens,
@@ -183,6 +190,17 @@ int32_t nvfp4_kv_amax(const void* k_src, const void* v_src, int32_t src_dtype, i
   a.partial = static_cast<float*>(workspace);
   a.out = amax_out;
   return hip_status(nvfp4kv::launch_amax(a, static_cast<hipStream_t>(stream)));
+}
+
+float nvfp4kv_global_scale_tight_for_amax(float amax) {
+  if (!(amax >= 0.0f) || !isfinite(amax)) return 0.0f;
+  if (amax == 0.0f) return 1.0f;
+  // the smallest binary32 g with amax <= 2688 g (an exact comparison in double:
+  // 2688 g has at most 29 significant bits)
+  float g = (float)((double)amax / 2688.0);
+  while (!((double)amax <= 2688.0 * (double)g)) g = nextafterf(g, INFINITY);
+  while (g > 0.0f && (double)amax <= 2688.0 * (double)nextafterf(g, 0.0f)) g = nextafterf(g, 0.0f);
+  return valid_global_scale(g) ? g : 0.0f;
 }
 
 float nvfp4kv_global_scale_for_amax(float amax) {
@@ -364,6 +382,7 @@ int32_t prepare_new_rows(const NewRows& n, int32_t batch, const PoolInfo& pool, 
   a.nw.pool = static_cast<uint8_t*>(pool.data);
   a.nw.num_kv_heads = pool.num_kv_heads;
   a.nw.g = pool.k_mul;
+  a.nw.g_pow2 = is_pow2(pool.k_mul);
   a.nw.fp8 = pool.fp8;
   a.nw.inv_k_scale = 1.0f / pool.k_mul;  // powers of two: exact
   a.nw.inv_v_scale = 1.0f / pool.v_mul;
@@ -385,16 +404,21 @@ int32_t decode_full(const void* q, const int32_t* page_table, int64_t page_table
   const bool phase1_only = new_rows && !out;
   if (phase1_only && lse) return NVFP4KV_ERR_NULL;
   if (batch == 0) return NVFP4KV_OK;
-  if (phase1_only) {
-    if (int32_t e = finish_decode(a)) return e;
-    return hip_status(nvfp4kv::launch_decode_partial(a, static_cast<hipStream_t>(stream)));
-  }
   nvfp4kv::DecodeArgs c;
-  if (int32_t e = prepare_combine(workspace, workspace_bytes, batch, num_q_heads, num_splits, out, out_dtype, lse, c))
-    return e;
+  if (!phase1_only)
+    if (int32_t e = prepare_combine(workspace, workspace_bytes, batch, num_q_heads, num_splits, out, out_dtype, lse, c))
+      return e;
   if (int32_t e = finish_decode(a)) return e;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  // The decode kernel writes the new rows itself only for a power-of-two global
+  // scale (the FP8 baseline's scales are powers of two); otherwise a launch of
+  // its own writes them first, with the same bytes.
+  if (a.write_new && !a.nw.fp8 && !a.nw.g_pow2) {
+    if (int32_t e = hip_status(nvfp4kv::launch_write_newest(a, st))) return e;
+    a.write_new = 0;
+  }
   if (int32_t e = hip_status(nvfp4kv::launch_decode_partial(a, st))) return e;
+  if (phase1_only) return NVFP4KV_OK;
   return hip_status(nvfp4kv::launch_decode_combine(c, st));
 }
 
@@ -490,6 +514,7 @@ int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page
   a.pool = static_cast<const uint8_t*>(pool->data);
   a.num_kv_heads = pool->num_kv_heads;
   a.g = pool->global_scale;
+  a.g_pow2 = is_pow2(pool->global_scale);
   a.page_table = page_table;
   a.pt_stride = page_table_stride;
   a.seq_lens = seq_lens;
@@ -504,8 +529,8 @@ int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page
 
 int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_prefix, int32_t prefix_dtype,
                           int64_t prefix_len, const void* k_chunk, const void* v_chunk, int64_t chunk_len,
-                          int32_t num_q_heads, int32_t num_kv_heads, float sm_scale, void* out, float* lse,
-                          const nvfp4kv_pool* chunk_pool, const int32_t* chunk_slots, void* stream) {
+                          int32_t num_q_heads, int32_t num_kv_heads, float sm_scale, float v_bound, void* out,
+                          float* lse, const nvfp4kv_pool* chunk_pool, const int32_t* chunk_slots, void* stream) {
   if (chunk_pool) {
     if (int32_t e = check_pool(chunk_pool)) return e;
     if (chunk_pool->num_kv_heads != num_kv_heads) return NVFP4KV_ERR_SHAPE;
@@ -517,7 +542,7 @@ int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_pre
   if (prefix_len > ((int64_t)1 << 40) / ((int64_t)num_kv_heads * 128) ||
       chunk_len > ((int64_t)1 << 31) / ((int64_t)num_q_heads * 128))
     return NVFP4KV_ERR_SHAPE;
-  if (!isfinite(sm_scale)) return NVFP4KV_ERR_VALUE;
+  if (!isfinite(sm_scale) || !(v_bound >= 0.0f) || !isfinite(v_bound)) return NVFP4KV_ERR_VALUE;
   if (chunk_len == 0) return NVFP4KV_OK;
   if (!q || !k_chunk || !v_chunk || !out || (prefix_len > 0 && (!k_prefix || !v_prefix))) return NVFP4KV_ERR_NULL;
   if (chunk_pool && !chunk_slots) return NVFP4KV_ERR_NULL;
@@ -539,6 +564,12 @@ int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_pre
   a.group = num_q_heads / num_kv_heads;
   a.qk_scale_log2 = fabsf(sm_scale) * 1.4426950408889634f;
   a.q_sign = sm_scale < 0.0f ? 0x80008000u : 0u;
+  // V is brought below 2^15 in magnitude by an exact power of two before its f16
+  // conversion, and the output scaled back
+  int v_exp = 0;
+  while (ldexpf(v_bound, -v_exp) > 32768.0f) ++v_exp;
+  a.v_mul = ldexpf(1.0f, -v_exp);
+  a.out_mul = ldexpf(1.0f, v_exp);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.tokens_per_block = nvfp4kv::extend_tokens_per_block(a.group);
@@ -558,10 +589,18 @@ int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_pre
     w.pool = static_cast<uint8_t*>(chunk_pool->data);
     w.num_kv_heads = num_kv_heads;
     w.g = chunk_pool->global_scale;
+    w.g_pow2 = is_pow2(chunk_pool->global_scale);
     w.fp8 = 0;
     w.inv_k_scale = w.inv_v_scale = 1.0f;
   }
-  return hip_status(nvfp4kv::launch_extend(a, static_cast<hipStream_t>(stream)));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.write_chunk && !a.qw.g_pow2) {
+    // the extend kernel fuses only the power-of-two encode; any other g is
+    // written by the quantize kernel first (the same bytes)
+    if (int32_t e = hip_status(nvfp4kv::launch_quantize(a.qw, st))) return e;
+    a.write_chunk = 0;
+  }
+  return hip_status(nvfp4kv::launch_extend(a, st));
 }
 
 }  // extern "C"

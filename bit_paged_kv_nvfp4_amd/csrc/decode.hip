@@ -174,9 +174,11 @@ struct Nvfp4Page {
 
   // Encode block j of K (kind 0) or V (kind 1) of token t of the new rows into
   // `slot`. The token is alone in this launch, so V nibbles go in with atomics.
+  // Only a power-of-two global scale is written here; for any other g the host
+  // writes the new rows with k_write_newest before this launch.
   __device__ static __forceinline__ void write_new(const QuantizeArgs& a, int64_t t, int64_t slot, int h, int kind,
                                                    int j) {
-    qenc::write_block(a, t, slot, h, kind, j, false);
+    qenc::write_block<true>(a, t, slot, h, kind, j, false);
   }
 
   // S^T = K^ Q^T for each page (two independent MFMA chains).

@@ -9,9 +9,11 @@
 // lane (G, n) reads channels 8n..8n+7 (4 code bytes) and the scale byte of
 // tokens G, G+4, G+8, G+12; V: lane (n, G) reads its 16-byte chunk (channels
 // 8n..8n+7 of tokens 4G..4G+3) and the four scale bytes of block n/2 for those
-// tokens. Values E2M1(c) * E4M3(s) * g are exact in fp32 and in bf16 (at most 6
-// significant bits); an FP8 E4M3 workspace (the pages' choice) rounds each of
-// them once, from its exact value.
+// tokens. With a power-of-two g the values E2M1(c) * E4M3(s) * g are exact in
+// fp32 and in bf16 (at most 6 significant bits); with any other g the exact
+// product has up to 30 significant bits, and every workspace dtype holds its
+// nearest-even rounding (one rounding). An FP8 E4M3 workspace (the pages'
+// choice) rounds each value once, from its exact value, in both cases.
 #include "nvfp4kv.h"
 #include "nvfp4kv_device.h"
 
@@ -28,14 +30,31 @@ __device__ __forceinline__ uint4 load_once(const uint8_t* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// Eight consecutive values of one output row (exact dequantized values), as
-// one 16-byte store (bf16), two (f32) or one 8-byte store (FP8 E4M3).
-// bf16: the values carry at most 6 significant bits, so the upper half of each
-// f32 is its bf16 encoding and a byte permute packs two. FP8: the hardware
-// conversion rounds to nearest even; clamping to +-448 first (one med3) makes
-// larger magnitudes saturate (a value above 448 rounds to 448 or, from 464 on,
-// would overflow the format).
-__device__ __forceinline__ void store8(void* base, size_t idx, const float (&v)[8], int dtype) {
+// x g rounded to odd in binary32, for an exact x: the nearest-even product hi,
+// its exact error lo = x g - hi (one fma), and, when lo != 0 and the last
+// significand bit of hi is even, the binary32 neighbour of hi on the side of
+// x g. Rounding that value to nearest even in a format of at most 22
+// significant bits (bf16 has 8, E4M3 at most 4) gives the nearest-even
+// rounding of x g itself (Boldo and Melquiond, "Emulation of FMA and correctly
+// rounded sums: proved algorithms using rounding to odd", 2008).
+__device__ __forceinline__ float product_round_odd(float x, float g) {
+#pragma clang fp contract(off)
+  const float hi = x * g;
+  const float lo = __builtin_fmaf(x, g, -hi);
+  uint32_t u = __float_as_uint(hi);
+  // same sign as hi: |x g| > |hi|, one step up in magnitude; else one down
+  if (lo != 0.0f && !(u & 1u)) u += ((__float_as_uint(lo) ^ u) >> 31) ? 0xFFFFFFFFu : 1u;
+  return __uint_as_float(u);
+}
+
+// Eight consecutive values of one output row, as one 16-byte store (bf16), two
+// (f32) or one 8-byte store (FP8 E4M3). bf16: exact values carry at most 6
+// significant bits, so the upper half of each f32 is its bf16 encoding and a
+// byte permute packs two; other values (exact = false) are rounded to nearest
+// even. FP8: the hardware conversion rounds to nearest even; clamping to +-448
+// first (one med3) makes larger magnitudes saturate (a value above 448 rounds to
+// 448 or, from 464 on, would overflow the format).
+__device__ __forceinline__ void store8(void* base, size_t idx, const float (&v)[8], int dtype, bool exact = true) {
   if (dtype == NVFP4KV_FP8_E4M3) {
     float c[8];
 #pragma unroll
@@ -49,9 +68,15 @@ __device__ __forceinline__ void store8(void* base, size_t idx, const float (&v)[
     *reinterpret_cast<uint2*>(static_cast<uint8_t*>(base) + idx) = make_uint2(p[0], p[1]);
   } else if (dtype == NVFP4KV_BF16) {
     uint32_t p[4];
+    if (exact) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      p[i] = __builtin_amdgcn_perm(__float_as_uint(v[2 * i + 1]), __float_as_uint(v[2 * i]), 0x07060302u);
+      for (int i = 0; i < 4; ++i)
+        p[i] = __builtin_amdgcn_perm(__float_as_uint(v[2 * i + 1]), __float_as_uint(v[2 * i]), 0x07060302u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p[i] = (uint32_t)f32_to_bf16_bits(v[2 * i]) | ((uint32_t)f32_to_bf16_bits(v[2 * i + 1]) << 16);
+    }
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx) = make_uint4(p[0], p[1], p[2], p[3]);
   } else {
     float4* o = reinterpret_cast<float4*>(static_cast<float*>(base) + idx);
@@ -60,12 +85,34 @@ __device__ __forceinline__ void store8(void* base, size_t idx, const float (&v)[
   }
 }
 
+// With kExact (power-of-two g) x holds the exact values E2M1(c) E4M3(s) g, and
+// they are stored as they are. Otherwise x holds the unscaled exact values
+// E2M1(c) E4M3(s), and each is multiplied by g here with one rounding to the
+// workspace dtype.
+template <bool kExact>
+__device__ __forceinline__ void scale_and_store8(void* base, size_t idx, const float (&x)[8], float g, int dtype) {
+  if (kExact) {
+    store8(base, idx, x, dtype, true);
+    return;
+  }
+  float v[8];
+  if (dtype == NVFP4KV_F32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = x[e] * g;  // the one rounding to binary32
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = product_round_odd(x[e], g);
+  }
+  store8(base, idx, v, dtype, false);
+}
+
 // One workgroup of 8 waves per (page, sequence); wave w takes KV heads w, w + 8,
 // ... of the page, so one workgroup writes whole workspace rows (all heads of
 // its 16 tokens), and consecutive workgroups write consecutive rows. Measured
 // on the 163840-token prefix (8 heads): one wave per (page, head) in head-major
 // order took 220 us into bf16, this order 142 us; 4 waves with two heads each
 // were 3% slower than 8.
+template <bool kExact>
 __global__ __launch_bounds__(512) void k_dequant(DequantArgs a) {
   const int pg = blockIdx.x;
   const int s = blockIdx.y;
@@ -97,11 +144,11 @@ __global__ __launch_bounds__(512) void k_dequant(DequantArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int tok = 4 * i + G;
       if (tok >= ntok) continue;
-      const float sc = e4m3_to_f32(ks[i]) * a.g;
+      const float sc = kExact ? e4m3_to_f32(ks[i]) * a.g : e4m3_to_f32(ks[i]);  // exact either way
       const f32x2 v0 = fp4x2_to_f32x2<0>(kc[i]), v1 = fp4x2_to_f32x2<1>(kc[i]);
       const f32x2 v2 = fp4x2_to_f32x2<2>(kc[i]), v3 = fp4x2_to_f32x2<3>(kc[i]);
       const float v[8] = {v0[0] * sc, v0[1] * sc, v1[0] * sc, v1[1] * sc, v2[0] * sc, v2[1] * sc, v3[0] * sc, v3[1] * sc};
-      store8(a.k_out, ((size_t)(row0 + tok) * H + h) * kHeadDim + 8 * n, v, dt);
+      scale_and_store8<kExact>(a.k_out, ((size_t)(row0 + tok) * H + h) * kHeadDim + 8 * n, v, a.g, dt);
     }
 
     // ---- V: chunk `lane` = channels 8n..8n+7 of tokens 4G..4G+3 (block n/2) ----
@@ -128,11 +175,12 @@ __global__ __launch_bounds__(512) void k_dequant(DequantArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int tok = 4 * G + i;
       if (tok >= ntok) continue;
-      const float sc = e4m3_to_f32((vs >> (8 * i)) & 0xFFu) * a.g;
+      const float e4 = e4m3_to_f32((vs >> (8 * i)) & 0xFFu);
+      const float sc = kExact ? e4 * a.g : e4;
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = val[i][e] * sc;
-      store8(a.v_out, ((size_t)(row0 + tok) * H + h) * kHeadDim + 8 * n, v, dt);
+      for (int e = 0; e < 8; ++e) v[e] = val[i][e] * sc;  // exact: at most 6 significant bits (times 2^k)
+      scale_and_store8<kExact>(a.v_out, ((size_t)(row0 + tok) * H + h) * kHeadDim + 8 * n, v, a.g, dt);
     }
   }
 }
@@ -142,7 +190,10 @@ __global__ __launch_bounds__(512) void k_dequant(DequantArgs a) {
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream) {
   const int max_pages = (a.max_seq_len + kPage - 1) / kPage;
   if (a.n_seqs == 0 || max_pages == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_dequant, dim3(max_pages, a.n_seqs), dim3(512), 0, stream, a);
+  if (a.g_pow2)
+    hipLaunchKernelGGL(k_dequant<true>, dim3(max_pages, a.n_seqs), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_dequant<false>, dim3(max_pages, a.n_seqs), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

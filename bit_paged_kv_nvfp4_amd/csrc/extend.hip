@@ -29,10 +29,11 @@
 // then converted by the whole workgroup: V into a transposed f16 tile, FP8 K
 // into bf16 (both exact). 16-byte and 8-byte pieces are XOR-swizzled by row so
 // that the rows a quarter-wave reads fall in distinct banks.
-// K enters the first product as bf16, V the second as f16: exact for
-// magnitudes in [2^-14, 65504] (every NVFP4- or FP8-derived workspace value at
-// g = 1 and the usual range of chunk values); below 2^-14 the absolute error
-// stays under 2^-25, and values must stay below 65504.
+// K enters the first product as bf16, V the second as f16: V is first
+// multiplied by a power of two v_mul (1 unless the caller's bound on |V| exceeds
+// 2^15) and the output by 1 / v_mul, so that V stays inside the f16 range; the
+// conversion is then exact for magnitudes in [2^-14, 65504] (after the scaling),
+// and below 2^-14 the absolute error stays under 2^-25 / v_mul.
 // With a pool given, the kernel also quantize-writes the chunk's K/V into it
 // (the prefill path's quantize fused into the attention), each workgroup the
 // blocks of its own tokens and KV head.
@@ -159,18 +160,23 @@ __device__ __forceinline__ uint32_t vt_piece(int d, int q) {
 // Workgroup pass over a landed stage: raw V -> V^T (f16); FP8 K -> bf16 K in the
 // K-operand layout. Thread t: channels 8c .. 8c+7 (c = t / 32) of keys 2m, 2m+1
 // (m = t % 32).
+// V is multiplied by vmul (a power of two, 1 unless the caller's bound on |V|
+// needs it) before the conversion, so that it stays inside the f16 range.
 __device__ __forceinline__ void convert_tile(bool fp8, int t, const uint8_t* k_st, const uint8_t* v_st,
-                                             uint8_t* vt, uint8_t* kconv) {
+                                             uint8_t* vt, uint8_t* kconv, float vmul) {
   const int c = t >> 5, m = t & 31;
   uint32_t lo[4], hi[4];  // channels (8c + 2e, 8c + 2e + 1) of key 2m and of key 2m + 1, as f16 pairs
+  float f0[8], f1[8];     // the same values as f32 (exact)
   if (!fp8) {
     const uint4 a0 = *reinterpret_cast<const uint4*>(v_st + 16 * ((2 * m) * 16 + (c ^ (m & 15))));
     const uint4 a1 = *reinterpret_cast<const uint4*>(v_st + 16 * ((2 * m + 1) * 16 + (c ^ (m & 15))));
     const uint32_t w0[4] = {a0.x, a0.y, a0.z, a0.w}, w1[4] = {a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      lo[e] = f16x2_rne(__uint_as_float(w0[e] << 16), __uint_as_float(w0[e] & 0xFFFF0000u));
-      hi[e] = f16x2_rne(__uint_as_float(w1[e] << 16), __uint_as_float(w1[e] & 0xFFFF0000u));
+      f0[2 * e] = __uint_as_float(w0[e] << 16);
+      f0[2 * e + 1] = __uint_as_float(w0[e] & 0xFFFF0000u);
+      f1[2 * e] = __uint_as_float(w1[e] << 16);
+      f1[2 * e + 1] = __uint_as_float(w1[e] & 0xFFFF0000u);
     }
   } else {
     const int off = 16 * ((c >> 1) ^ (m & 7)) + 8 * (c & 1);
@@ -179,10 +185,26 @@ __device__ __forceinline__ void convert_tile(bool fp8, int t, const uint8_t* k_s
     const uint32_t w0[2] = {b0.x, b0.y}, w1[2] = {b1.x, b1.y};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const f32x2 f0 = fp8x2(w0[e >> 1], e & 1), f1 = fp8x2(w1[e >> 1], e & 1);
-      lo[e] = f16x2_rne(f0[0], f0[1]);
-      hi[e] = f16x2_rne(f1[0], f1[1]);
+      const f32x2 x0 = fp8x2(w0[e >> 1], e & 1), x1 = fp8x2(w1[e >> 1], e & 1);
+      f0[2 * e] = x0[0];
+      f0[2 * e + 1] = x0[1];
+      f1[2 * e] = x1[0];
+      f1[2 * e + 1] = x1[1];
     }
+  }
+  if (vmul != 1.0f) {  // uniform
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      f0[e] *= vmul;
+      f1[e] *= vmul;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo[e] = f16x2_rne(f0[2 * e], f0[2 * e + 1]);
+    hi[e] = f16x2_rne(f1[2 * e], f1[2 * e + 1]);
+  }
+  if (fp8) {
     // FP8 K: thread t widens 16 channels (piece t % 8) of key t / 8
     const int r = t >> 3, j = t & 7;
     const uint4 kb = *reinterpret_cast<const uint4*>(k_st + r * 128 + 16 * j);
@@ -229,7 +251,7 @@ __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   if (a.write_chunk) {
     const int64_t n_blk = (t_last - t_first + 1) * 16;
     for (int64_t idx = t; idx < n_blk; idx += kXThreads)
-      qenc::quantize_one(a.qw, t_first + idx / 16, h, (int)((idx >> 3) & 1), (int)(idx & 7));
+      qenc::quantize_one<true>(a.qw, t_first + idx / 16, h, (int)((idx >> 3) & 1), (int)(idx & 7));
   }
 
   __shared__ __attribute__((aligned(16))) uint8_t k_ring[kStages][kStageBytes];
@@ -316,7 +338,7 @@ __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       issue_tile(tile_of<kPreFp8>(a, h, n_pre, i + 2), Hkv, k_ring_lds + s2 * kStageBytes,
                  v_ring_lds + s2 * kStageBytes, wave, lane);
     }
-    convert_tile(x.fp8, t, k_ring[st], v_ring[st], vt, kconv);
+    convert_tile(x.fp8, t, k_ring[st], v_ring[st], vt, kconv, a.v_mul);
     lds_barrier();  // V^T (and widened K) of tile i complete
 
     // ---- S^T = K Q^T ----
@@ -409,7 +431,7 @@ __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   for (int rb = 0; rb < 2; ++rb) {
     const float l = lacc[rb][0];  // the same row sum in every element
     if (!valid[rb]) continue;
-    const float inv = 1.0f / l;
+    const float inv = a.out_mul / l;  // out_mul = 1 / v_mul, a power of two
     uint16_t* o = a.out + (tok[rb] * a.num_q_heads + qh[rb]) * kHeadDim;
 #pragma unroll
     for (int d = 0; d < 8; ++d) {

@@ -123,6 +123,7 @@ struct QuantizeArgs {
   uint8_t* pool;
   int32_t num_kv_heads;
   float g;
+  int32_t g_pow2;          // 1: g is a power of two (the fast encode applies)
   int32_t fp8;             // 1: the pool is the FP8 baseline
   float inv_k_scale;       // FP8 baseline: 1 / k_scale, 1 / v_scale (powers of two)
   float inv_v_scale;
@@ -172,6 +173,7 @@ struct DequantArgs {
   const uint8_t* pool;
   int32_t num_kv_heads;
   float g;
+  int32_t g_pow2;     // 1: g is a power of two (every dequantized value is exact in fp32)
   const int32_t* page_table;
   int64_t pt_stride;
   const int32_t* seq_lens;
@@ -197,6 +199,8 @@ struct ExtendArgs {
   int32_t group;           // Hq / Hkv
   float qk_scale_log2;     // |sm_scale| * log2(e)
   uint32_t q_sign;         // 0x80008000 when sm_scale < 0 (flips the sign of Q), else 0
+  float v_mul;             // power of two applied to V before its f16 conversion
+  float out_mul;           // 1 / v_mul, applied to the output
   uint16_t* out;           // bf16 bits [C][Hq][128]
   float* lse;              // [C][Hq] natural log, or null
   int32_t tokens_per_block;
@@ -212,6 +216,9 @@ int decode_waves_per_split(bool fp8);
 // Workgroups of the decode kernel that fit on the device at once, per page format.
 int decode_resident_workgroups(int num_cus, bool fp8);
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t stream);
+// The newest token of every sequence (a.nw, a.page_table, a.seq_lens) into the
+// pool, for a global scale that is not a power of two.
+hipError_t launch_write_newest(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
 // Chunk tokens per workgroup of the extend kernel for a GQA group size.

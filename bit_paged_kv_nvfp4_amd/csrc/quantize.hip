@@ -23,6 +23,9 @@ namespace {
 // each word have traded codes across lanes. Otherwise each thread writes its
 // block alone, as the shared block writer does. (K and V in one 256-thread
 // workgroup measured 2-3% slower.)
+// kPow2: the pool's global scale is a power of two (the fast encode); any other
+// g takes the fp64 threshold encode in its own instantiation.
+template <bool kPow2>
 __global__ __launch_bounds__(128) void k_quantize(QuantizeArgs a) {
   const int h = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * kPage;
@@ -35,13 +38,13 @@ __global__ __launch_bounds__(128) void k_quantize(QuantizeArgs a) {
   const int32_t s0 = a.slots[t0];
   const bool whole = __syncthreads_and(live && s0 >= 0 && (s0 & (kPage - 1)) == 0 && slot == s0 + row);
   if (!whole) {
-    if (slot >= 0) qenc::write_block(a, t, slot, h, kind, j, true);
+    if (slot >= 0) qenc::write_block<kPow2>(a, t, slot, h, kind, j, true);
     return;
   }
   uint8_t* slab = a.pool + (((int64_t)(s0 / kPage) * a.num_kv_heads + h) * 2 + kind) * (int64_t)kSlab;
   uint32_t w[2];
   int s;
-  qenc::encode_block(a, t, h, kind, j, w, s);
+  qenc::encode_block<kPow2>(a, t, h, kind, j, w, s);
   if (kind == 0) {
     // K: row r holds its 64 code bytes at 64 r (block j at 8 j), scales at 1024 + 8 r + j
     *reinterpret_cast<uint2*>(slab + row * 64 + j * 8) = make_uint2(w[0], w[1]);
@@ -76,6 +79,22 @@ __global__ __launch_bounds__(128) void k_quantize(QuantizeArgs a) {
   *reinterpret_cast<uint2*>(slab + ((row >> 2) * 16 + 2 * j + (r4 >> 1)) * 16 + 8 * (r4 & 1)) =
       make_uint2(out[0], out[1]);
   slab[kCodeBytes + j * 16 + row] = (uint8_t)s;
+}
+
+// The newest token (position L - 1, L = seq_lens[b]) of every sequence b, token
+// b of nw, written into the pool as the decode kernel's fused write does it
+// (one workgroup per (sequence, KV head), one thread per 16-value block, V
+// nibbles by atomics). The fused decode step runs this first when the global
+// scale is not a power of two, so that the decode kernel itself compiles only
+// the power-of-two encode.
+__global__ __launch_bounds__(64) void k_write_newest(DecodeArgs a) {
+  const int b = blockIdx.x;
+  const int h = blockIdx.y;
+  const int j = threadIdx.x;
+  const int L = a.seq_lens[b];
+  if (L < 1 || j >= 16) return;
+  const int64_t slot = (int64_t)a.page_table[(int64_t)b * a.pt_stride + (L - 1) / kPage] * kPage + (L - 1) % kPage;
+  qenc::write_block<false>(a.nw, b, slot, h, j >> 3, j & 7, false);
 }
 
 // FP8 baseline quantize-on-write: one thread per (token, KV head, K|V, 16-value
@@ -180,6 +199,12 @@ hipError_t launch_amax(const AmaxArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_write_newest(const DecodeArgs& a, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_write_newest, dim3((unsigned)a.batch, (unsigned)a.num_kv_heads), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
   const int64_t threads = a.num_tokens * a.num_kv_heads * 16;
   if (threads == 0) return hipSuccess;
@@ -188,7 +213,11 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(k_quantize_fp8, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   } else {
     const int64_t groups = (a.num_tokens + kPage - 1) / kPage;
-    hipLaunchKernelGGL(k_quantize, dim3((unsigned)groups, (unsigned)a.num_kv_heads, 2), dim3(128), 0, stream, a);
+    const dim3 grid((unsigned)groups, (unsigned)a.num_kv_heads, 2);
+    if (a.g_pow2)
+      hipLaunchKernelGGL(k_quantize<true>, grid, dim3(128), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_quantize<false>, grid, dim3(128), 0, stream, a);
   }
   return hipGetLastError();
 }

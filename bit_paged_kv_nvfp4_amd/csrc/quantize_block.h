@@ -9,10 +9,12 @@
 // auf der NVIDIA RTX PRO 6000 Blackwell Server Edition" (section "Bytes pro
 // Token"): E2M1 values, one E4M3 scale per 16 values, one FP32 scale per tensor.
 //
-// Every rounding decision is taken by exact comparisons in fp32: the thresholds
-// are products of numbers with few significant bits and a power-of-two global
-// scale, so no quotient is ever rounded. This realizes "nearest, ties to even"
-// on the exact real quotients amax/(6g) and x/(E4M3(s) g).
+// Every rounding decision is the one on the exact real quotients amax/(6g) and
+// x/(E4M3(s) g), "nearest, ties to even": for a power-of-two g through a
+// correctly rounded fp32 quotient (proven to take the same decisions), or exact
+// comparisons against threshold products; for any other g through comparisons
+// in fp64, where every threshold (a few-bit constant times an E4M3 value times
+// the 24-bit g, at most 31 significant bits) is exact.
 #pragma once
 
 #include "nvfp4kv_device.h"
@@ -20,22 +22,25 @@
 namespace nvfp4kv {
 namespace qenc {
 
-// E4M3 value of a non-negative finite byte k (0..126), exact in fp32.
-__device__ inline __attribute__((always_inline)) float e4m3_value(int k) {
-  return k < 8 ? (float)k * 0x1p-9f : __builtin_ldexpf((float)(8 + (k & 7)), (k >> 3) - 10);
+// E4M3 value of a non-negative finite byte k (0..126), exact in fp32 (and fp64).
+template <typename T = float>
+__device__ inline __attribute__((always_inline)) T e4m3_value(int k) {
+  return k < 8 ? (T)k * (T)0x1p-9 : __builtin_ldexp((T)(8 + (k & 7)), (k >> 3) - 10);
 }
 
 // Byte of the E4M3 value nearest to amax / six_g (six_g = 6 g), ties to the even
 // byte, clamped to 448 (0x7E). Binary search for the first midpoint between
 // consecutive E4M3 values that amax does not pass; a tie passes the midpoint
-// only when its lower neighbour is odd.
-__device__ inline __attribute__((always_inline)) int scale_byte(float amax, float six_g) {
+// only when its lower neighbour is odd. T = float is exact for a power-of-two g,
+// T = double for any g.
+template <typename T>
+__device__ inline __attribute__((always_inline)) int scale_byte(T amax, T six_g) {
   int lo = 0, hi = 126;
 #pragma unroll
   for (int it = 0; it < 7; ++it) {
     if (lo < hi) {
       const int k = (lo + hi) >> 1;
-      const float thr = (0.5f * (e4m3_value(k) + e4m3_value(k + 1))) * six_g;
+      const T thr = ((T)0.5 * (e4m3_value<T>(k) + e4m3_value<T>(k + 1))) * six_g;
       const bool pass = amax > thr || (amax == thr && (k & 1));
       lo = pass ? k + 1 : lo;
       hi = pass ? hi : k;
@@ -47,14 +52,36 @@ __device__ inline __attribute__((always_inline)) int scale_byte(float amax, floa
 // E2M1 code of x for block divisor D = E4M3(s) g: count of the magnitude
 // midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 (times D) that |x| passes, where
 // a tie passes only midpoints whose lower code is odd; sign bit from x.
-__device__ inline __attribute__((always_inline)) uint32_t e2m1_code(float x, float D, bool zero_scale) {
+template <typename T>
+__device__ inline __attribute__((always_inline)) uint32_t e2m1_code(float x, T D, bool zero_scale) {
   const uint32_t sign = (__float_as_uint(x) >> 28) & 8u;
-  const float ax = __builtin_fabsf(x);
-  uint32_t c = (uint32_t)(ax > 0.25f * D) + (uint32_t)(ax >= 0.75f * D) + (uint32_t)(ax > 1.25f * D) +
-               (uint32_t)(ax >= 1.75f * D) + (uint32_t)(ax > 2.5f * D) + (uint32_t)(ax >= 3.5f * D) +
-               (uint32_t)(ax > 5.0f * D);
+  const T ax = (T)__builtin_fabsf(x);
+  uint32_t c = (uint32_t)(ax > (T)0.25 * D) + (uint32_t)(ax >= (T)0.75 * D) + (uint32_t)(ax > (T)1.25 * D) +
+               (uint32_t)(ax >= (T)1.75 * D) + (uint32_t)(ax > (T)2.5 * D) + (uint32_t)(ax >= (T)3.5 * D) +
+               (uint32_t)(ax > (T)5.0 * D);
   c = zero_scale ? 0u : c;
   return sign | c;
+}
+
+// The threshold path: scale byte by binary search over exact midpoint products,
+// codes by seven exact threshold compares per value. amax ignores NaN elements
+// (fmax drops them), which then pass no threshold and get magnitude 0.
+template <typename T>
+__device__ inline __attribute__((always_inline)) void encode_thresholds(const float (&x)[16], float g,
+                                                                        uint32_t (&w)[2], int& s) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+  s = scale_byte<T>((T)amax, (T)6 * (T)g);
+  const T D = e4m3_value<T>(s) * (T)g;
+  const bool zs = (s == 0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v |= e2m1_code<T>(x[8 * h + i], D, zs) << (4 * i);
+    w[h] = v;
+  }
 }
 
 // The 16 values of block j of token t, head h, kind (0 K, 1 V) as f32.
@@ -100,16 +127,22 @@ __device__ inline __attribute__((always_inline)) float quotient(float x, float D
 // Codes (packed: value i in nibble i % 8 of word i / 8, i.e. the K byte order)
 // and scale byte of the 16 values x, for global scale g.
 //
-// Blocks whose values are all finite, whose scale is not saturated and not zero
-// take the fast path: the scale byte is the nearest-even E4M3 of the quotient
-// amax / (6 g), and every code the nearest-even E2M1 of x / D, D = E4M3(s) g,
-// rounded by the hardware f32 -> fp4 conversion (scale operand 1.0), which
-// saturates at 6 and keeps the sign. Other blocks (NaN or infinite values,
-// amax / (6 g) above 448, a zero scale) take the threshold path: a binary search
-// over exact midpoint products for the scale and seven exact threshold compares
-// per value, where NaN values are ignored by amax and get magnitude 0.
+// With a power-of-two g, blocks whose values are all finite, whose scale is not
+// saturated and not zero take the fast path: the scale byte is the nearest-even
+// E4M3 of the quotient amax / (6 g), and every code the nearest-even E2M1 of
+// x / D, D = E4M3(s) g, rounded by the hardware f32 -> fp4 conversion (scale
+// operand 1.0), which saturates at 6 and keeps the sign. Other blocks (NaN or
+// infinite values, amax / (6 g) above 448, a zero scale) take the threshold
+// path in fp32, whose products are exact for such g. Any other g takes the
+// threshold path in fp64 (kPow2 = false: a separate instantiation, so that the
+// kernels of the power-of-two case keep their registers).
+template <bool kPow2>
 __device__ inline __attribute__((always_inline)) void encode_values(const float (&x)[16], float g, uint32_t (&w)[2],
                                                                     int& s) {
+  if (!kPow2) {
+    encode_thresholds<double>(x, g, w, s);
+    return;
+  }
   float ap = __builtin_fabsf(x[0]);  // NaN-propagating max of |x|
 #pragma unroll
   for (int i = 1; i < 16; ++i) ap = __builtin_elementwise_maximum(ap, __builtin_fabsf(x[i]));
@@ -131,19 +164,7 @@ __device__ inline __attribute__((always_inline)) void encode_values(const float 
       w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, quotient(y[6], D, r), quotient(y[7], D, r), 1.0f, 3);
     }
   } else {
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
-    s = scale_byte(amax, six_g);
-    const float D = e4m3_value(s) * g;
-    const bool zs = (s == 0);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t v = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v |= e2m1_code(x[8 * h + i], D, zs) << (4 * i);
-      w[h] = v;
-    }
+    encode_thresholds<float>(x, g, w, s);
   }
 }
 
@@ -152,12 +173,14 @@ __device__ inline __attribute__((always_inline)) uint32_t nibble(const uint32_t 
   return (w[q >> 3] >> (4 * (q & 7))) & 15u;
 }
 
-// Codes and scale byte of block j of token t, head h, kind (0 K, 1 V).
-__device__ inline __attribute__((always_inline)) void encode_block(const QuantizeArgs& a, int64_t t, int h, int kind, int j,
-                                             uint32_t (&w)[2], int& s) {
+// Codes and scale byte of block j of token t, head h, kind (0 K, 1 V); kPow2
+// must equal a.g_pow2.
+template <bool kPow2>
+__device__ inline __attribute__((always_inline)) void encode_block(const QuantizeArgs& a, int64_t t, int h, int kind,
+                                                                   int j, uint32_t (&w)[2], int& s) {
   float x[16];
   load_block(a, t, h, kind, j, x);
-  encode_values(x, a.g, w, s);
+  encode_values<kPow2>(x, a.g, w, s);
 }
 
 // Encode block j of token t, KV head h, kind (0 K, 1 V) and write its codes and
@@ -165,6 +188,7 @@ __device__ inline __attribute__((always_inline)) void encode_block(const Quantiz
 // written by this call as four consecutive tokens of a.slots (of a.num_tokens)
 // is left to the thread of the group's first token, which writes whole words;
 // otherwise the block's nibbles are set with atomics.
+template <bool kPow2>
 __device__ inline __attribute__((always_inline)) void write_block(const QuantizeArgs& a, int64_t t, int64_t slot,
                                                                   int h, int kind, int j, bool grouped) {
   const int64_t page = slot >> 4;
@@ -187,7 +211,7 @@ __device__ inline __attribute__((always_inline)) void write_block(const Quantize
       uint32_t c4[4][2];
       int s4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) encode_block(a, t + i, h, 1, j, c4[i], s4[i]);
+      for (int i = 0; i < 4; ++i) encode_block<kPow2>(a, t + i, h, 1, j, c4[i], s4[i]);
       // chunk (row/4)*16 + 2j + c holds channels 16j + 8c .. +7; its word wi holds
       // channel q = 8c + 2wi (bytes 0, 1) and q + 1 (bytes 2, 3), rows 0|2 in the
       // even byte and rows 1|3 in the odd one
@@ -211,7 +235,7 @@ __device__ inline __attribute__((always_inline)) void write_block(const Quantize
 
   uint32_t code[2];
   int s;
-  encode_block(a, t, h, kind, j, code, s);
+  encode_block<kPow2>(a, t, h, kind, j, code, s);
   if (kind == 0) {
     // K: the token's 8 code bytes of block j are contiguous, channel 2i in the low
     // nibble of byte i
@@ -242,11 +266,12 @@ __device__ inline __attribute__((always_inline)) void write_block(const Quantize
 
 // Block j of token t (of a.num_tokens), KV head h, kind into slot a.slots[t]
 // (negative: skipped).
+template <bool kPow2>
 __device__ inline __attribute__((always_inline)) void quantize_one(const QuantizeArgs& a, int64_t t, int h,
                                                                    int kind, int j) {
   const int32_t slot = a.slots[t];
   if (slot < 0) return;
-  write_block(a, t, slot, h, kind, j, true);
+  write_block<kPow2>(a, t, slot, h, kind, j, true);
 }
 
 // FP8 baseline pool: block j of token t, head h, kind into `slot` (>= 0), the

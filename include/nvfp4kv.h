@@ -109,7 +109,7 @@ typedef struct nvfp4kv_pool {
   void* data;            /* device, 16-byte aligned, num_pages*num_kv_heads*2*1152 bytes */
   int64_t num_pages;     /* >= 1 */
   int32_t num_kv_heads;  /* >= 1 */
-  float global_scale;    /* g: a power of two in [2^-64, 2^64] (1.0 in all workloads) */
+  float global_scale;    /* g: any finite float in [2^-64, 2^64] (1.0 in all workloads) */
 } nvfp4kv_pool;
 
 /* Bytes of a pool of num_pages pages and num_kv_heads heads. */
@@ -118,7 +118,7 @@ int64_t nvfp4kv_pool_bytes(int64_t num_pages, int32_t num_kv_heads);
 /* Static string for a status code (never NULL). */
 const char* nvfp4kv_status_string(int32_t status);
 
-/* Library ABI version (incremented on any signature or layout change). */
+/* Library ABI version (incremented on any signature or layout change): 2. */
 int32_t nvfp4kv_version(void);
 
 /*
@@ -135,9 +135,13 @@ int32_t nvfp4kv_version(void);
  *   head_stride     elements; multiples of 4 (F32) or 8 (BF16)
  *   slot_mapping    device int32 [num_tokens]
  *   num_tokens      >= 0 (0 is a no-op)
+ * Every rounding decision is the one on the exact real quotients amax/(6 g) and
+ * x/(E4M3(s) g), for any allowed g: with a power of two through an exact fp32
+ * quotient test, otherwise through fp64 comparisons against exact threshold
+ * products (slower: about three times the arithmetic per value).
  * Errors: NULL pointers (ERR_NULL); bad dtype (ERR_DTYPE); unaligned pointer or
  * stride (ERR_ALIGN); negative sizes, a non-positive page or head count
- * (ERR_SHAPE); global scale not a power of two in range (ERR_VALUE).
+ * (ERR_SHAPE); global scale not finite or outside [2^-64, 2^64] (ERR_VALUE).
  */
 int32_t nvfp4_kv_quantize(const void* k_src, const void* v_src, int32_t src_dtype, int64_t token_stride,
                           int64_t head_stride, const int32_t* slot_mapping, int64_t num_tokens,
@@ -292,11 +296,13 @@ int32_t nvfp4_paged_decode_attn_append(const void* q, const void* k_new, const v
  * dequantized into one workspace shared across layers and attended alongside the
  * current chunk). For each listed sequence s and t < seq_lens[s], writes the
  * dequantized K and V rows of every KV head to row row_offsets[s] + t of the
- * dense workspaces k_out / v_out, shaped [rows][num_kv_heads][128]. The values
- * (at most 6 significant bits) are exact in f32 and bf16. With
- * NVFP4KV_FP8_E4M3 (the pages' FP8 workspace) each value is rounded to the
- * nearest E4M3 value, ties to the even code, and values of magnitude above 448
- * become +-448 (saturation); the sign of zero is kept.
+ * dense workspaces k_out / v_out, shaped [rows][num_kv_heads][128]. Each value
+ * is the nearest value of the workspace dtype to the exact E2M1 * E4M3 * g, ties
+ * to even (one rounding): with a power-of-two g the values (at most 6
+ * significant bits) are exact in f32 and bf16; with any other g they carry up
+ * to 30 significant bits and are rounded. With NVFP4KV_FP8_E4M3 (the pages' FP8
+ * workspace) values of magnitude above 448 become +-448 (saturation); the sign
+ * of zero is kept. No value exceeds 2688 g in magnitude.
  *   page_table      device int32 [n_seqs][page_table_stride]
  *   seq_lens        device int32 [n_seqs], prefix tokens to dequantize, each in
  *                   [0, max_seq_len]
@@ -322,6 +328,11 @@ int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page
  * block scale saturates and the largest ones use the top of the E4M3 range; 1.0
  * for amax = 0; 0.0 when amax is negative, not finite, or g would fall outside
  * [2^-64, 2^64]. One pool has one g: pass max(amax[0], amax[1]).
+ * nvfp4kv_global_scale_tight_for_amax (host, pure) returns the smallest binary32
+ * g with amax <= 2688 g ([EUROK] "Bytes pro Token": the global scale is an FP32
+ * number), so that the largest block scale is 448 or just below; the same
+ * conventions for amax = 0 and invalid input. Values dequantized at g reach at
+ * most 2688 g in magnitude: pass that bound as nvfp4_extend_attn's v_bound.
  * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_HIP.
  */
 size_t nvfp4_kv_amax_workspace_bytes(void);
@@ -329,6 +340,7 @@ int32_t nvfp4_kv_amax(const void* k_src, const void* v_src, int32_t src_dtype, i
                       int64_t head_stride, int64_t num_tokens, int32_t num_kv_heads, float* amax_out,
                       void* workspace, size_t workspace_bytes, void* stream);
 float nvfp4kv_global_scale_for_amax(float amax);
+float nvfp4kv_global_scale_tight_for_amax(float amax);
 
 /*
  * ---- FP8 E4M3 baseline ------------------------------------------------------
@@ -415,11 +427,19 @@ int32_t fp8_paged_decode_attn_append(const void* q, const void* k_new, const voi
  * num_q_heads must be a multiple of num_kv_heads with a quotient of at most 16.
  * Arithmetic: fp32 accumulation on the matrix cores; Q and K enter the first
  * product as bf16; V and the softmax weights enter the second as f16 (the row
- * sums use the same rounded weights). V converts exactly for magnitudes in
- * [2^-14, 65504], which holds every NVFP4- or FP8-derived workspace value at
- * g = 1; smaller values carry an absolute error below 2^-25; V values must stay
- * below 65504 in magnitude. All device pointers 16-byte aligned; nothing is
- * allocated; the call is asynchronous on `stream`.
+ * sums use the same rounded weights).
+ *   v_bound         an upper bound of |V| over the workspace and the chunk, or 0
+ *                   when every |V| is at most 2^15. V is multiplied by 2^-e, e the
+ *                   smallest integer >= 0 with v_bound * 2^-e <= 2^15,
+ *                   before its f16 conversion, and the output by 2^e
+ *                   (both exact). A workspace dequantized at global scale g is
+ *                   bounded by 2688 g; a chunk by its amax (nvfp4_kv_amax). With
+ *                   the scaling, V converts exactly for magnitudes in
+ *                   [2^(e-14), 2^(e+15)] and smaller values carry an absolute
+ *                   error below 2^(e-25); a |V| above 65504 * 2^e becomes
+ *                   infinite (a bound that is too small gives a wrong result).
+ * All device pointers 16-byte aligned; nothing is allocated; the call is
+ * asynchronous on `stream`.
  * Fused quantize-on-write ([LMSYS] "Interpretation": the prefill path writes
  * the prompt's keys and values into the NVFP4 cache): when chunk_pool is not
  * NULL, the same launch also writes chunk token i's K/V to slot chunk_slots[i]
@@ -429,13 +449,13 @@ int32_t fp8_paged_decode_attn_append(const void* q, const void* k_new, const voi
  *   chunk_pool      NVFP4 pool or NULL (no write)
  *   chunk_slots     device int32 [C] when chunk_pool is given
  * Errors: ERR_NULL, ERR_SHAPE (counts out of range, group > 16, pool heads),
- * ERR_ALIGN, ERR_DTYPE (prefix_dtype), ERR_VALUE (sm_scale not finite, pool
- * global scale), ERR_HIP.
+ * ERR_ALIGN, ERR_DTYPE (prefix_dtype), ERR_VALUE (sm_scale not finite, v_bound
+ * negative or not finite, pool global scale), ERR_HIP.
  */
 int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_prefix, int32_t prefix_dtype,
                           int64_t prefix_len, const void* k_chunk, const void* v_chunk, int64_t chunk_len,
-                          int32_t num_q_heads, int32_t num_kv_heads, float sm_scale, void* out, float* lse,
-                          const nvfp4kv_pool* chunk_pool, const int32_t* chunk_slots, void* stream);
+                          int32_t num_q_heads, int32_t num_kv_heads, float sm_scale, float v_bound, void* out,
+                          float* lse, const nvfp4kv_pool* chunk_pool, const int32_t* chunk_slots, void* stream);
 
 #ifdef __cplusplus
 }

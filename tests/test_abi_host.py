@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_constants_and_strings(L):
-    assert L.nvfp4kv_version() == 1
+    assert L.nvfp4kv_version() == 2
     assert L.nvfp4kv_pool_bytes(10, 8) == 10 * 8 * 2 * 1152
     for s in range(9):
         assert len(B.status_string(s)) > 0
@@ -81,7 +81,10 @@ def test_quantize_validation(L):
     assert q_call(L, pool(data=FAKE + 8)) == ERR_ALIGN
     assert q_call(L, pool(num_pages=0)) == ERR_SHAPE
     assert q_call(L, pool(hkv=0)) == ERR_SHAPE
-    assert q_call(L, pool(g=3.0)) == ERR_VALUE
+    assert q_call(L, pool(g=3.0), T=0) == OK  # any finite g in [2^-64, 2^64]
+    assert q_call(L, pool(g=0.0)) == ERR_VALUE
+    assert q_call(L, pool(g=-0.3)) == ERR_VALUE
+    assert q_call(L, pool(g=2.0 ** -70)) == ERR_VALUE
     assert q_call(L, pool(g=float("nan"))) == ERR_VALUE
     assert q_call(L, pool(g=2.0 ** 70)) == ERR_VALUE
     assert q_call(L, pool(), dt=2) == ERR_DTYPE
@@ -103,7 +106,8 @@ def d_call(L, p, q=FAKE, pt=FAKE, stride=8, sl=FAKE, B_=2, hq=8, maxlen=100, sm=
 
 def test_decode_validation(L):
     assert d_call(L, None) == ERR_NULL
-    assert d_call(L, pool(g=0.3)) == ERR_VALUE
+    assert d_call(L, pool(g=float("inf"))) == ERR_VALUE
+    assert d_call(L, pool(g=0.3), B_=0) == OK
     assert d_call(L, pool(), odt=2) == ERR_DTYPE
     assert d_call(L, pool(), B_=-1) == ERR_SHAPE
     assert d_call(L, pool(), hq=0) == ERR_SHAPE
@@ -144,7 +148,7 @@ def test_dequant_validation(L):
 
 def e_call(L, q=FAKE, kp=FAKE, vp=FAKE, pdt=1, P=100, kc=FAKE, vc=FAKE, C=10, hq=8, hkv=1, sm=0.088, out=FAKE,
            lse=None):
-    return L.nvfp4_extend_attn(q, kp, vp, pdt, P, kc, vc, C, hq, hkv, sm, out, lse, None, None, None)
+    return L.nvfp4_extend_attn(q, kp, vp, pdt, P, kc, vc, C, hq, hkv, sm, 0.0, out, lse, None, None, None)
 
 
 def test_extend_validation(L):
@@ -234,10 +238,10 @@ def test_amax_validation(L):
 
 def test_extend_fused_write_validation(L):
     p = pool(hkv=1)
-    call = lambda pl, slots: L.nvfp4_extend_attn(FAKE, FAKE, FAKE, 1, 100, FAKE, FAKE, 10, 8, 1, 0.088, FAKE, None,
+    call = lambda pl, slots: L.nvfp4_extend_attn(FAKE, FAKE, FAKE, 1, 100, FAKE, FAKE, 10, 8, 1, 0.088, 0.0, FAKE, None,
                                                  ctypes.byref(pl) if pl is not None else None, slots, None)
     assert call(pool(hkv=2), FAKE) == ERR_SHAPE  # pool heads differ
-    assert call(pool(g=3.0, hkv=1), FAKE) == ERR_VALUE
+    assert call(pool(g=2.0 ** 65, hkv=1), FAKE) == ERR_VALUE
     assert call(p, None) == ERR_NULL
     assert call(p, FAKE + 2) == ERR_ALIGN
 
@@ -250,7 +254,7 @@ def test_decode_append_validation(L):
                   FAKE, 8, FAKE, kw.get("B", 2), kw.get("hq", 8), 100, ctypes.byref(p) if p is not None else None,
                   0.088, 2, FAKE, 1 << 30, kw.get("out", FAKE), kw.get("odt", 1), kw.get("lse"), None)
 
-    for fn, good, bad_scale in ((L.nvfp4_paged_decode_attn_append, pool(hkv=2), pool(hkv=2, g=0.3)),
+    for fn, good, bad_scale in ((L.nvfp4_paged_decode_attn_append, pool(hkv=2), pool(hkv=2, g=0.0)),
                                 (L.fp8_paged_decode_attn_append, fp8_pool(hkv=2), fp8_pool(hkv=2, ks=3.0))):
         assert a(fn, None) == ERR_NULL
         assert a(fn, bad_scale) == ERR_VALUE
@@ -365,3 +369,25 @@ def test_noalloc_decode_rejects_before_any_hip_call(L):
     assert fn(*common, ctypes.byref(P), 0.1, 8, FAKE + 4, 1, None, None) == ERR_ALIGN
     assert fn(FAKE, FAKE, 4096, FAKE, 0, 64, 32768, ctypes.byref(P), 0.1, 8, FAKE, 1, None, None) == OK
     assert L.nvfp4_paged_decode_attn_workspace_bytes(44, 64, 47) > (64 << 20)
+
+
+def test_tight_global_scale_matches_oracle(L):
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(5)
+    for a in np.float32(np.exp(rng.uniform(np.log(1e-9), np.log(1e12), 2000))):
+        assert B.nvfp4kv_global_scale_tight_for_amax(float(a)) == oracle.global_scale_tight_for_amax(float(a)), a
+    assert B.nvfp4kv_global_scale_tight_for_amax(0.0) == 1.0
+    assert B.nvfp4kv_global_scale_tight_for_amax(float("inf")) == 0.0
+    assert B.nvfp4kv_global_scale_tight_for_amax(-2.0) == 0.0
+
+
+def test_extend_v_bound_validation(L):
+    call = lambda vb: L.nvfp4_extend_attn(FAKE, FAKE, FAKE, 1, 100, FAKE, FAKE, 0, 8, 1, 0.088, vb, FAKE, None, None,
+                                          None, None)
+    assert call(0.0) == OK and call(1e30) == OK  # C = 0: nothing to do
+    assert call(-1.0) == ERR_VALUE
+    assert call(float("nan")) == ERR_VALUE
+    assert call(float("inf")) == ERR_VALUE
