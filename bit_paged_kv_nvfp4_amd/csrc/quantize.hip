@@ -24,8 +24,9 @@ namespace {
 // block alone, as the shared block writer does. (K and V in one 256-thread
 // workgroup measured 2-3% slower.)
 // kPow2: the pool's global scale is a power of two (the fast encode); any other
-// g takes the fp64 threshold encode in its own instantiation.
-template <bool kPow2>
+// g takes the fp64 threshold encode in its own instantiation. kBf16: the source
+// dtype (a.bf16).
+template <bool kPow2, bool kBf16>
 __global__ __launch_bounds__(128) void k_quantize(QuantizeArgs a) {
   const int h = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * kPage;
@@ -34,6 +35,10 @@ __global__ __launch_bounds__(128) void k_quantize(QuantizeArgs a) {
   const int j = threadIdx.x & 7;
   const int64_t t = t0 + row;
   const bool live = t < a.num_tokens;
+  // The row's values are requested before the slots and the workgroup vote, so
+  // that the two memory round trips overlap instead of following each other.
+  uint4 raw[4];  // rows past the end load the last token (their values are not used)
+  qenc::load_raw_block<kBf16>(a, live ? t : a.num_tokens - 1, h, kind, j, raw);
   const int32_t slot = live ? a.slots[t] : -1;
   const int32_t s0 = a.slots[t0];
   const bool whole = __syncthreads_and(live && s0 >= 0 && (s0 & (kPage - 1)) == 0 && slot == s0 + row);
@@ -42,9 +47,11 @@ __global__ __launch_bounds__(128) void k_quantize(QuantizeArgs a) {
     return;
   }
   uint8_t* slab = a.pool + (((int64_t)(s0 / kPage) * a.num_kv_heads + h) * 2 + kind) * (int64_t)kSlab;
+  float x[16];
+  qenc::unpack_block<kBf16>(raw, x);
   uint32_t w[2];
   int s;
-  qenc::encode_block<kPow2>(a, t, h, kind, j, w, s);
+  qenc::encode_values<kPow2>(x, a.g, w, s);
   if (kind == 0) {
     // K: row r holds its 64 code bytes at 64 r (block j at 8 j), scales at 1024 + 8 r + j
     *reinterpret_cast<uint2*>(slab + row * 64 + j * 8) = make_uint2(w[0], w[1]);
@@ -214,10 +221,14 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream) {
   } else {
     const int64_t groups = (a.num_tokens + kPage - 1) / kPage;
     const dim3 grid((unsigned)groups, (unsigned)a.num_kv_heads, 2);
-    if (a.g_pow2)
-      hipLaunchKernelGGL(k_quantize<true>, grid, dim3(128), 0, stream, a);
+    if (a.g_pow2 && a.bf16)
+      hipLaunchKernelGGL((k_quantize<true, true>), grid, dim3(128), 0, stream, a);
+    else if (a.g_pow2)
+      hipLaunchKernelGGL((k_quantize<true, false>), grid, dim3(128), 0, stream, a);
+    else if (a.bf16)
+      hipLaunchKernelGGL((k_quantize<false, true>), grid, dim3(128), 0, stream, a);
     else
-      hipLaunchKernelGGL(k_quantize<false>, grid, dim3(128), 0, stream, a);
+      hipLaunchKernelGGL((k_quantize<false, false>), grid, dim3(128), 0, stream, a);
   }
   return hipGetLastError();
 }

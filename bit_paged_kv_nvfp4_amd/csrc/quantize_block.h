@@ -84,6 +84,46 @@ __device__ inline __attribute__((always_inline)) void encode_thresholds(const fl
   }
 }
 
+// The raw bytes of block j of token t, head h, kind (0 K, 1 V): four 16-byte
+// pieces (f32) or two (bf16, u[2] and u[3] unused), converted by unpack_block.
+// Split from the conversion so that a kernel can issue the loads early and wait
+// for them later.
+template <bool kBf16>
+__device__ inline __attribute__((always_inline)) void load_raw_block(const QuantizeArgs& a, int64_t t, int h,
+                                                                     int kind, int j, uint4 (&u)[4]) {
+  const int64_t off = t * a.token_stride + (int64_t)h * a.head_stride + j * 16;
+  if (kBf16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(kind ? a.v : a.k) + off);
+    u[0] = p[0];
+    u[1] = p[1];
+    u[2] = u[3] = make_uint4(0, 0, 0, 0);
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(kind ? a.v : a.k) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = p[i];
+  }
+}
+
+template <bool kBf16>
+__device__ inline __attribute__((always_inline)) void unpack_block(const uint4 (&u)[4], float (&x)[16]) {
+  if (kBf16) {
+    const uint32_t w[8] = {u[0].x, u[0].y, u[0].z, u[0].w, u[1].x, u[1].y, u[1].z, u[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[4 * i] = __uint_as_float(u[i].x);
+      x[4 * i + 1] = __uint_as_float(u[i].y);
+      x[4 * i + 2] = __uint_as_float(u[i].z);
+      x[4 * i + 3] = __uint_as_float(u[i].w);
+    }
+  }
+}
+
 // The 16 values of block j of token t, head h, kind (0 K, 1 V) as f32.
 __device__ inline __attribute__((always_inline)) void load_block(const QuantizeArgs& a, int64_t t, int h, int kind,
                                                                  int j, float (&x)[16]) {
