@@ -46,6 +46,7 @@ EXPORTED = [
     "fp8_paged_decode_attn_partial",
     "fp8_paged_decode_attn_append",
     "nvfp4_paged_decode_attn_noalloc",
+    "nvfp4kv_check_page_table",
 ]
 
 
@@ -128,6 +129,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_paged_decode_attn_noalloc.argtypes = [P, P, c.c_int64, P, c.c_int32, c.c_int32, c.c_int32,
                                                       c.POINTER(PoolDesc), c.c_float, c.c_int32, P, c.c_int32, P, P]
         L.nvfp4_paged_decode_attn_noalloc.restype = c.c_int32
+        L.nvfp4kv_check_page_table.argtypes = [P, c.c_int64, P, c.c_int32, c.c_int32, c.c_int64, P,
+                                               c.POINTER(c.c_int64)]
+        L.nvfp4kv_check_page_table.restype = c.c_int32
         _lib = L
     return _lib
 
@@ -540,3 +544,29 @@ def nvfp4kv_global_scale_for_amax(amax: float) -> float:
 
 def nvfp4kv_global_scale_tight_for_amax(amax: float) -> float:
     return float(lib().nvfp4kv_global_scale_tight_for_amax(float(amax)))
+
+
+def nvfp4kv_check_page_table(page_table, seq_lens, max_seq_len: int, num_pages: int, exclusive: bool = False) -> None:
+    """CPU check of the decode inputs' data preconditions (page ids inside the
+    pool, lengths within max_seq_len and the table row; with ``exclusive``, no
+    physical page holding live tokens of two sequences). Takes host arrays (numpy,
+    or CPU tensors) and raises ValueError naming the first offending entry."""
+    import numpy as np
+
+    pt = np.ascontiguousarray(np.asarray(page_table), dtype=np.int32)
+    sl = np.ascontiguousarray(np.asarray(seq_lens), dtype=np.int32)
+    if pt.ndim != 2 or sl.ndim != 1 or pt.shape[0] < sl.shape[0]:
+        raise ValueError("page_table must be [>= B, stride] and seq_lens [B]")
+    seen = np.zeros(int(num_pages), dtype=np.uint8) if exclusive else None
+    bad = ctypes.c_int64(-1)
+    code = lib().nvfp4kv_check_page_table(pt.ctypes.data, pt.shape[1], sl.ctypes.data, sl.shape[0],
+                                          int(max_seq_len), int(num_pages),
+                                          None if seen is None else seen.ctypes.data, ctypes.byref(bad))
+    if code == 2 and bad.value >= 0:
+        raise ValueError(f"seq_lens[{bad.value}] = {int(sl[bad.value])} is negative or exceeds max_seq_len "
+                         f"{max_seq_len} or the page table row ({pt.shape[1]} pages)")
+    if code == 6:
+        b, p = divmod(bad.value, pt.shape[1])
+        raise ValueError(f"page_table[{b}][{p}] = {int(pt[b, p])} is outside the pool of {num_pages} pages"
+                         + (" or already holds live tokens" if exclusive else ""))
+    _check("nvfp4kv_check_page_table", code)

@@ -157,6 +157,32 @@ const char* nvfp4kv_status_string(int32_t status) {
 
 int32_t nvfp4kv_version(void) { return 2; }
 
+int32_t nvfp4kv_check_page_table(const int32_t* page_table, int64_t page_table_stride, const int32_t* seq_lens,
+                                 int32_t batch, int32_t max_seq_len, int64_t num_pages, uint8_t* seen,
+                                 int64_t* bad_index) {
+  if (batch < 0 || page_table_stride < 1 || max_seq_len < 0 || num_pages < 1) return NVFP4KV_ERR_SHAPE;
+  if (batch == 0) return NVFP4KV_OK;
+  if (!page_table || !seq_lens) return NVFP4KV_ERR_NULL;
+  if (seen) memset(seen, 0, (size_t)num_pages);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t L = seq_lens[b];
+    if (L < 0 || L > max_seq_len || L > page_table_stride * NVFP4KV_PAGE_SIZE) {
+      if (bad_index) *bad_index = b;
+      return NVFP4KV_ERR_SHAPE;
+    }
+    const int64_t pages = (L + NVFP4KV_PAGE_SIZE - 1) / NVFP4KV_PAGE_SIZE;
+    for (int64_t p = 0; p < pages; ++p) {
+      const int64_t id = page_table[b * page_table_stride + p];
+      if (id < 0 || id >= num_pages || (seen && seen[id])) {
+        if (bad_index) *bad_index = b * page_table_stride + p;
+        return NVFP4KV_ERR_VALUE;
+      }
+      if (seen) seen[id] = 1;
+    }
+  }
+  return NVFP4KV_OK;
+}
+
 int32_t nvfp4_kv_quantize(const void* k_src, const void* v_src, int32_t src_dtype, int64_t token_stride,
                           int64_t head_stride, const int32_t* slot_mapping, int64_t num_tokens,
                           const nvfp4kv_pool* pool, void* stream) {

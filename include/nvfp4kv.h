@@ -68,7 +68,8 @@
  *   - Every host-side check runs before any HIP call; on error nothing is
  *     enqueued and a status > 0 is returned. Device-side data errors (a page id
  *     outside the pool, seq_lens[b] > max_seq_len or beyond the page table row,
- *     a slot outside the pool) are undefined behaviour.
+ *     a slot outside the pool) are undefined behaviour; nvfp4kv_check_page_table
+ *     checks them on host copies.
  */
 #ifndef NVFP4KV_H_
 #define NVFP4KV_H_
@@ -120,6 +121,26 @@ const char* nvfp4kv_status_string(int32_t status);
 
 /* Library ABI version (incremented on any signature or layout change): 2. */
 int32_t nvfp4kv_version(void);
+
+/*
+ * Host-side check of the data preconditions the kernels do not check (a page id
+ * outside the pool or a length beyond the table makes them read or write out of
+ * bounds). It reads HOST copies of the page table and the lengths, runs on the
+ * CPU only and makes no HIP call; call it where such inputs are built or in a
+ * debug run. For each b < batch: 0 <= seq_lens[b] <= max_seq_len, seq_lens[b] <=
+ * page_table_stride * 16, and every page id of the first ceil(seq_lens[b] / 16)
+ * entries of row b lies in [0, num_pages). With `seen` (host, num_pages bytes,
+ * contents overwritten) it also checks that no physical page holds live tokens of
+ * two sequences, or twice in one sequence (the fused decode step writes each
+ * sequence's newest page while the others are read). Returns NVFP4KV_OK, or
+ * NVFP4KV_ERR_SHAPE for a length and NVFP4KV_ERR_VALUE for a page id, with
+ * *bad_index (if not NULL) set to the offending b (lengths) or b *
+ * page_table_stride + logical page (ids); NVFP4KV_ERR_NULL / ERR_SHAPE for
+ * missing pointers or negative sizes.
+ */
+int32_t nvfp4kv_check_page_table(const int32_t* page_table, int64_t page_table_stride, const int32_t* seq_lens,
+                                 int32_t batch, int32_t max_seq_len, int64_t num_pages, uint8_t* seen,
+                                 int64_t* bad_index);
 
 /*
  * Quantize-on-write ([LMSYS] "Interpretation"; format per [EUROK] "Bytes pro

@@ -391,3 +391,44 @@ def test_extend_v_bound_validation(L):
     assert call(-1.0) == ERR_VALUE
     assert call(float("nan")) == ERR_VALUE
     assert call(float("inf")) == ERR_VALUE
+
+
+def test_host_page_table_check(L):
+    import numpy as np
+
+    from bit_paged_kv_nvfp4_amd import workload as W
+
+    w = W.small_workload(3, 4, 8, 1, [40, 16, 0, 33])
+    B.nvfp4kv_check_page_table(w.page_table, w.seq_lens, w.max_seq_len, w.num_pages, exclusive=True)
+    bad = w.page_table.copy()
+    bad[1, 0] = w.num_pages  # outside the pool
+    with pytest.raises(ValueError, match=r"page_table\[1\]\[0\]"):
+        B.nvfp4kv_check_page_table(bad, w.seq_lens, w.max_seq_len, w.num_pages)
+    bad = w.page_table.copy()
+    bad[3, 2] = -1
+    with pytest.raises(ValueError, match=r"page_table\[3\]\[2\]"):
+        B.nvfp4kv_check_page_table(bad, w.seq_lens, w.max_seq_len, w.num_pages)
+    # entries past a sequence's last page are not read, so they are not checked
+    ok = w.page_table.copy()
+    ok[1, 1:] = 10 ** 6
+    B.nvfp4kv_check_page_table(ok, w.seq_lens, w.max_seq_len, w.num_pages)
+    lens = w.seq_lens.copy()
+    lens[0] = 41  # beyond max_seq_len 40
+    with pytest.raises(ValueError, match=r"seq_lens\[0\]"):
+        B.nvfp4kv_check_page_table(w.page_table, lens, 40, w.num_pages)
+    lens = w.seq_lens.copy()
+    lens[2] = -1
+    with pytest.raises(ValueError, match=r"seq_lens\[2\]"):
+        B.nvfp4kv_check_page_table(w.page_table, lens, w.max_seq_len, w.num_pages)
+    with pytest.raises(ValueError, match=r"seq_lens\[0\]"):  # more tokens than the row has pages
+        B.nvfp4kv_check_page_table(w.page_table, np.array([16 * w.page_table.shape[1] + 1, 0, 0, 0]), 10 ** 6,
+                                   w.num_pages)
+    shared = w.page_table.copy()
+    shared[3, 1] = shared[0, 2]  # one physical page in two sequences
+    B.nvfp4kv_check_page_table(shared, w.seq_lens, w.max_seq_len, w.num_pages)  # fine without exclusive
+    with pytest.raises(ValueError, match=r"page_table\[3\]\[1\].*already holds"):
+        B.nvfp4kv_check_page_table(shared, w.seq_lens, w.max_seq_len, w.num_pages, exclusive=True)
+    # the C entry point's own argument checks
+    assert L.nvfp4kv_check_page_table(None, 4, None, 0, 0, 1, None, None) == OK
+    assert L.nvfp4kv_check_page_table(None, 4, FAKE, 1, 0, 1, None, None) == ERR_NULL
+    assert L.nvfp4kv_check_page_table(FAKE, 0, FAKE, 1, 0, 1, None, None) == ERR_SHAPE
