@@ -9,83 +9,165 @@
 //
 // One thread encodes one 16-value block (token, KV head, K|V, block); the encode
 // and write rules are in quantize_block.h.
+#include <type_traits>
+
 #include "nvfp4kv_device.h"
 #include "quantize_block.h"
 
 namespace nvfp4kv {
 namespace {
 
-// One workgroup per (16 consecutive tokens, KV head, K|V); thread (row, block)
-// = (threadIdx / 8, threadIdx % 8) encodes block j of token t0 + row. When the
-// 16 tokens fill one page in order (slots s0 .. s0 + 15, s0 a multiple of 16),
-// the workgroup owns that page's K or V slab of this head and writes it whole:
-// K codes and all scales with plain stores, V code words after the four rows of
-// each word have traded codes across lanes. Otherwise each thread writes its
-// block alone, as the shared block writer does. (K and V in one 256-thread
-// workgroup measured 2-3% slower.)
+// Max over the kLB lanes of a 16-value block (aligned groups of 2 or 4
+// consecutive lanes), NaN-propagating (kNan) or NaN-ignoring, by DPP quad
+// permutes.
+template <int kLB, bool kNan>
+__device__ __forceinline__ float block_lanes_max(float v) {
+  auto mx = [](float x, float y) { return kNan ? __builtin_elementwise_maximum(x, y) : __builtin_fmaxf(x, y); };
+  v = mx(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
+  if (kLB == 4)
+    v = mx(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));  // lane ^ 2
+  return v;
+}
+
+// Codes (nibble i = value i) and scale byte of the kVP values x that one lane
+// holds of a 16-value block whose other values sit in the neighbouring lanes of
+// its group of kLB = 16 / kVP: the same decisions as qenc::encode_values on the
+// whole block (amax over the group, then the fast or the threshold rule).
+template <bool kPow2, int kVP>
+__device__ __forceinline__ uint32_t encode_part(const float (&x)[kVP], float g, int& s) {
+  constexpr int kLB = 16 / kVP;
+  float ap = __builtin_fabsf(x[0]);  // NaN-propagating max of |x|
+#pragma unroll
+  for (int i = 1; i < kVP; ++i) ap = __builtin_elementwise_maximum(ap, __builtin_fabsf(x[i]));
+  ap = block_lanes_max<kLB, true>(ap);
+  const float six_g = 6.0f * g;
+  bool fast = kPow2 && ap <= 2688.0f * g;  // 6 * 448 g: false for NaN and infinities
+  if (fast) {
+    s = (int)f32_to_e4m3(qenc::quotient(ap, six_g, 1.0f / six_g));
+    fast = s != 0;
+  }
+  uint32_t cw = 0;
+  if (fast) {  // the same on every lane of the block
+    const float D = e4m3_to_f32((uint32_t)s) * g;
+    const float r = 1.0f / D;
+    auto q = [&](int i) { return qenc::quotient(x[i], D, r); };
+    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, q(0), q(1), 1.0f, 0);
+    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, q(2), q(3), 1.0f, 1);
+    if (kVP == 8) {
+      cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, q(4 % kVP), q(5 % kVP), 1.0f, 2);
+      cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, q(6 % kVP), q(7 % kVP), 1.0f, 3);
+    }
+  } else {
+    using T = typename std::conditional<kPow2, float, double>::type;
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kVP; ++i) am = __builtin_fmaxf(am, __builtin_fabsf(x[i]));
+    am = block_lanes_max<kLB, false>(am);  // NaN elements are left out of amax
+    s = qenc::scale_byte<T>((T)am, (T)6 * (T)g);
+    const T D = qenc::e4m3_value<T>(s) * (T)g;
+#pragma unroll
+    for (int i = 0; i < kVP; ++i) cw |= qenc::e2m1_code<T>(x[i], D, s == 0) << (4 * i);
+  }
+  return cw;
+}
+
+// One workgroup per (16 consecutive tokens, KV head, K|V). When the 16 tokens
+// fill one page in order (slots s0 .. s0 + 15, s0 a multiple of 16), the
+// workgroup owns that page's K or V slab of this head and writes it whole:
+//   - the rows are read with consecutive lanes on consecutive 16-byte pieces
+//     (a wave reads 1 KB per instruction), kVP values per lane, so the kLB
+//     lanes of a 16-value block share its amax through DPP;
+//   - each lane encodes its values and places codes and scale in an image of the
+//     slab in LDS (K bytes by plain writes; V bytes, which hold two rows, by LDS
+//     ORs into zeroed words);
+//   - 72 lanes write the 1,152-byte slab out in 16-byte pieces.
+// Otherwise thread (row, block) = (threadIdx / 8, threadIdx % 8) writes its block
+// alone, as the shared block writer does. The rows are requested before the
+// slots and the workgroup vote, so that the two memory round trips overlap.
 // kPow2: the pool's global scale is a power of two (the fast encode); any other
 // g takes the fp64 threshold encode in its own instantiation. kBf16: the source
 // dtype (a.bf16).
 template <bool kPow2, bool kBf16>
 __global__ __launch_bounds__(128) void k_quantize(QuantizeArgs a) {
+  constexpr int kVP = kBf16 ? 8 : 4;          // values per lane and 16-byte piece
+  constexpr int kLanesPerRow = kBf16 ? 16 : 32;
+  constexpr int kRowsPerLoad = 64 / kLanesPerRow;
+  constexpr int kLoads = 8 / kRowsPerLoad;    // a wave's 8 rows
+  __shared__ __attribute__((aligned(16))) uint8_t img[kSlab];
+
   const int h = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * kPage;
   const int kind = blockIdx.z;
-  const int row = (threadIdx.x >> 3) & 15;
-  const int j = threadIdx.x & 7;
-  const int64_t t = t0 + row;
-  const bool live = t < a.num_tokens;
-  // The row's values are requested before the slots and the workgroup vote, so
-  // that the two memory round trips overlap instead of following each other.
-  uint4 raw[4];  // rows past the end load the last token (their values are not used)
-  qenc::load_raw_block<kBf16>(a, live ? t : a.num_tokens - 1, h, kind, j, raw);
-  const int32_t slot = live ? a.slots[t] : -1;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane % kLanesPerRow;        // 16-byte piece of the row
+  const int sub = lane / kLanesPerRow;
+  const int blk = col * kVP / 16;             // its 16-value block
+  const int d0 = col * kVP;                   // its first channel
+
+  const uint8_t* src = static_cast<const uint8_t*>(kind ? a.v : a.k);
+  const int esz = kBf16 ? 2 : 4;
+  uint4 raw[kLoads];
+#pragma unroll
+  for (int p = 0; p < kLoads; ++p) {
+    const int r = 8 * wave + kRowsPerLoad * p + sub;
+    const int64_t t = min(t0 + r, a.num_tokens - 1);  // rows past the end: not used
+    raw[p] = *reinterpret_cast<const uint4*>(src + (t * a.token_stride + (int64_t)h * a.head_stride + d0) * esz);
+  }
+  const int vrow = (tid >> 3) & 15;
+  const int64_t vt = t0 + vrow;
+  const bool live = vt < a.num_tokens;
+  const int32_t slot = live ? a.slots[vt] : -1;
   const int32_t s0 = a.slots[t0];
-  const bool whole = __syncthreads_and(live && s0 >= 0 && (s0 & (kPage - 1)) == 0 && slot == s0 + row);
+  const bool whole = __syncthreads_and(live && s0 >= 0 && (s0 & (kPage - 1)) == 0 && slot == s0 + vrow);
   if (!whole) {
-    if (slot >= 0) qenc::write_block<kPow2>(a, t, slot, h, kind, j, true);
+    if (slot >= 0) qenc::write_block<kPow2>(a, vt, slot, h, kind, tid & 7, true);
     return;
   }
+  if (tid < kSlab / 16) reinterpret_cast<uint4*>(img)[tid] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < kLoads; ++p) {
+    const int r = 8 * wave + kRowsPerLoad * p + sub;
+    float x[kVP];
+    const uint32_t w[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (kBf16) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      } else {
+        x[i] = __uint_as_float(w[i]);
+      }
+    }
+    int sb;
+    const uint32_t cw = encode_part<kPow2, kVP>(x, a.g, sb);
+    const bool first = (col % (16 / kVP)) == 0;  // the block's first lane writes its scale
+    if (kind == 0) {
+      // K: row r's codes at 64 r, channel d in byte d / 2 (even channel low)
+      if (kBf16)
+        *reinterpret_cast<uint32_t*>(img + r * 64 + d0 / 2) = cw;
+      else
+        *reinterpret_cast<uint16_t*>(img + r * 64 + d0 / 2) = (uint16_t)cw;
+      if (first) img[kCodeBytes + r * 8 + blk] = (uint8_t)sb;
+    } else {
+      // V: channel d of row r in byte ((r/4)*16 + d/8)*16 + 2 (d%8) + r%2, high
+      // nibble for r%4 >= 2; the lane's kVP channels fall in one 16-byte chunk,
+      // two per 32-bit word
+      uint32_t* chunk = reinterpret_cast<uint32_t*>(img + (((r >> 2) * 16 + (d0 >> 3)) * 16));
+      const int sh = 8 * (r & 1) + 4 * ((r >> 1) & 1);
+#pragma unroll
+      for (int i = 0; i < kVP / 2; ++i) {
+        const int e = (d0 & 7) + 2 * i;  // channels d0 + 2i, + 1: bytes 2e and 2e + 2 of the chunk
+        const uint32_t bits = (((cw >> (8 * i)) & 15u) << sh) | (((cw >> (8 * i + 4)) & 15u) << (sh + 16));
+        __hip_atomic_fetch_or(chunk + (e >> 1), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      if (first) img[kCodeBytes + blk * 16 + r] = (uint8_t)sb;
+    }
+  }
+  __syncthreads();
   uint8_t* slab = a.pool + (((int64_t)(s0 / kPage) * a.num_kv_heads + h) * 2 + kind) * (int64_t)kSlab;
-  float x[16];
-  qenc::unpack_block<kBf16>(raw, x);
-  uint32_t w[2];
-  int s;
-  qenc::encode_values<kPow2>(x, a.g, w, s);
-  if (kind == 0) {
-    // K: row r holds its 64 code bytes at 64 r (block j at 8 j), scales at 1024 + 8 r + j
-    *reinterpret_cast<uint2*>(slab + row * 64 + j * 8) = make_uint2(w[0], w[1]);
-    slab[kCodeBytes + row * 8 + j] = (uint8_t)s;
-    return;
-  }
-  // V: the 32 code bytes of block j for rows 4G .. 4G+3 sit in 16-byte chunks
-  // 16 G + 2 j + c (c = 0, 1: channels 8c .. 8c+7 of the block); word wi of a
-  // chunk holds channels q = 8c + 2 wi and q + 1, each as a byte of rows 0|2 (low
-  // nibble row 0) and a byte of rows 1|3. The lane of row 4G + r4 writes the 8
-  // bytes of words 2 (r4 & 1), +1 of chunk c = r4 >> 1, i.e. channels 4 r4 .. 4 r4 + 3
-  // of the four rows: 16-bit field r4 of each row's packed codes.
-  const int r4 = row & 3;
-  const int lane = threadIdx.x & 63;  // = (row % 8) * 8 + j
-  uint32_t f[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int src = lane + 8 * (i - r4);
-    const uint32_t lo = (uint32_t)__shfl((int)w[0], src, 64);
-    const uint32_t hi = (uint32_t)__shfl((int)w[1], src, 64);
-    f[i] = ((r4 >> 1) ? hi : lo) >> (16 * (r4 & 1));
-  }
-  uint32_t out[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    uint32_t b[4];  // channels 4 r4 + 2k (low nibble) and + 1 (high nibble) of row i
-#pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = (f[i] >> (8 * k)) & 0xFFu;
-    out[k] = (b[0] & 15u) | ((b[2] & 15u) << 4) | ((b[1] & 15u) << 8) | ((b[3] & 15u) << 12) |
-             ((b[0] >> 4) << 16) | ((b[2] >> 4) << 20) | ((b[1] >> 4) << 24) | ((b[3] >> 4) << 28);
-  }
-  *reinterpret_cast<uint2*>(slab + ((row >> 2) * 16 + 2 * j + (r4 >> 1)) * 16 + 8 * (r4 & 1)) =
-      make_uint2(out[0], out[1]);
-  slab[kCodeBytes + j * 16 + row] = (uint8_t)s;
+  if (tid < kSlab / 16) reinterpret_cast<uint4*>(slab)[tid] = reinterpret_cast<const uint4*>(img)[tid];
 }
 
 // The newest token (position L - 1, L = seq_lens[b]) of every sequence b, token
