@@ -1,9 +1,13 @@
 """Parity at the five workloads' full sizes, in the launch configuration bench.py
 times (same split rule). The GPU fills the whole pool and decodes the whole batch;
-the oracle recomputes sampled (sequence, KV head) pairs on its own: it quantizes
-the same seeded K/V (bytes must match the GPU pool exactly) and evaluates fp64
-attention for that head's query heads (outputs within 2e-3 + 1e-2 |ref|). Every
-output and LSE of the batch must be finite. Workload 5 also checks the extend
+the oracle recomputes (sequence, KV head) pairs on its own: it quantizes the
+same seeded K/V (bytes must match the GPU pool exactly) and evaluates fp64
+attention for those heads' query heads (outputs within 2e-3 + 1e-2 |ref|). The
+pairs: every KV head of the longest sequence (each of its segments is cut by
+many workgroup windows, so window starts inside a segment and the merged runs
+that close them are all in the check), and one head each of the first, last,
+shortest and a random sequence. Every output and LSE of the batch must be
+finite. Workload 5 also checks the extend
 path: the 8192-token bf16 chunk's quantized bytes in full and sampled rows of the
 dequantized 163840-token prefix, bit-exact."""
 import os
@@ -33,16 +37,19 @@ def fill(w, pool, seqs):
     torch.cuda.synchronize()
 
 
-def oracle_head_pool(w, b, h, L):
-    """The oracle's own single-head pool of sequence b, KV head h (same page ids)."""
-    pool = np.zeros(oracle.pool_bytes(w.num_pages, 1), dtype=np.uint8)
+def oracle_head_pools(w, b, L, heads):
+    """The oracle's own single-head pools of sequence b, one per listed KV head
+    (same page ids); the K/V draws are made once."""
+    pools = {h: np.zeros(oracle.pool_bytes(w.num_pages, 1), dtype=np.uint8) for h in heads}
     for t0 in range(0, L, CHUNK):
         t1 = min(L, t0 + CHUNK)
         k, v = W.kv(w, b, t0, t1, device="cuda")
-        oracle.quantize_to_pool(np.ascontiguousarray(k[:, h:h + 1].cpu().numpy()),
-                                np.ascontiguousarray(v[:, h:h + 1].cpu().numpy()), W.slots(w, b, t0, t1), w.num_pages,
-                                pool=pool, n_threads=THREADS)
-    return pool
+        k, v = k.cpu().numpy(), v.cpu().numpy()
+        for h in heads:
+            oracle.quantize_to_pool(np.ascontiguousarray(k[:, h:h + 1]), np.ascontiguousarray(v[:, h:h + 1]),
+                                    W.slots(w, b, t0, t1), w.num_pages, pool=pools[h], n_threads=THREADS)
+        del k, v
+    return pools
 
 
 def gpu_slabs(w, gpool, pages, h):
@@ -51,10 +58,16 @@ def gpu_slabs(w, gpool, pages, h):
     return data[torch.as_tensor(pages, device="cuda", dtype=torch.long), h].cpu().numpy()
 
 
-def samples(w, n):
+def plan(w):
+    """(sequence, KV heads) to check: every head of the longest sequence, one
+    head each of the first, last, shortest and a random one."""
     rng = np.random.default_rng(w.seed)
-    bs = sorted(set([0, w.batch - 1] + list(rng.integers(0, w.batch, n))))[:n]
-    return [(int(b), int(rng.integers(0, w.num_kv_heads))) for b in bs]
+    lens = w.seq_lens
+    longest = int(np.argmax(lens))
+    out = [(longest, list(range(w.num_kv_heads)))]
+    for b in sorted({0, w.batch - 1, int(np.argmin(lens)), int(rng.integers(0, w.batch))} - {longest}):
+        out.append((b, [int(rng.integers(0, w.num_kv_heads))]))
+    return out
 
 
 @pytest.mark.timeout(900)
@@ -76,22 +89,26 @@ def test_full_size_workload(cfg):
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     qbits = bf16_bits(q.cpu())
     group = w.num_q_heads // w.num_kv_heads
-    for b, h in samples(w, 2 if cfg < 5 else 1):
+    pairs = 0
+    for b, heads in plan(w):
         L = int(w.seq_lens[b])
-        print(f"  sample seq {b} (len {L}) KV head {h}", flush=True)
-        opool = oracle_head_pool(w, b, h, L)
+        print(f"  seq {b} (len {L}) KV heads {heads}", flush=True)
+        pools = oracle_head_pools(w, b, L, heads)
         pages = w.page_table[b, :(L + 15) // 16]
-        got = gpu_slabs(w, gpool, pages, h)
-        want = opool.reshape(w.num_pages, 2 * 1152)[pages]
-        assert np.array_equal(got, want), f"seq {b} head {h}: {int((got != want).sum())} pool bytes differ"
-        units = [b * w.num_q_heads + h * group + g for g in range(group)]
-        # the oracle's single-head view: query heads of KV head h become heads 0..group-1
-        qh = np.ascontiguousarray(qbits[b:b + 1, h * group:(h + 1) * group])
-        ref, ref_lse = oracle.decode_attn(qh, w.page_table[b:b + 1], w.seq_lens[b:b + 1], opool, 1, w.sm_scale,
-                                          n_threads=THREADS)
-        err = assert_close(out[b, h * group:(h + 1) * group], ref[0], what=f"cfg {cfg} seq {b} head {h}")
-        assert_close(lse[b, h * group:(h + 1) * group], ref_lse[0], atol=1e-3, rtol=1e-4, what="lse")
-        print(f"    max abs err {err:.2e}", flush=True)
+        for h in heads:
+            got = gpu_slabs(w, gpool, pages, h)
+            want = pools[h].reshape(w.num_pages, 2 * 1152)[pages]
+            assert np.array_equal(got, want), f"seq {b} head {h}: {int((got != want).sum())} pool bytes differ"
+            # the oracle's single-head view: query heads of KV head h become heads 0..group-1
+            qh = np.ascontiguousarray(qbits[b:b + 1, h * group:(h + 1) * group])
+            ref, ref_lse = oracle.decode_attn(qh, w.page_table[b:b + 1], w.seq_lens[b:b + 1], pools[h], 1,
+                                              w.sm_scale, n_threads=THREADS)
+            err = assert_close(out[b, h * group:(h + 1) * group], ref[0], what=f"cfg {cfg} seq {b} head {h}")
+            assert_close(lse[b, h * group:(h + 1) * group], ref_lse[0], atol=1e-3, rtol=1e-4, what="lse")
+            print(f"    head {h}: max abs err {err:.2e}", flush=True)
+        del pools
+        pairs += len(heads)
+    print(f"  {pairs} of {w.batch * w.num_kv_heads} (sequence, KV head) pairs checked", flush=True)
     if w.extend_prefix:
         extend_checks(w, gpool)
 
