@@ -377,6 +377,8 @@ def extend_step(w, pool, B, W, torch, steps, warmup):
     v_ws = torch.empty_like(k_ws)
     k_w8 = torch.empty((P, w.num_kv_heads, 128), dtype=torch.float8_e4m3fn, device="cuda")
     v_w8 = torch.empty_like(k_w8)
+    k_wt = torch.empty_like(k_ws)  # the tiled workspace: bf16 K rows, f16 V^T tiles
+    v_wt = B.tiled_v_workspace(P, w.num_kv_heads)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     for i in range(warmup):
@@ -395,15 +397,19 @@ def extend_step(w, pool, B, W, torch, steps, warmup):
     d_ms = loop(lambda i: B.nvfp4_kv_dequant_workspace(pool, pts[i % 2], sl, ro, P, k_ws, v_ws, stream=stream), n_small)
     d8_ms = loop(lambda i: B.nvfp4_kv_dequant_workspace(pool, pts[i % 2], sl, ro, P, k_w8, v_w8, stream=stream),
                  n_small)
+    dt_ms = loop(lambda i: B.nvfp4_kv_dequant_workspace(pool, pts[i % 2], sl, ro, P, k_wt, v_wt, stream=stream),
+                 n_small)
     # attention over the bf16 and the FP8 workspace, then the fused prefill path
     # (attention that also quantize-writes the chunk)
     B.nvfp4_kv_dequant_workspace(pool, pts[0], sl, ro, P, k_ws, v_ws, stream=stream)
     B.nvfp4_kv_dequant_workspace(pool, pts[0], sl, ro, P, k_w8, v_w8, stream=stream)
+    B.nvfp4_kv_dequant_workspace(pool, pts[0], sl, ro, P, k_wt, v_wt, stream=stream)
+    at_ms = loop(lambda i: B.nvfp4_extend_attn(qc, k_wt, v_wt, kc, vc, w.sm_scale, out=att_out, stream=stream), n_att)
     a_ms = loop(lambda i: B.nvfp4_extend_attn(qc, k_ws, v_ws, kc, vc, w.sm_scale, out=att_out, stream=stream), n_att)
     a8_ms = loop(lambda i: B.nvfp4_extend_attn(qc, k_w8, v_w8, kc, vc, w.sm_scale, out=att_out, stream=stream), n_att)
     af_ms = loop(lambda i: B.nvfp4_extend_attn(qc, k_ws, v_ws, kc, vc, w.sm_scale, out=att_out, chunk_pool=pool,
                                                chunk_slots=cslots, stream=stream), n_att)
-    del k_ws, v_ws, k_w8, v_w8
+    del k_ws, v_ws, k_w8, v_w8, k_wt, v_wt
     # attention flops: QK^T and PV, 2 x 128 multiply-adds per (query row, visible key)
     a_flops = 4 * w.num_q_heads * 128 * (C * P + C * (C + 1) // 2)
     q_bytes = C * w.num_kv_heads * 128 * 2 * 2 + C * w.num_kv_heads * 2 * 8 * 9  # bf16 in + NVFP4 out
@@ -422,6 +428,10 @@ def extend_step(w, pool, B, W, torch, steps, warmup):
             "attn_ms": round(a_ms, 4), "attn_TFLOPs": round(a_flops / (a_ms * 1e-3) / 1e12, 1),
             "attn_fp8_ms": round(a8_ms, 4), "attn_fp8_TFLOPs": round(a_flops / (a8_ms * 1e-3) / 1e12, 1),
             "attn_flops": a_flops,
+            "dequant_prefix_tiled_ms": round(dt_ms, 5), "attn_tiled_ms": round(at_ms, 4),
+            "attn_tiled_TFLOPs": round(a_flops / (at_ms * 1e-3) / 1e12, 1),
+            "attn_tiled_roofline": roof("mfma", a_flops / (at_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"),
+            "step_tiled_ms": round(q_ms + dt_ms + at_ms, 4),
             "attn_roofline": roof("mfma", a_flops / (a_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"),
             "quantize_roofline": roof("hbm", q_bytes / (q_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
             "dequant_roofline": roof("hbm", d_bytes / (d_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
@@ -598,6 +608,8 @@ def main(argv=None):
     }
     if "fp8_baseline" in head:
         res["fp8_baseline"] = head["fp8_baseline"]
+    if "extend" in head:
+        res["extend"] = head["extend"]
     if fp8 and not args.no_capacity:
         res["capacity"] = capacity(B, W, torch, args.steps, args.warmup, rows_by_len)
     res["workloads"] = {k: v for k, v in workloads.items() if k != w.name}

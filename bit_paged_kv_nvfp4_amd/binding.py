@@ -21,6 +21,7 @@ SLAB_BYTES = 1152
 F32 = 0
 BF16 = 1
 FP8_E4M3 = 2  # extend workspace only
+F16_TILED = 3  # extend workspace: K bf16 rows, V f16 tiles of 64 rows
 
 EXPORTED = [
     "nvfp4kv_pool_bytes",
@@ -47,6 +48,7 @@ EXPORTED = [
     "fp8_paged_decode_attn_append",
     "nvfp4_paged_decode_attn_noalloc",
     "nvfp4kv_check_page_table",
+    "nvfp4kv_tiled_v_bytes",
 ]
 
 
@@ -132,6 +134,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4kv_check_page_table.argtypes = [P, c.c_int64, P, c.c_int32, c.c_int32, c.c_int64, P,
                                                c.POINTER(c.c_int64)]
         L.nvfp4kv_check_page_table.restype = c.c_int32
+        L.nvfp4kv_tiled_v_bytes.argtypes = [c.c_int64, c.c_int32]
+        L.nvfp4kv_tiled_v_bytes.restype = c.c_int64
         _lib = L
     return _lib
 
@@ -409,13 +413,21 @@ def nvfp4_kv_dequant_workspace(pool: Pool, page_table: torch.Tensor, seq_lens: t
         raise ValueError(f"page_table must be contiguous int32 [>= {n}, stride]")
     if int(max_seq_len) > page_table.shape[1] * PAGE_SIZE:
         raise ValueError(f"max_seq_len {max_seq_len} exceeds the page table row ({page_table.shape[1]} pages)")
-    if k_out.dtype != v_out.dtype or not k_out.is_contiguous() or not v_out.is_contiguous():
-        raise ValueError("k_out and v_out must be contiguous and share a dtype")
-    if k_out.shape != v_out.shape or k_out.dim() != 3 or k_out.shape[1:] != (pool.num_kv_heads, HEAD_DIM):
-        raise ValueError(f"k_out and v_out must be [rows, {pool.num_kv_heads}, 128]")
+    if not k_out.is_contiguous() or not v_out.is_contiguous():
+        raise ValueError("k_out and v_out must be contiguous")
+    if k_out.dim() != 3 or k_out.shape[1:] != (pool.num_kv_heads, HEAD_DIM):
+        raise ValueError(f"k_out must be [rows, {pool.num_kv_heads}, 128]")
+    tiled = k_out.dtype == torch.bfloat16 and v_out.dtype == torch.float16
+    if tiled:
+        if v_out.dim() != 4 or v_out.shape[1:] != (pool.num_kv_heads, HEAD_DIM, 64) or \
+                v_out.shape[0] * 64 < k_out.shape[0]:
+            raise ValueError(f"a tiled v_out must be float16 [>= rows / 64, {pool.num_kv_heads}, 128, 64]")
+    elif k_out.dtype != v_out.dtype or k_out.shape != v_out.shape:
+        raise ValueError(f"k_out and v_out must share dtype and shape [rows, {pool.num_kv_heads}, 128] "
+                         "(or be bfloat16 rows and float16 tiles)")
     _same_device(k_out, v_out=v_out, page_table=page_table, seq_lens=seq_lens, row_offsets=row_offsets,
                  pool=pool.data)
-    odt = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}.get(k_out.dtype)
+    odt = F16_TILED if tiled else {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}.get(k_out.dtype)
     if odt is None:
         raise ValueError("workspace dtype must be float32, bfloat16 or float8_e4m3fn")
     d = pool.desc()
@@ -443,16 +455,24 @@ def nvfp4_extend_attn(q: torch.Tensor, k_prefix: torch.Tensor, v_prefix: torch.T
     for name, t in (("q", q), ("k_chunk", k_chunk), ("v_chunk", v_chunk)):
         if t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous bfloat16")
-    if k_prefix.dtype != v_prefix.dtype or not k_prefix.is_contiguous() or not v_prefix.is_contiguous():
-        raise ValueError("k_prefix and v_prefix must be contiguous and share a dtype")
-    pdt = {torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}.get(k_prefix.dtype)
+    if not k_prefix.is_contiguous() or not v_prefix.is_contiguous():
+        raise ValueError("k_prefix and v_prefix must be contiguous")
+    tiled = k_prefix.dtype == torch.bfloat16 and v_prefix.dtype == torch.float16
+    if not tiled and k_prefix.dtype != v_prefix.dtype:
+        raise ValueError("k_prefix and v_prefix must share a dtype (or be bfloat16 rows and float16 tiles)")
+    pdt = F16_TILED if tiled else {torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}.get(k_prefix.dtype)
     if pdt is None:
         raise ValueError("prefix workspace dtype must be bfloat16 or float8_e4m3fn")
     if q.dim() != 3 or q.shape[2] != HEAD_DIM or k_prefix.dim() != 3 or k_chunk.dim() != 3:
         raise ValueError("q, k/v_prefix and k/v_chunk must be [rows, heads, 128]")
     C, hq, _ = q.shape
     P, hkv, _ = k_prefix.shape
-    if tuple(k_prefix.shape) != (P, hkv, HEAD_DIM) or v_prefix.shape != k_prefix.shape:
+    if tuple(k_prefix.shape) != (P, hkv, HEAD_DIM):
+        raise ValueError("k_prefix must be [P, Hkv, 128]")
+    if tiled:
+        if v_prefix.dim() != 4 or v_prefix.shape[1:] != (hkv, HEAD_DIM, 64) or v_prefix.shape[0] * 64 < P:
+            raise ValueError("a tiled v_prefix must be float16 [>= P / 64, Hkv, 128, 64]")
+    elif v_prefix.shape != k_prefix.shape:
         raise ValueError("k_prefix and v_prefix must both be [P, Hkv, 128]")
     if tuple(k_chunk.shape) != (C, hkv, HEAD_DIM) or v_chunk.shape != k_chunk.shape:
         raise ValueError(f"k_chunk and v_chunk must both be [{C}, {hkv}, 128]")
@@ -570,3 +590,13 @@ def nvfp4kv_check_page_table(page_table, seq_lens, max_seq_len: int, num_pages: 
         raise ValueError(f"page_table[{b}][{p}] = {int(pt[b, p])} is outside the pool of {num_pages} pages"
                          + (" or already holds live tokens" if exclusive else ""))
     _check("nvfp4kv_check_page_table", code)
+
+
+def nvfp4kv_tiled_v_bytes(rows: int, num_kv_heads: int) -> int:
+    return int(lib().nvfp4kv_tiled_v_bytes(int(rows), int(num_kv_heads)))
+
+
+def tiled_v_workspace(rows: int, num_kv_heads: int, device="cuda") -> torch.Tensor:
+    """A float16 [ceil(rows / 64), Hkv, 128, 64] tensor for the V part of an
+    NVFP4KV_F16_TILED workspace (layout in the C header)."""
+    return torch.empty(((rows + 63) // 64, num_kv_heads, HEAD_DIM, 64), dtype=torch.float16, device=device)

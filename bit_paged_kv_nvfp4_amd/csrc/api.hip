@@ -239,6 +239,11 @@ float nvfp4kv_global_scale_for_amax(float amax) {
   return valid_global_scale(gf) ? gf : 0.0f;
 }
 
+int64_t nvfp4kv_tiled_v_bytes(int64_t rows, int32_t num_kv_heads) {
+  if (rows < 0 || num_kv_heads < 0) return 0;
+  return (rows + 63) / 64 * num_kv_heads * (int64_t)(64 * NVFP4KV_HEAD_DIM * 2);
+}
+
 int64_t fp8kv_pool_bytes(int64_t num_pages, int32_t num_kv_heads) {
   if (num_pages < 0 || num_kv_heads < 0) return 0;
   return num_pages * num_kv_heads * 2 * (int64_t)FP8KV_SLAB_BYTES;
@@ -526,8 +531,11 @@ int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page
                                    const int32_t* seq_lens, const int64_t* row_offsets, int32_t n_seqs,
                                    int32_t max_seq_len, void* k_out, void* v_out, int32_t out_dtype, void* stream) {
   if (int32_t e = check_pool(pool)) return e;
-  if (out_dtype != NVFP4KV_F32 && out_dtype != NVFP4KV_BF16 && out_dtype != NVFP4KV_FP8_E4M3)
+  if (out_dtype != NVFP4KV_F32 && out_dtype != NVFP4KV_BF16 && out_dtype != NVFP4KV_FP8_E4M3 &&
+      out_dtype != NVFP4KV_F16_TILED)
     return NVFP4KV_ERR_DTYPE;
+  // f16 holds every dequantized value (at most 2688 g) only for g <= 16
+  if (out_dtype == NVFP4KV_F16_TILED && !(pool->global_scale <= 16.0f)) return NVFP4KV_ERR_VALUE;
   if (n_seqs < 0 || max_seq_len < 0 || page_table_stride < 1) return NVFP4KV_ERR_SHAPE;
   if ((int64_t)max_seq_len > page_table_stride * NVFP4KV_PAGE_SIZE) return NVFP4KV_ERR_SHAPE;
   if (n_seqs > 65535 || pool->num_kv_heads > 65535) return NVFP4KV_ERR_SHAPE;
@@ -561,7 +569,10 @@ int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_pre
     if (int32_t e = check_pool(chunk_pool)) return e;
     if (chunk_pool->num_kv_heads != num_kv_heads) return NVFP4KV_ERR_SHAPE;
   }
-  if (prefix_dtype != NVFP4KV_BF16 && prefix_dtype != NVFP4KV_FP8_E4M3) return NVFP4KV_ERR_DTYPE;
+  if (prefix_dtype != NVFP4KV_BF16 && prefix_dtype != NVFP4KV_FP8_E4M3 && prefix_dtype != NVFP4KV_F16_TILED)
+    return NVFP4KV_ERR_DTYPE;
+  // a tiled prefix's V arrives in f16 as it is: no room for a power-of-two scaling
+  if (prefix_dtype == NVFP4KV_F16_TILED && prefix_len > 0 && v_bound > 32768.0f) return NVFP4KV_ERR_VALUE;
   if (prefix_len < 0 || chunk_len < 0 || num_q_heads < 1 || num_kv_heads < 1) return NVFP4KV_ERR_SHAPE;
   if (num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > NVFP4KV_MAX_GROUP) return NVFP4KV_ERR_SHAPE;
   // element offsets of every operand stay far inside int64
@@ -580,7 +591,7 @@ int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_pre
   a.q = static_cast<const uint16_t*>(q);
   a.k_pre = k_prefix;
   a.v_pre = v_prefix;
-  a.pre_fp8 = prefix_dtype == NVFP4KV_FP8_E4M3;
+  a.pre_kind = prefix_dtype == NVFP4KV_FP8_E4M3 ? 1 : prefix_dtype == NVFP4KV_F16_TILED ? 2 : 0;
   a.prefix_len = prefix_len;
   a.k_chunk = static_cast<const uint16_t*>(k_chunk);
   a.v_chunk = static_cast<const uint16_t*>(v_chunk);

@@ -106,13 +106,33 @@ __device__ __forceinline__ void scale_and_store8(void* base, size_t idx, const f
   store8(base, idx, v, dtype, false);
 }
 
+// The V side of the NVFP4KV_F16_TILED workspace: key (row) r of KV head h sits
+// in tile r / 64 at byte ((r / 64) H + h) 16384: 128 channel rows of 128 bytes,
+// key k = r % 64 of channel d at byte d 128 + 16 u + 8 half + 2 pos with
+// u = 4 (k / 32) + (k / 4) % 4, half = (k / 16) % 2, pos = k % 4. That is the
+// order in which the extend attention's PV operands take the keys (unit u = 4 ks
+// + G holds keys 32 ks + 4 G .. +3, then 32 ks + 16 + 4 G .. +3), so its tiles
+// are copied into LDS as they are.
+__device__ __forceinline__ size_t vt_offset(int64_t r, int h, int H, int d) {
+  const int k = (int)(r & 63);
+  return ((size_t)(r >> 6) * H + h) * 16384 + d * 128 + 16 * (4 * (k >> 5) + ((k >> 2) & 3)) + 8 * ((k >> 4) & 1) +
+         2 * (k & 3);
+}
+
+// Four f16 values of one channel, keys r .. r + 3 (r % 4 == 0), as 8 bytes.
+__device__ __forceinline__ void store_vt4(void* base, size_t off, const float (&x)[4]) {
+  const f16x2 lo = {(_Float16)x[0], (_Float16)x[1]}, hi = {(_Float16)x[2], (_Float16)x[3]};
+  *reinterpret_cast<uint2*>(static_cast<uint8_t*>(base) + off) = make_uint2(as_u32(lo), as_u32(hi));
+}
+
 // One workgroup of 8 waves per (page, sequence); wave w takes KV heads w, w + 8,
 // ... of the page, so one workgroup writes whole workspace rows (all heads of
 // its 16 tokens), and consecutive workgroups write consecutive rows. Measured
 // on the 163840-token prefix (8 heads): one wave per (page, head) in head-major
 // order took 220 us into bf16, this order 142 us; 4 waves with two heads each
 // were 3% slower than 8.
-template <bool kExact>
+// kTiled: the NVFP4KV_F16_TILED workspace (K as bf16 rows, V as f16 tiles).
+template <bool kExact, bool kTiled>
 __global__ __launch_bounds__(512) void k_dequant(DequantArgs a) {
   const int pg = blockIdx.x;
   const int s = blockIdx.y;
@@ -124,8 +144,10 @@ __global__ __launch_bounds__(512) void k_dequant(DequantArgs a) {
   const int64_t pid = a.page_table[(int64_t)s * a.pt_stride + pg];
   const int64_t row0 = a.row_offsets[s] + (int64_t)pg * kPage;
   const int H = a.num_kv_heads;
-  const int dt = a.out_dtype;
+  const int dt = kTiled ? NVFP4KV_BF16 : a.out_dtype;  // the K side
   const int ntok = min(kPage, L - pg * kPage);
+  // tiled V: 8-byte stores when the sequence starts on a multiple of 4 rows
+  const bool vt_aligned = (a.row_offsets[s] & 3) == 0;
 
   for (int h = threadIdx.x >> 6; h < H; h += 8) {
     const uint8_t* kslab = a.pool + (pid * H + h) * (int64_t)(2 * kSlab);
@@ -171,16 +193,55 @@ __global__ __launch_bounds__(512) void k_dequant(DequantArgs a) {
       val[1][2 * w + 1] = c3[0];
       val[3][2 * w + 1] = c3[1];
     }
+    if (!kTiled) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 4 * G + i;
+        if (tok >= ntok) continue;
+        const float e4 = e4m3_to_f32((vs >> (8 * i)) & 0xFFu);
+        const float sc = kExact ? e4 * a.g : e4;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = val[i][e] * sc;  // exact: at most 6 significant bits (times 2^k)
+        scale_and_store8<kExact>(a.v_out, ((size_t)(row0 + tok) * H + h) * kHeadDim + 8 * n, v, a.g, dt);
+      }
+      continue;
+    }
+    // tiled V: per channel, the lane's four keys 4G .. 4G+3 (zeros past the
+    // sequence), each value rounded once to f16
+    float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tok = 4 * G + i;
-      if (tok >= ntok) continue;
       const float e4 = e4m3_to_f32((vs >> (8 * i)) & 0xFFu);
-      const float sc = kExact ? e4 * a.g : e4;
-      float v[8];
+      sc[i] = kExact ? e4 * a.g : e4;
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = val[i][e] * sc;  // exact: at most 6 significant bits (times 2^k)
-      scale_and_store8<kExact>(a.v_out, ((size_t)(row0 + tok) * H + h) * kHeadDim + 8 * n, v, a.g, dt);
+    for (int e = 0; e < 8; ++e) {
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = val[i][e] * sc[i];  // exact
+        x[i] = 4 * G + i >= ntok ? 0.0f : kExact ? v : product_round_odd(v, a.g);
+      }
+      const int d = 8 * n + e;
+      if (vt_aligned) {
+        store_vt4(a.v_out, vt_offset(row0 + 4 * G, h, H, d), x);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * G + i < ntok)
+            *reinterpret_cast<_Float16*>(static_cast<uint8_t*>(a.v_out) + vt_offset(row0 + 4 * G + i, h, H, d)) =
+                (_Float16)x[i];
+      }
+    }
+    // the sequence's last page also zeroes the rest of its last tile, so that the
+    // attention's masked keys multiply finite values
+    if (vt_aligned && (pg + 1) * kPage >= L) {
+      const float zero[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      const int64_t tile_end = ((row0 + kPage + 63) >> 6) << 6;
+      for (int64_t r = row0 + kPage + 4 * G; r < tile_end; r += 16)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) store_vt4(a.v_out, vt_offset(r, h, H, 8 * n + e), zero);
     }
   }
 }
@@ -190,10 +251,16 @@ __global__ __launch_bounds__(512) void k_dequant(DequantArgs a) {
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream) {
   const int max_pages = (a.max_seq_len + kPage - 1) / kPage;
   if (a.n_seqs == 0 || max_pages == 0) return hipSuccess;
-  if (a.g_pow2)
-    hipLaunchKernelGGL(k_dequant<true>, dim3(max_pages, a.n_seqs), dim3(512), 0, stream, a);
+  const dim3 grid(max_pages, a.n_seqs);
+  const bool tiled = a.out_dtype == NVFP4KV_F16_TILED;
+  if (a.g_pow2 && tiled)
+    hipLaunchKernelGGL((k_dequant<true, true>), grid, dim3(512), 0, stream, a);
+  else if (a.g_pow2)
+    hipLaunchKernelGGL((k_dequant<true, false>), grid, dim3(512), 0, stream, a);
+  else if (tiled)
+    hipLaunchKernelGGL((k_dequant<false, true>), grid, dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_dequant<false>, dim3(max_pages, a.n_seqs), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((k_dequant<false, false>), grid, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -82,32 +82,40 @@ __device__ __forceinline__ uint32_t bf16x2_exact(f32x2 f) {
   return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
 }
 
+// Prefix workspace kinds: bf16 rows, FP8 E4M3 rows, or bf16 K rows with V as
+// f16 tiles already in the PV operand order (NVFP4KV_F16_TILED).
+constexpr int kPreBf16 = 0, kPreFp8Rows = 1, kPreTiled = 2;
+
 // One tile: its keys' source rows and dtype.
 struct Tile {
   const uint8_t* k;  // K row of the tile's first key, this head
-  const uint8_t* v;
+  const uint8_t* v;  // V row of the tile's first key, or the tile's V^T (vtile)
   int n_valid;       // keys of the tile that exist (the rest is masked)
   bool fp8;          // rows are E4M3 bytes (else bf16)
+  bool vtile;        // V arrives as a ready f16 V^T tile (16 KB, operand order)
   bool chunk;        // chunk tile (causal mask) or prefix tile
   int64_t first;     // index of the first key in the chunk (chunk tile) or prefix
 };
 
-template <bool kPreFp8>
+template <int kPre>
 __device__ __forceinline__ Tile tile_of(const ExtendArgs& a, int h, int n_pre, int i) {
   Tile x;
   const int64_t Hkv = a.num_kv_heads;
   if (i < n_pre) {
+    constexpr bool fp8 = kPre == kPreFp8Rows;
     x.first = (int64_t)i * kTile;
     x.n_valid = (int)min<int64_t>(kTile, a.prefix_len - x.first);
-    x.fp8 = kPreFp8;
+    x.fp8 = fp8;
+    x.vtile = kPre == kPreTiled;
     x.chunk = false;
-    const int64_t row = (x.first * Hkv + h) * kHeadDim * (kPreFp8 ? 1 : 2);
+    const int64_t row = (x.first * Hkv + h) * kHeadDim * (fp8 ? 1 : 2);
     x.k = static_cast<const uint8_t*>(a.k_pre) + row;
-    x.v = static_cast<const uint8_t*>(a.v_pre) + row;
+    x.v = static_cast<const uint8_t*>(a.v_pre) + (x.vtile ? ((int64_t)i * Hkv + h) * (kTile * kHeadDim * 2) : row);
   } else {
     x.first = (int64_t)(i - n_pre) * kTile;
     x.n_valid = (int)min<int64_t>(kTile, a.chunk_len - x.first);
     x.fp8 = false;
+    x.vtile = false;
     x.chunk = true;
     const int64_t row = (x.first * Hkv + h) * kHeadDim * 2;
     x.k = reinterpret_cast<const uint8_t*>(a.k_chunk) + row;
@@ -123,6 +131,8 @@ __device__ __forceinline__ Tile tile_of(const ExtendArgs& a, int h, int n_pre, i
 //   K FP8:  piece (16 B = 16 channels) j of key r at slot r * 8 + j
 //   V FP8:  piece j of key r at slot r * 8 + (j ^ ((r >> 1) & 7))
 // Keys past n_valid copy the tile's last valid row (in bounds; masked later).
+//   V^T tile (vtile): the f16 tile lands in the V^T layout below (vt_unit), its
+//   16-byte units XOR-swizzled by channel as the conversion pass writes them.
 __device__ __forceinline__ void issue_tile(const Tile& x, int hkv, uint32_t k_lds, uint32_t v_lds, int w,
                                            int lane) {
   if (!x.fp8) {
@@ -133,7 +143,13 @@ __device__ __forceinline__ void issue_tile(const Tile& x, int hkv, uint32_t k_ld
       const int r = p >> 4, cs = p & 15;
       const uint32_t rr = (uint32_t)min(r, x.n_valid - 1);
       dma16(x.k, rr * rs + 16 * (cs ^ (r & 15)), k_lds + (2 * w + j) * 1024);
-      dma16(x.v, rr * rs + 16 * (cs ^ ((r >> 1) & 15)), v_lds + (2 * w + j) * 1024);
+      if (x.vtile) {
+        // LDS unit p = 8 d + u' holds source unit u' ^ (d & 7) of channel d
+        const int d = p >> 3, up = p & 7;
+        dma16(x.v, (uint32_t)(d * 128 + 16 * (up ^ (d & 7))), v_lds + (2 * w + j) * 1024);
+      } else {
+        dma16(x.v, rr * rs + 16 * (cs ^ ((r >> 1) & 15)), v_lds + (2 * w + j) * 1024);
+      }
     }
   } else {
     const uint32_t rs = (uint32_t)hkv * 128;
@@ -229,8 +245,9 @@ __device__ __forceinline__ void convert_tile(bool fp8, int t, const uint8_t* k_s
   }
 }
 
-template <bool kPreFp8>
+template <int kPre>
 __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_extend_attn(ExtendArgs a) {
+  constexpr bool kPreFp8 = kPre == kPreFp8Rows;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -319,12 +336,12 @@ __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 
   // prologue: tiles 0 and 1 in flight
   for (int i = 0; i < 2 && i < n_tiles; ++i)
-    issue_tile(tile_of<kPreFp8>(a, h, n_pre, i), Hkv, k_ring_lds + i * kStageBytes, v_ring_lds + i * kStageBytes,
+    issue_tile(tile_of<kPre>(a, h, n_pre, i), Hkv, k_ring_lds + i * kStageBytes, v_ring_lds + i * kStageBytes,
                wave, lane);
 
   for (int i = 0; i < n_tiles; ++i) {
     const int st = i % kStages;
-    const Tile x = tile_of<kPreFp8>(a, h, n_pre, i);
+    const Tile x = tile_of<kPre>(a, h, n_pre, i);
     // this wave's copies of tile i have landed once only tile i+1's are pending
     if (i + 1 >= n_tiles)
       wait_dma<0>();
@@ -335,11 +352,14 @@ __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     lds_barrier();  // every wave: tile i landed, tile i-1 fully consumed
     if (i + 2 < n_tiles) {
       const int s2 = (i + 2) % kStages;
-      issue_tile(tile_of<kPreFp8>(a, h, n_pre, i + 2), Hkv, k_ring_lds + s2 * kStageBytes,
+      issue_tile(tile_of<kPre>(a, h, n_pre, i + 2), Hkv, k_ring_lds + s2 * kStageBytes,
                  v_ring_lds + s2 * kStageBytes, wave, lane);
     }
-    convert_tile(x.fp8, t, k_ring[st], v_ring[st], vt, kconv, a.v_mul);
-    lds_barrier();  // V^T (and widened K) of tile i complete
+    if (!x.vtile) {
+      convert_tile(x.fp8, t, k_ring[st], v_ring[st], vt, kconv, a.v_mul);
+      lds_barrier();  // V^T (and widened K) of tile i complete
+    }
+    const uint8_t* vsrc = x.vtile ? v_ring[st] : vt;  // a V^T tile that arrived ready, or the converted one
 
     // ---- S^T = K Q^T ----
     const uint4* kt = reinterpret_cast<const uint4*>(x.fp8 ? kconv : k_ring[st]);
@@ -415,7 +435,7 @@ __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         const int dim = 16 * d + n;
-        const f16x8 vf = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(vt + vt_unit(dim, 4 * ks + G)));
+        const f16x8 vf = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(vsrc + vt_unit(dim, 4 * ks + G)));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
           oacc[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[ks][rb], oacc[d][rb], 0, 0, 0);
@@ -451,10 +471,12 @@ int extend_tokens_per_block(int group) { return kXWaves * kXRows / group; }
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream) {
   if (a.chunk_len == 0) return hipSuccess;
   const dim3 grid((unsigned)a.num_token_blocks * (unsigned)a.num_kv_heads), block(kXThreads);
-  if (a.pre_fp8)
-    hipLaunchKernelGGL(k_extend_attn<true>, grid, block, 0, stream, a);
+  if (a.pre_kind == kPreFp8Rows)
+    hipLaunchKernelGGL(k_extend_attn<kPreFp8Rows>, grid, block, 0, stream, a);
+  else if (a.pre_kind == kPreTiled)
+    hipLaunchKernelGGL(k_extend_attn<kPreTiled>, grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(k_extend_attn<false>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(k_extend_attn<kPreBf16>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

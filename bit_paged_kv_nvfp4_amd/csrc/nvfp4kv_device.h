@@ -188,8 +188,8 @@ struct DequantArgs {
 struct ExtendArgs {
   const uint16_t* q;       // bf16 bits [C][Hq][128]
   const void* k_pre;       // prefix workspace [P][Hkv][128], bf16 or FP8 E4M3
-  const void* v_pre;
-  int32_t pre_fp8;         // 1: the prefix workspace holds FP8 E4M3 bytes
+  const void* v_pre;       // the same, or f16 V^T tiles [ceil(P/64)][Hkv][128][64] (pre_kind 2)
+  int32_t pre_kind;        // 0: bf16 rows, 1: FP8 E4M3 rows, 2: bf16 K rows + f16 V^T tiles
   int64_t prefix_len;      // P
   const uint16_t* k_chunk; // bf16 bits [C][Hkv][128]
   const uint16_t* v_chunk;

@@ -102,8 +102,18 @@ enum nvfp4kv_status {
 
 /* Element types. NVFP4KV_FP8_E4M3 (OCP E4M3 "fn": 1 sign, 4 exponent bits with
  * bias 7, 3 mantissa bits, largest finite 448, no infinities) is an output type
- * of the extend dequantization only. */
-enum nvfp4kv_dtype { NVFP4KV_F32 = 0, NVFP4KV_BF16 = 1, NVFP4KV_FP8_E4M3 = 2 };
+ * of the extend dequantization only. NVFP4KV_F16_TILED is an extend workspace of
+ * two parts: K as bf16 rows [rows][Hkv][128] (as NVFP4KV_BF16), and V as f16 in
+ * tiles of 64 rows: row r of KV head h, channel d lies at byte
+ *   ((r/64) Hkv + h) 16384 + d 128 + 16 u + 8 ((k/16) % 2) + 2 (k % 4),
+ *   k = r % 64, u = 4 (k/32) + (k/4) % 4
+ * (nvfp4kv_tiled_v_bytes bytes for `rows` rows): each 16-byte unit holds the
+ * eight keys one matrix-core operand of nvfp4_extend_attn takes, so its V tiles
+ * are copied into the kernel's local memory unchanged. */
+enum nvfp4kv_dtype { NVFP4KV_F32 = 0, NVFP4KV_BF16 = 1, NVFP4KV_FP8_E4M3 = 2, NVFP4KV_F16_TILED = 3 };
+
+/* Bytes of the V part of an NVFP4KV_F16_TILED workspace of `rows` rows. */
+int64_t nvfp4kv_tiled_v_bytes(int64_t rows, int32_t num_kv_heads);
 
 /* NVFP4 KV pool of one layer. */
 typedef struct nvfp4kv_pool {
@@ -329,9 +339,16 @@ int32_t nvfp4_paged_decode_attn_append(const void* q, const void* k_new, const v
  *                   [0, max_seq_len]
  *   row_offsets     device int64 [n_seqs], first workspace row of each sequence
  *   max_seq_len     host upper bound of seq_lens (<= page_table_stride*16)
- *   k_out, v_out    device, f32, bf16 or FP8 E4M3 (one byte) per out_dtype
- * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_VALUE (global scale),
- * ERR_HIP.
+ *   k_out, v_out    device, f32, bf16 or FP8 E4M3 (one byte) per out_dtype; with
+ *                   NVFP4KV_F16_TILED, k_out bf16 rows and v_out f16 tiles (see
+ *                   the dtype): every value is the f16 nearest the exact value
+ *                   (one rounding; g <= 16, so that no value exceeds the f16
+ *                   range), and the rows of a sequence's last tile after its
+ *                   last row are set to zero (give each sequence its own tiles:
+ *                   row_offsets multiples of 64; offsets that are not multiples
+ *                   of 4 take a slower per-value store and get no zero rows)
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_VALUE (global scale; g
+ * above 16 with NVFP4KV_F16_TILED), ERR_HIP.
  */
 int32_t nvfp4_kv_dequant_workspace(const nvfp4kv_pool* pool, const int32_t* page_table, int64_t page_table_stride,
                                    const int32_t* seq_lens, const int64_t* row_offsets, int32_t n_seqs,
@@ -440,8 +457,11 @@ int32_t fp8_paged_decode_attn_append(const void* q, const void* k_new, const voi
  *   q               device bf16 [C][num_q_heads][128], contiguous
  *   k_prefix, v_prefix  device [P][num_kv_heads][128] workspace as written by
  *                   nvfp4_kv_dequant_workspace: NVFP4KV_BF16 or
- *                   NVFP4KV_FP8_E4M3 per prefix_dtype (finite values); may be
- *                   NULL when P = 0
+ *                   NVFP4KV_FP8_E4M3 per prefix_dtype (finite values), or
+ *                   NVFP4KV_F16_TILED (K bf16 rows, V f16 tiles whose rows past
+ *                   P are finite, as the dequant writes them); may be NULL when
+ *                   P = 0. With the tiled V the prefix's V^T tiles need no
+ *                   conversion pass in the kernel.
  *   k_chunk, v_chunk    device bf16 [C][num_kv_heads][128], contiguous
  *   out             device bf16 [C][num_q_heads][128]
  *   lse             device f32 [C][num_q_heads] or NULL
@@ -471,7 +491,8 @@ int32_t fp8_paged_decode_attn_append(const void* q, const void* k_new, const voi
  *   chunk_slots     device int32 [C] when chunk_pool is given
  * Errors: ERR_NULL, ERR_SHAPE (counts out of range, group > 16, pool heads),
  * ERR_ALIGN, ERR_DTYPE (prefix_dtype), ERR_VALUE (sm_scale not finite, v_bound
- * negative or not finite, pool global scale), ERR_HIP.
+ * negative or not finite, or above 2^15 with a tiled prefix, pool global scale),
+ * ERR_HIP.
  */
 int32_t nvfp4_extend_attn(const void* q, const void* k_prefix, const void* v_prefix, int32_t prefix_dtype,
                           int64_t prefix_len, const void* k_chunk, const void* v_chunk, int64_t chunk_len,

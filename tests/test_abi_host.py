@@ -339,7 +339,7 @@ def test_binding_rejects_bad_extend_and_dequant_shapes(L):
     ko = torch.zeros((32, 2, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="row_offsets"):
         B.nvfp4_kv_dequant_workspace(p, pt, sl, ro[:1], 16, ko, ko.clone())
-    with pytest.raises(ValueError, match="k_out and v_out must be"):
+    with pytest.raises(ValueError, match="k_out must be"):
         B.nvfp4_kv_dequant_workspace(p, pt, sl, ro, 16, torch.zeros((32, 3, 128), dtype=torch.bfloat16),
                                      torch.zeros((32, 3, 128), dtype=torch.bfloat16))
     q = torch.zeros((5, 4, 128), dtype=torch.bfloat16)

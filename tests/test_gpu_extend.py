@@ -160,3 +160,83 @@ def test_extend_fused_chunk_write_full_size():
     got = gpool.data.view(w.num_pages, -1)[slab_pages].cpu().numpy()
     ref = opool.reshape(w.num_pages, -1)[pages]
     assert np.array_equal(got, ref), f"{int((got != ref).sum())} bytes differ"
+
+
+def _untile_v(vt: np.ndarray, rows: int) -> np.ndarray:
+    """[tiles, Hkv, 128, 64] f16 tiles (layout of the C header's NVFP4KV_F16_TILED)
+    back to rows [rows, Hkv, 128]."""
+    tiles, hkv, _, _ = vt.shape
+    flat = vt.reshape(tiles, hkv, 128, 8, 2, 4)  # [tile][h][d][unit][half][pos]
+    out = np.empty((tiles * 64, hkv, 128), dtype=vt.dtype)
+    for k in range(64):
+        u, half, pos = 4 * (k // 32) + (k // 4) % 4, (k // 16) % 2, k % 4
+        out[k::64] = flat[:, :, :, u, half, pos]
+    return out[:rows]
+
+
+@pytest.mark.parametrize("g", [1.0, float(np.float32(0.3))])
+def test_dequant_tiled_workspace_bitexact(g):
+    """K as bf16 rows, V as f16 tiles: every value the nearest of its dtype to the
+    exact dequantized value (one rounding), rows of the last tile past the prefix
+    zero."""
+    lens = [37, 200]
+    w = W.small_workload(870, 2, 8, 2, lens, name="tiled")
+    kv = [(k * g, v * g) for k, v in (W.kv(w, b, 0, L) for b, L in enumerate(lens))]
+    gpool = gpu_pool_from_kv(w, kv, g=g)
+    opool = oracle_pool_from_kv(w, kv, g=g)
+    offs = [0, 64]  # each sequence on its own tiles
+    rows = offs[-1] + lens[-1]
+    k_ws = torch.full((rows, 2, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    v_ws = B.tiled_v_workspace(rows, 2)
+    v_ws.fill_(float("nan"))
+    B.nvfp4_kv_dequant_workspace(gpool, torch.as_tensor(w.page_table, device="cuda"),
+                                 torch.as_tensor(w.seq_lens, device="cuda"),
+                                 torch.tensor(offs, dtype=torch.int64, device="cuda"), max(lens), k_ws, v_ws)
+    torch.cuda.synchronize()
+    ko, vo = oracle.dequant_workspace(opool, 2, w.page_table, w.seq_lens, g=g)
+    v_rows = _untile_v(v_ws.cpu().numpy(), rows)
+    kb = bf16_bits(k_ws)
+    cum = np.concatenate([[0], np.cumsum(lens)])
+    for s_, (o, L) in enumerate(zip(offs, lens)):
+        ref_k, ref_v = ko[cum[s_]:cum[s_] + L], vo[cum[s_]:cum[s_] + L]
+        assert np.array_equal(kb[o:o + L], oracle.bf16_bits_of(ref_k)), f"K rows of sequence {s_}"
+        want = ref_v.astype(np.float16)  # one rounding from the exact value
+        got = v_rows[o:o + L]
+        assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), f"V of sequence {s_}"
+        end = -(-(o + L) // 64) * 64
+        pad = _untile_v(v_ws.cpu().numpy(), end)[o + L:end]
+        assert np.all(pad == 0), f"padding rows of sequence {s_} not zero"
+
+
+@pytest.mark.parametrize("P,C,hq,hkv", [(100, 37, 8, 1), (200, 130, 64, 8), (64, 64, 16, 2)])
+def test_extend_over_tiled_workspace(P, C, hq, hkv):
+    """Attention over the tiled workspace (V^T tiles copied as they are) equals
+    attention over the bf16 workspace of the same pool bit for bit (the f16 V
+    values are the same), and the oracle within the bar."""
+    print(f"tiled extend P={P} C={C} Hq={hq} Hkv={hkv}", flush=True)
+    w = W.small_workload(880 + P, 1, hq, hkv, [P + C])
+    k, v = W.kv(w, 0, 0, P + C)
+    gpool = gpu_pool_from_kv(w, [(k[:P], v[:P])])
+    pt = torch.as_tensor(w.page_table, device="cuda")
+    sl = torch.tensor([P], dtype=torch.int32, device="cuda")
+    ro = torch.zeros(1, dtype=torch.int64, device="cuda")
+    kb = torch.empty((P, hkv, 128), dtype=torch.bfloat16, device="cuda")
+    vb = torch.empty_like(kb)
+    B.nvfp4_kv_dequant_workspace(gpool, pt, sl, ro, P, kb, vb)
+    vt = B.tiled_v_workspace(P, hkv)
+    kt = torch.empty_like(kb)
+    B.nvfp4_kv_dequant_workspace(gpool, pt, sl, ro, P, kt, vt)
+    q = W.extend_inputs(881 + P, 0, C, hq, hkv)[0]
+    kc, vc = k[P:].to(torch.bfloat16), v[P:].to(torch.bfloat16)
+    sm = 128 ** -0.5
+    lse_a = torch.empty((C, hq), dtype=torch.float32, device="cuda")
+    lse_b = torch.empty_like(lse_a)
+    out_b = B.nvfp4_extend_attn(q.cuda(), kb, vb, kc.cuda(), vc.cuda(), sm, lse=lse_b)
+    out_t = B.nvfp4_extend_attn(q.cuda(), kt, vt, kc.cuda(), vc.cuda(), sm, lse=lse_a)
+    torch.cuda.synchronize()
+    assert torch.equal(out_t, out_b) and torch.equal(lse_a, lse_b)
+    kp = kb.float().cpu().numpy()
+    vp = _untile_v(vt.cpu().numpy(), P).astype(np.float32)
+    ref, ref_lse = oracle.extend_attn(bf16_bits(q), kp, vp, bf16_bits(kc), bf16_bits(vc), sm, n_threads=8)
+    assert_close(out_t.float().cpu().numpy(), ref, what="tiled extend")
+    assert_close(lse_a.cpu().numpy(), ref_lse, atol=1e-3, rtol=1e-4, what="tiled extend lse")
