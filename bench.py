@@ -71,6 +71,9 @@ def parse(argv=None):
                     help="no GPU work: summarize a rocprofv3 --kernel-trace output directory of a bench.py run "
                          "(per kernel: every launch, and the launches after the first --trace-skip of each)")
     ap.add_argument("--trace-skip", type=int, default=0)
+    ap.add_argument("--trace-steps", type=int, default=0,
+                    help="with --trace-summary: the traced run's --steps, to group its decode launches by phase")
+    ap.add_argument("--trace-warmup", type=int, default=0, help="with --trace-steps: the traced run's --warmup")
     return ap.parse_args(argv)
 
 
@@ -93,10 +96,63 @@ def copy_calibration(nbytes, steps):
                       "GBps_read_plus_write": round(2 * src.numel() * 4 / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
-def trace_summary(path, skip):
+def decode_phases(launches, steps, warmup):
+    """The headline decode step's launches grouped the way decode_step() issues
+    them: ``warmup`` pairs of one fused and one three-launch step, three passes
+    of ``steps`` fused then ``steps`` three-launch steps, then the
+    kernel-timing pass of ``steps`` fused steps. ``launches`` is (kernel, start
+    ns, end ns) in start order; a fused step is split + combine, a three-launch
+    step is quantize + split + combine. Per phase: mean, min and max of the
+    split kernel, the mean combine and new-token quantize, and the mean span of
+    a step from its first kernel's start to its last kernel's end (in us).
+    Returns [] when the trace does not hold the whole sequence."""
+    import statistics
+
+    first = next((i for i, x in enumerate(launches) if x[0] == "k_decode_split"), None)
+    if first is None:
+        return []
+    seq = [x for x in launches[first:] if x[0] in ("k_decode_split", "k_decode_combine", "k_quantize")]
+    grouped, i = [], 0
+    while i < len(seq):
+        names = tuple(x[0] for x in seq[i:i + 3])
+        if names == ("k_quantize", "k_decode_split", "k_decode_combine"):
+            grouped.append(seq[i:i + 3])
+            i += 3
+        elif names[:2] == ("k_decode_split", "k_decode_combine"):
+            grouped.append(seq[i:i + 2])
+            i += 2
+        else:
+            break  # the decode steps end at the first launch that is not part of one
+    plan = [("warm-up, fused and three-launch in turn", 2 * warmup)]
+    for p in range(3):
+        plan += [(f"pass {p}, fused", steps), (f"pass {p}, three-launch", steps)]
+    plan.append(("kernel-timing pass (fused)", steps))
+    if len(grouped) < sum(n for _, n in plan):
+        return []
+    out, k = [], 0
+
+    def us(v):
+        return round(statistics.mean(v) / 1000, 1) if v else None
+
+    for label, n in plan:
+        grp = grouped[k:k + n]
+        k += n
+        dur = {name: [e - s for g in grp for (nm, s, e) in g if nm == name]
+               for name in ("k_decode_split", "k_decode_combine", "k_quantize")}
+        sp = dur["k_decode_split"]
+        out.append({"phase": label, "steps": n, "split_mean_us": us(sp), "split_min_us": round(min(sp) / 1000, 1),
+                    "split_max_us": round(max(sp) / 1000, 1), "combine_mean_us": us(dur["k_decode_combine"]),
+                    "quantize_mean_us": us(dur["k_quantize"]),
+                    "step_span_mean_us": us([g[-1][2] - g[0][1] for g in grp])})
+    return out
+
+
+def trace_summary(path, skip, steps=0, warmup=0):
     """Per-kernel durations from a rocprofv3 kernel-trace CSV under ``path``:
     all launches, and the launches after the first ``skip`` of each kernel
-    (launches keep their dispatch order), with the grid they ran on."""
+    (launches keep their dispatch order), with the grid they ran on. With
+    ``steps`` > 0, also the headline decode step's launches by phase (the
+    bench.py run's --steps and --warmup)."""
     import csv
     import glob
     import statistics
@@ -108,14 +164,15 @@ def trace_summary(path, skip):
     for f in files:
         rows += list(csv.DictReader(open(f)))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    per = {}
+    per, launches = {}, []
     for r in rows:
         m = re.search(r"\b(k_[A-Za-z0-9_]+)\s*[(<]", r["Kernel_Name"])  # the library's kernels are k_*
         if not m:
             continue
         name = m.group(1)
-        per.setdefault(name, []).append(((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])),
-                                         r.get("Grid_Size_X", r.get("Grid_Size", ""))))
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        launches.append((name, t0, t1))
+        per.setdefault(name, []).append((t1 - t0, r.get("Grid_Size_X", r.get("Grid_Size", ""))))
     out = {}
     for name, v in per.items():
         d = [x for x, _ in v]
@@ -123,6 +180,8 @@ def trace_summary(path, skip):
         out[name] = {"launches": len(d), "mean_ns": round(statistics.mean(d)), "min_ns": min(d), "max_ns": max(d),
                      "steady_launches": len(steady), "steady_mean_ns": round(statistics.mean(steady)),
                      "steady_median_ns": round(statistics.median(steady)), "grids": sorted({g for _, g in v})}
+    if steps > 0:
+        out["decode_phases"] = decode_phases(launches, steps, warmup)
     print(json.dumps(out, indent=1))
 
 
@@ -152,9 +211,9 @@ def committed_traffic(workload, splits, kernel="k_decode_split"):
         h = hashlib.sha256()
         for f in srcs:
             h.update(open(f, "rb").read())
-        if h.hexdigest() != fields.get("kernel_source_sha256"):
-            return None
-        return int(fields["traffic_bytes_per_launch"])
+        if h.hexdigest() == fields.get("kernel_source_sha256"):
+            return int(fields["traffic_bytes_per_launch"])
+        # taken on other kernel sources: look on
     return None
 
 
@@ -530,7 +589,7 @@ def capacity(B, W, torch, steps, warmup, rows_by_len):
 def main(argv=None):
     args = parse(argv)
     if args.trace_summary:
-        trace_summary(args.trace_summary, args.trace_skip)
+        trace_summary(args.trace_summary, args.trace_skip, args.trace_steps, args.trace_warmup)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode",
