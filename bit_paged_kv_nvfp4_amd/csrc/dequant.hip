@@ -119,10 +119,54 @@ __device__ __forceinline__ size_t vt_offset(int64_t r, int h, int H, int d) {
          2 * (k & 3);
 }
 
-// Four f16 values of one channel, keys r .. r + 3 (r % 4 == 0), as 8 bytes.
-__device__ __forceinline__ void store_vt4(void* base, size_t off, const float (&x)[4]) {
-  const f16x2 lo = {(_Float16)x[0], (_Float16)x[1]}, hi = {(_Float16)x[2], (_Float16)x[3]};
-  *reinterpret_cast<uint2*>(static_cast<uint8_t*>(base) + off) = make_uint2(as_u32(lo), as_u32(hi));
+// K rows of one (page, KV head) into the row-major workspace: store i writes
+// tokens 4i .. 4i+3; lane (G, n) holds token 4i + G, channels 8n .. 8n+7 (4 code
+// bytes; the scale byte of block n/2). Tokens at or past ntok are not written.
+template <bool kExact>
+__device__ __forceinline__ void dequant_k_page(const DequantArgs& a, const uint8_t* kslab, int64_t row0, int h,
+                                               int ntok, int n, int G, int dt) {
+  uint32_t kc[4], ks[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = 4 * i + G;
+    kc[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kslab + tok * 64 + 4 * n));
+    ks[i] = kslab[kCodeBytes + tok * 8 + (n >> 1)];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = 4 * i + G;
+    if (tok >= ntok) continue;
+    const float sc = kExact ? e4m3_to_f32(ks[i]) * a.g : e4m3_to_f32(ks[i]);  // exact either way
+    const f32x2 v0 = fp4x2_to_f32x2<0>(kc[i]), v1 = fp4x2_to_f32x2<1>(kc[i]);
+    const f32x2 v2 = fp4x2_to_f32x2<2>(kc[i]), v3 = fp4x2_to_f32x2<3>(kc[i]);
+    const float v[8] = {v0[0] * sc, v0[1] * sc, v1[0] * sc, v1[1] * sc, v2[0] * sc, v2[1] * sc, v3[0] * sc, v3[1] * sc};
+    scale_and_store8<kExact>(a.k_out, ((size_t)(row0 + tok) * a.num_kv_heads + h) * kHeadDim + 8 * n, v, a.g, dt);
+  }
+}
+
+// The V chunk of lane (n, G) of one slab: channels 8n .. 8n+7 of tokens 4G ..
+// 4G+3 (block n/2), unscaled, as val[token 4G + i][channel 8n + e], and the four
+// tokens' block scales.
+__device__ __forceinline__ void load_v_chunk(const uint8_t* vslab, int lane, int n, int G, float (&val)[4][8],
+                                             uint32_t& scales) {
+  const uint4 vc = load_once(vslab + 16 * lane);
+  scales = *reinterpret_cast<const uint32_t*>(vslab + kCodeBytes + (n >> 1) * 16 + 4 * G);
+  const uint32_t vw[4] = {vc.x, vc.y, vc.z, vc.w};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    // byte 0: channel 2w of tokens 0|2, byte 1: channel 2w of tokens 1|3,
+    // bytes 2, 3: the same for channel 2w + 1
+    const f32x2 c0 = fp4x2_to_f32x2<0>(vw[w]), c1 = fp4x2_to_f32x2<1>(vw[w]);
+    const f32x2 c2 = fp4x2_to_f32x2<2>(vw[w]), c3 = fp4x2_to_f32x2<3>(vw[w]);
+    val[0][2 * w] = c0[0];
+    val[2][2 * w] = c0[1];
+    val[1][2 * w] = c1[0];
+    val[3][2 * w] = c1[1];
+    val[0][2 * w + 1] = c2[0];
+    val[2][2 * w + 1] = c2[1];
+    val[1][2 * w + 1] = c3[0];
+    val[3][2 * w + 1] = c3[1];
+  }
 }
 
 // One workgroup of 8 waves per (page, sequence); wave w takes KV heads w, w + 8,
@@ -131,8 +175,7 @@ __device__ __forceinline__ void store_vt4(void* base, size_t off, const float (&
 // on the 163840-token prefix (8 heads): one wave per (page, head) in head-major
 // order took 220 us into bf16, this order 142 us; 4 waves with two heads each
 // were 3% slower than 8.
-// kTiled: the NVFP4KV_F16_TILED workspace (K as bf16 rows, V as f16 tiles).
-template <bool kExact, bool kTiled>
+template <bool kExact>
 __global__ __launch_bounds__(512) void k_dequant(DequantArgs a) {
   const int pg = blockIdx.x;
   const int s = blockIdx.y;
@@ -144,105 +187,139 @@ __global__ __launch_bounds__(512) void k_dequant(DequantArgs a) {
   const int64_t pid = a.page_table[(int64_t)s * a.pt_stride + pg];
   const int64_t row0 = a.row_offsets[s] + (int64_t)pg * kPage;
   const int H = a.num_kv_heads;
-  const int dt = kTiled ? NVFP4KV_BF16 : a.out_dtype;  // the K side
+  const int dt = a.out_dtype;
   const int ntok = min(kPage, L - pg * kPage);
-  // tiled V: 8-byte stores when the sequence starts on a multiple of 4 rows
-  const bool vt_aligned = (a.row_offsets[s] & 3) == 0;
 
   for (int h = threadIdx.x >> 6; h < H; h += 8) {
     const uint8_t* kslab = a.pool + (pid * H + h) * (int64_t)(2 * kSlab);
-    const uint8_t* vslab = kslab + kSlab;
-
-    // ---- K: store i writes tokens 4i .. 4i+3; lane (G, n) holds token 4i + G,
-    // channels 8n .. 8n+7 (4 code bytes; scale byte of block n/2) ----
-    uint32_t kc[4], ks[4];
+    dequant_k_page<kExact>(a, kslab, row0, h, ntok, n, G, dt);
+    float val[4][8];
+    uint32_t vs;
+    load_v_chunk(kslab + kSlab, lane, n, G, val, vs);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tok = 4 * i + G;
-      kc[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kslab + tok * 64 + 4 * n));
-      ks[i] = kslab[kCodeBytes + tok * 8 + (n >> 1)];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = 4 * i + G;
+      const int tok = 4 * G + i;
       if (tok >= ntok) continue;
-      const float sc = kExact ? e4m3_to_f32(ks[i]) * a.g : e4m3_to_f32(ks[i]);  // exact either way
-      const f32x2 v0 = fp4x2_to_f32x2<0>(kc[i]), v1 = fp4x2_to_f32x2<1>(kc[i]);
-      const f32x2 v2 = fp4x2_to_f32x2<2>(kc[i]), v3 = fp4x2_to_f32x2<3>(kc[i]);
-      const float v[8] = {v0[0] * sc, v0[1] * sc, v1[0] * sc, v1[1] * sc, v2[0] * sc, v2[1] * sc, v3[0] * sc, v3[1] * sc};
-      scale_and_store8<kExact>(a.k_out, ((size_t)(row0 + tok) * H + h) * kHeadDim + 8 * n, v, a.g, dt);
-    }
-
-    // ---- V: chunk `lane` = channels 8n..8n+7 of tokens 4G..4G+3 (block n/2) ----
-    const uint4 vc = load_once(vslab + 16 * lane);
-    const uint32_t vs = *reinterpret_cast<const uint32_t*>(vslab + kCodeBytes + (n >> 1) * 16 + 4 * G);
-    const uint32_t vw[4] = {vc.x, vc.y, vc.z, vc.w};
-    float val[4][8];  // [token 4G + i][channel 8n + e], unscaled
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // byte 0: channel 2w of tokens 0|2, byte 1: channel 2w of tokens 1|3,
-      // bytes 2, 3: the same for channel 2w + 1
-      const f32x2 c0 = fp4x2_to_f32x2<0>(vw[w]), c1 = fp4x2_to_f32x2<1>(vw[w]);
-      const f32x2 c2 = fp4x2_to_f32x2<2>(vw[w]), c3 = fp4x2_to_f32x2<3>(vw[w]);
-      val[0][2 * w] = c0[0];
-      val[2][2 * w] = c0[1];
-      val[1][2 * w] = c1[0];
-      val[3][2 * w] = c1[1];
-      val[0][2 * w + 1] = c2[0];
-      val[2][2 * w + 1] = c2[1];
-      val[1][2 * w + 1] = c3[0];
-      val[3][2 * w + 1] = c3[1];
-    }
-    if (!kTiled) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = 4 * G + i;
-        if (tok >= ntok) continue;
-        const float e4 = e4m3_to_f32((vs >> (8 * i)) & 0xFFu);
-        const float sc = kExact ? e4 * a.g : e4;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = val[i][e] * sc;  // exact: at most 6 significant bits (times 2^k)
-        scale_and_store8<kExact>(a.v_out, ((size_t)(row0 + tok) * H + h) * kHeadDim + 8 * n, v, a.g, dt);
-      }
-      continue;
-    }
-    // tiled V: per channel, the lane's four keys 4G .. 4G+3 (zeros past the
-    // sequence), each value rounded once to f16
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
       const float e4 = e4m3_to_f32((vs >> (8 * i)) & 0xFFu);
-      sc[i] = kExact ? e4 * a.g : e4;
+      const float sc = kExact ? e4 * a.g : e4;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = val[i][e] * sc;  // exact: at most 6 significant bits (times 2^k)
+      scale_and_store8<kExact>(a.v_out, ((size_t)(row0 + tok) * H + h) * kHeadDim + 8 * n, v, a.g, dt);
     }
+  }
+}
+
+// The unscaled V values val[i][e] of one lane's chunk times their block scales
+// (exact), rounded once to f16: key 4G + i of channel 8n + e, zero where
+// `valid` is clear for key i. The product is passed through an empty asm
+// operand: left visible, a multiply followed by the f16 rounding is selected
+// as one mixed fma with a +0 addend, which turns the product of a -0 code into
+// +0.
+template <bool kExact>
+__device__ __forceinline__ float v_value(const float (&val)[4][8], uint32_t vs, int i, int e, float g, bool valid) {
+  const float e4 = e4m3_to_f32((vs >> (8 * i)) & 0xFFu);
+  float v = val[i][e] * (kExact ? e4 * g : e4);  // exact
+  if (!kExact) v = product_round_odd(v, g);
+  asm("" : "+v"(v));
+  return valid ? v : 0.0f;
+}
+
+// The V^T tile of KV head h for the tile's (up to) four pages. kOwn (the
+// sequence's first row a multiple of 64, so it owns its tiles): the whole 16 KB
+// tile is written, keys past the sequence's end as zeros. Lane (n, G) takes
+// chunk (n, G) of pages 2ks and 2ks + 1 of the tile, which is exactly unit
+// u = 4ks + G (keys 32ks + 4G .. +3, then 32ks + 16 + 4G .. +3) of channel rows
+// 8n .. 8n+7: one 16-byte store per channel, so every 128-byte channel row is
+// written whole by one wave. Otherwise only the sequence's own values are
+// stored, one at a time.
+template <bool kExact, bool kOwn>
+__device__ __forceinline__ void dequant_v_tile(const DequantArgs& a, const int64_t (&pid)[4], int npg, int rows,
+                                               int64_t row_t, int h, int lane, int n, int G) {
+  const int H = a.num_kv_heads;
+#pragma unroll 1
+  for (int ks = 0; ks < 2; ++ks) {
+    uint32_t x[2][8][2];  // [half][channel e]: keys 32 ks + 16 half + 4G .. +3 as 4 f16
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = val[i][e] * sc[i];  // exact
-        x[i] = 4 * G + i >= ntok ? 0.0f : kExact ? v : product_round_odd(v, a.g);
-      }
-      const int d = 8 * n + e;
-      if (vt_aligned) {
-        store_vt4(a.v_out, vt_offset(row0 + 4 * G, h, H, d), x);
+    for (int half = 0; half < 2; ++half) {
+      const int j = 2 * ks + half;
+      if (!kOwn && j >= npg) break;
+      float val[4][8];
+      uint32_t vs = 0;
+      if (j < npg) {
+        load_v_chunk(a.pool + (pid[j] * H + h) * (int64_t)(2 * kSlab) + kSlab, lane, n, G, val, vs);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (4 * G + i < ntok)
-            *reinterpret_cast<_Float16*>(static_cast<uint8_t*>(a.v_out) + vt_offset(row0 + 4 * G + i, h, H, d)) =
-                (_Float16)x[i];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) val[i][e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (kOwn) {
+          float y[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) y[i] = v_value<kExact>(val, vs, i, e, a.g, kPage * j + 4 * G + i < rows);
+          x[half][e][0] = as_u32(f16x2{(_Float16)y[0], (_Float16)y[1]});
+          x[half][e][1] = as_u32(f16x2{(_Float16)y[2], (_Float16)y[3]});
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int k = kPage * j + 4 * G + i;
+            if (k < rows)
+              *reinterpret_cast<_Float16*>(static_cast<uint8_t*>(a.v_out) + vt_offset(row_t + k, h, H, 8 * n + e)) =
+                  (_Float16)v_value<kExact>(val, vs, i, e, a.g, true);
+          }
+        }
       }
     }
-    // the sequence's last page also zeroes the rest of its last tile, so that the
-    // attention's masked keys multiply finite values
-    if (vt_aligned && (pg + 1) * kPage >= L) {
-      const float zero[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      const int64_t tile_end = ((row0 + kPage + 63) >> 6) << 6;
-      for (int64_t r = row0 + kPage + 4 * G; r < tile_end; r += 16)
+    if (kOwn) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) store_vt4(a.v_out, vt_offset(r, h, H, 8 * n + e), zero);
+      for (int e = 0; e < 8; ++e) {
+        const size_t off = vt_offset(row_t + 32 * ks + 4 * G, h, H, 8 * n + e);  // start of unit 4ks + G
+        *reinterpret_cast<uint4*>(static_cast<uint8_t*>(a.v_out) + off) =
+            make_uint4(x[0][e][0], x[0][e][1], x[1][e][0], x[1][e][1]);
+      }
     }
+  }
+}
+
+// The NVFP4KV_F16_TILED workspace (K as bf16 rows, V as f16 V^T tiles). One
+// workgroup of 8 waves per (64-row tile, sequence), wave w taking KV heads w,
+// w + 8, ...: the K rows of the tile's (up to) four pages as k_dequant writes
+// them, and the head's V^T tile. (With a workgroup per page, four workgroups on
+// different XCDs wrote into each 128-byte channel row of a tile, and the
+// half-written 64-byte blocks doubled the V bytes that reached HBM.)
+template <bool kExact>
+__global__ __launch_bounds__(512) void k_dequant_tiled(DequantArgs a) {
+  const int t = blockIdx.x;
+  const int s = blockIdx.y;
+  const int L = a.seq_lens[s];
+  if (t * 64 >= L) return;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;
+  const int G = lane >> 4;
+  const int H = a.num_kv_heads;
+  const int64_t first = a.row_offsets[s];
+  const int rows = min(64, L - 64 * t);  // rows of this sequence in the tile
+  const int npg = (rows + kPage - 1) / kPage;
+  int64_t pid[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pid[j] = j < npg ? a.page_table[(int64_t)s * a.pt_stride + 4 * t + j] : 0;
+  const int64_t row_t = first + 64 * (int64_t)t;  // workspace row of the tile's first key
+
+  for (int h = threadIdx.x >> 6; h < H; h += 8) {
+    // this loop and the V one over ks stay rolled: unrolled, the kernel took 199
+    // VGPRs (two waves per SIMD), rolled 116 (four)
+#pragma unroll 1
+    for (int j = 0; j < 4; ++j)
+      if (j < npg)
+        dequant_k_page<kExact>(a, a.pool + (pid[j] * H + h) * (int64_t)(2 * kSlab), row_t + kPage * j, h,
+                               min(kPage, rows - kPage * j), n, G, NVFP4KV_BF16);
+    if ((first & 63) == 0)
+      dequant_v_tile<kExact, true>(a, pid, npg, rows, row_t, h, lane, n, G);
+    else
+      dequant_v_tile<kExact, false>(a, pid, npg, rows, row_t, h, lane, n, G);
   }
 }
 
@@ -251,16 +328,19 @@ __global__ __launch_bounds__(512) void k_dequant(DequantArgs a) {
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream) {
   const int max_pages = (a.max_seq_len + kPage - 1) / kPage;
   if (a.n_seqs == 0 || max_pages == 0) return hipSuccess;
+  if (a.out_dtype == NVFP4KV_F16_TILED) {
+    const dim3 grid((max_pages + 3) / 4, a.n_seqs);
+    if (a.g_pow2)
+      hipLaunchKernelGGL((k_dequant_tiled<true>), grid, dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_dequant_tiled<false>), grid, dim3(512), 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 grid(max_pages, a.n_seqs);
-  const bool tiled = a.out_dtype == NVFP4KV_F16_TILED;
-  if (a.g_pow2 && tiled)
-    hipLaunchKernelGGL((k_dequant<true, true>), grid, dim3(512), 0, stream, a);
-  else if (a.g_pow2)
-    hipLaunchKernelGGL((k_dequant<true, false>), grid, dim3(512), 0, stream, a);
-  else if (tiled)
-    hipLaunchKernelGGL((k_dequant<false, true>), grid, dim3(512), 0, stream, a);
+  if (a.g_pow2)
+    hipLaunchKernelGGL((k_dequant<true>), grid, dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL((k_dequant<false, false>), grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((k_dequant<false>), grid, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

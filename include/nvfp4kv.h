@@ -343,10 +343,12 @@ int32_t nvfp4_paged_decode_attn_append(const void* q, const void* k_new, const v
  *                   NVFP4KV_F16_TILED, k_out bf16 rows and v_out f16 tiles (see
  *                   the dtype): every value is the f16 nearest the exact value
  *                   (one rounding; g <= 16, so that no value exceeds the f16
- *                   range), and the rows of a sequence's last tile after its
- *                   last row are set to zero (give each sequence its own tiles:
- *                   row_offsets multiples of 64; offsets that are not multiples
- *                   of 4 take a slower per-value store and get no zero rows)
+ *                   range). A sequence whose row_offsets entry is a multiple
+ *                   of 64 owns its tiles (no other sequence may have rows in
+ *                   them): they are written whole, the rows of its last tile
+ *                   after its last row as zeros. Any other
+ *                   sequence gets only its own rows, one value at a time
+ *                   (slower), so sequences may share a tile.
  * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_VALUE (global scale; g
  * above 16 with NVFP4KV_F16_TILED), ERR_HIP.
  */

@@ -208,6 +208,44 @@ def test_dequant_tiled_workspace_bitexact(g):
         assert np.all(pad == 0), f"padding rows of sequence {s_} not zero"
 
 
+@pytest.mark.parametrize("offs", [[3, 40, 300], [0, 69, 320]])
+def test_dequant_tiled_packed_sequences(offs):
+    """Sequences packed into shared tiles: every sequence's K and V rows are
+    exact (one rounding), a sequence on a multiple of 64 gets zero rows to the
+    end of its last tile, and every other workspace row is left as it was."""
+    lens = [37, 200, 50]
+    print(f"tiled dequant, row offsets {offs}", flush=True)
+    w = W.small_workload(890 + offs[0], 3, 8, 2, lens, name="tiled_packed")
+    kv = [W.kv(w, b, 0, L) for b, L in enumerate(lens)]
+    gpool = gpu_pool_from_kv(w, kv)
+    opool = oracle_pool_from_kv(w, kv)
+    rows = 384
+    k_ws = torch.full((rows, 2, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    v_ws = B.tiled_v_workspace(rows, 2)
+    v_ws.fill_(float("nan"))
+    B.nvfp4_kv_dequant_workspace(gpool, torch.as_tensor(w.page_table, device="cuda"),
+                                 torch.as_tensor(w.seq_lens, device="cuda"),
+                                 torch.tensor(offs, dtype=torch.int64, device="cuda"), max(lens), k_ws, v_ws)
+    torch.cuda.synchronize()
+    ko, vo = oracle.dequant_workspace(opool, 2, w.page_table, w.seq_lens)
+    v_rows = _untile_v(v_ws.cpu().numpy(), rows)
+    kb = bf16_bits(k_ws)
+    cum = np.concatenate([[0], np.cumsum(lens)])
+    written = np.zeros(rows, dtype=bool)
+    zero = np.zeros(rows, dtype=bool)
+    for s_, (o, L) in enumerate(zip(offs, lens)):
+        assert np.array_equal(kb[o:o + L], oracle.bf16_bits_of(ko[cum[s_]:cum[s_] + L])), f"K rows of sequence {s_}"
+        want = vo[cum[s_]:cum[s_] + L].astype(np.float16)
+        assert np.array_equal(v_rows[o:o + L].view(np.uint16), want.view(np.uint16)), f"V of sequence {s_}"
+        written[o:o + L] = True
+        if o % 64 == 0:
+            zero[o + L:-(-(o + L) // 64) * 64] = True
+    assert np.all(v_rows[zero] == 0), "padding rows of an own-tile sequence not zero"
+    untouched = ~(written | zero)
+    assert np.all(np.isnan(v_rows[untouched])), "V rows of no sequence were written"
+    assert np.all(np.isnan(k_ws.float().cpu().numpy()[untouched | zero])), "K rows of no sequence were written"
+
+
 @pytest.mark.parametrize("P,C,hq,hkv", [(100, 37, 8, 1), (200, 130, 64, 8), (64, 64, 16, 2)])
 def test_extend_over_tiled_workspace(P, C, hq, hkv):
     """Attention over the tiled workspace (V^T tiles copied as they are) equals
