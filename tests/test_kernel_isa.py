@@ -152,3 +152,16 @@ def test_quantize_encodes_with_the_fp4_conversion(all_asm):
     body = _function(all_asm["quantize.hip"], "10k_quantize")
     assert re.search(r"v_maximum3_f32", body)
     assert len(re.findall(r"v_cvt_scalef32_pk_fp4_f32", body)) >= 8
+
+
+def test_dequant_has_no_mixed_fma(all_asm):
+    """The dequant kernels' f16 and bf16 values are each one rounding of an exact
+    product, and the sign of a zero product must survive. A multiply followed by
+    the f16 rounding, left visible to the compiler, was once selected as one mixed
+    fma (v_fma_mixlo_f16) with a +0 addend, which turns the product of a -0 code
+    into +0 (the tiled workspace's V went through it); the V product now passes
+    through an opaque register. No mixed fma may appear in any dequant kernel."""
+    asm = all_asm["dequant.hip"]
+    for kernel in ("9k_dequant", "15k_dequant_tiled"):
+        body = _function(asm, kernel)
+        assert not re.search(r"v_fma_mix(lo|hi)?_f16|v_mad_mix", body), kernel
