@@ -10,7 +10,7 @@
  *   [EUROK]  "NVFP4-KV-Cache auf der NVIDIA RTX PRO 6000 Blackwell Server
  *            Edition: Genauigkeit, Nutzer".
  *
- * The library computes three things on the GPU, each in hand-written HIP:
+ * The library computes four things on the GPU, each in hand-written HIP:
  *   - nvfp4_kv_quantize: quantize-on-write of K/V rows into the NVFP4 pool
  *     ([LMSYS] "Interpretation": initial prefill quantizes the prompt's keys and
  *     values into the NVFP4 cache).
